@@ -1,0 +1,213 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the smoke check.
+
+This module draws random numbers, rounds them to bfloat16 and lays K/V out in pages. It
+holds none of the attention arithmetic, and neither the oracle nor the HIP path imports
+the other through it.
+
+Workloads (the shapes of prefill at 2K-32K tokens and long-context decode that the pages
+discuss; every value is drawn from N(0, 1) with numpy's PCG64 ``default_rng(seed)``):
+
+1. single-head forward, fp32: B=1, H=1, N=256, d=64, no mask, seed 1.
+2. causal multi-head prefill, bf16: B=4, H=16, N=2048, d=64, seed 2.
+3. causal multi-head prefill (long), bf16: B=2, H=32, N=8192, d=128, K scaled by 2 so that
+   softmax rows are peaky, seed 3.
+4. causal grouped-query prefill, bf16: B=1, 32 query heads over 8 KV heads, N=32768,
+   d=128, seed 4.
+5. split-K decode over a paged KV cache, bf16: B=8 sequences with one query token each,
+   32 query heads over 8 KV heads, d=128, lengths uniform in [16384, 32768] (inclusive),
+   16-token pages at randomly permuted physical slots named by an int32 block table,
+   seed 5.
+
+Draw order: Q, then K, then V (forward); lengths, q, then K_b and V_b per sequence, then
+the page permutation (decode). Values are rounded to bfloat16 with round-to-nearest-even
+before anyone sees them, so both sides receive identical, exactly representable inputs.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BF16_NAN_BITS = 0x7FC0
+
+
+@dataclass(frozen=True)
+class FwdConfig:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    dtype: str  # "f32" or "bf16"
+    causal: bool
+    seed: int
+    k_mult: float = 1.0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def flops(self) -> float:
+        """Algorithmic FLOPs: 4*d per admissible (query, key) pair (two contractions)."""
+        per_head = self.N * (self.N + 1) / 2 if self.causal else float(self.N) * self.N
+        return 4.0 * self.d * per_head * self.B * self.Hq
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    page_size: int
+    len_min: int
+    len_max: int
+    seed: int
+    lens: tuple = field(default=())  # fixed lengths instead of drawing them
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+CONFIGS = {
+    1: FwdConfig("single-head fwd fp32 B=1 H=1 N=256 d=64", 1, 1, 1, 256, 64, "f32", False, 1),
+    2: FwdConfig("causal MHA prefill bf16 B=4 H=16 N=2048 d=64", 4, 16, 16, 2048, 64, "bf16", True, 2),
+    3: FwdConfig("causal MHA prefill bf16 B=2 H=32 N=8192 d=128 (K x2)", 2, 32, 32, 8192, 128,
+                 "bf16", True, 3, k_mult=2.0),
+    4: FwdConfig("causal GQA prefill bf16 B=1 Hq=32 Hkv=8 N=32768 d=128", 1, 32, 8, 32768, 128,
+                 "bf16", True, 4),
+    5: DecodeConfig("paged split-K decode bf16 B=8 Hq=32 Hkv=8 d=128 L~U[16384,32768] page=16",
+                    8, 32, 8, 128, 16, 16384, 32768, 5),
+}
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))
+    rounded = (bits + bias) & np.uint32(0xFFFF0000)
+    nan = np.isnan(x)
+    if nan.any():
+        rounded = np.where(nan, np.uint32(BF16_NAN_BITS << 16), rounded)
+    return rounded.view(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """The uint16 bfloat16 encodings of float32 values that are already bf16-exact."""
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return (bits >> np.uint32(16)).astype(np.uint16)
+
+
+@dataclass
+class FwdInputs:
+    q: np.ndarray  # [B, Hq, N, d] float32 (bf16-exact when dtype == "bf16")
+    k: np.ndarray  # [B, Hkv, N, d]
+    v: np.ndarray  # [B, Hkv, N, d]
+    scale: float
+    causal: bool
+    dtype: str
+
+
+def fwd_inputs(B, Hq, Hkv, N, d, seed, dtype="bf16", causal=True, k_mult=1.0, scale=None):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, N, d), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, N, d), dtype=np.float32)
+    if k_mult != 1.0:
+        k *= np.float32(k_mult)
+    v = rng.standard_normal((B, Hkv, N, d), dtype=np.float32)
+    if dtype == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    return FwdInputs(q, k, v, 1.0 / math.sqrt(d) if scale is None else scale, causal, dtype)
+
+
+def config_fwd_inputs(cfg: FwdConfig) -> FwdInputs:
+    return fwd_inputs(cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.d, cfg.seed, cfg.dtype, cfg.causal,
+                      cfg.k_mult)
+
+
+@dataclass
+class DecodeInputs:
+    lens: np.ndarray  # [B] int32
+    q: np.ndarray  # [B, Hq, d] float32, bf16-exact
+    k_seqs: list  # per sequence [Hkv, L_b, d] (logical cache)
+    v_seqs: list
+    k_cache: np.ndarray  # [num_pages, Hkv, page_size, d]; unused slots hold NaN
+    v_cache: np.ndarray
+    block_table: np.ndarray  # [B, max_pages_per_seq] int32; unused entries are -1
+    page_size: int
+    scale: float
+
+    @property
+    def num_pages(self) -> int:
+        return self.k_cache.shape[0]
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.lens.max()) if self.lens.size else 0
+
+    def kv_bytes(self, elem_bytes=2) -> int:
+        """Bytes of K and V a decode step must read: every admissible token once per KV head."""
+        hkv, d = self.k_cache.shape[1], self.k_cache.shape[3]
+        return int(2 * int(self.lens.sum()) * hkv * d * elem_bytes)
+
+
+def decode_inputs(B, Hq, Hkv, d, page_size, seed, lens=None, len_min=None, len_max=None,
+                  max_pages_per_seq=None, scale=None, unused_fill=np.nan):
+    rng = np.random.default_rng(seed)
+    if lens is None:
+        lens = rng.integers(len_min, len_max + 1, size=B)
+    lens = np.asarray(lens, dtype=np.int32)
+    q = round_to_bf16(rng.standard_normal((B, Hq, d), dtype=np.float32))
+    k_seqs, v_seqs = [], []
+    for b in range(B):
+        k_seqs.append(round_to_bf16(rng.standard_normal((Hkv, int(lens[b]), d), dtype=np.float32)))
+        v_seqs.append(round_to_bf16(rng.standard_normal((Hkv, int(lens[b]), d), dtype=np.float32)))
+    pages = [-(-int(L) // page_size) for L in lens]
+    total = int(sum(pages))
+    perm = rng.permutation(total).astype(np.int32)
+    width = max(pages + [1]) if max_pages_per_seq is None else max_pages_per_seq
+    if width < max(pages + [0]):
+        raise ValueError("max_pages_per_seq too small for the drawn lengths")
+    block_table = np.full((B, width), -1, dtype=np.int32)
+    k_cache = np.full((total, Hkv, page_size, d), unused_fill, dtype=np.float32)
+    v_cache = np.full((total, Hkv, page_size, d), unused_fill, dtype=np.float32)
+    offset = 0
+    for b in range(B):
+        npg, L = pages[b], int(lens[b])
+        phys = perm[offset:offset + npg]
+        block_table[b, :npg] = phys
+        for cache, seq in ((k_cache, k_seqs[b]), (v_cache, v_seqs[b])):
+            padded = np.full((Hkv, npg * page_size, d), unused_fill, dtype=np.float32)
+            padded[:, :L] = seq
+            cache[phys] = padded.reshape(Hkv, npg, page_size, d).transpose(1, 0, 2, 3)
+        offset += npg
+    return DecodeInputs(lens, q, k_seqs, v_seqs, k_cache, v_cache, block_table, page_size,
+                        1.0 / math.sqrt(d) if scale is None else scale)
+
+
+def config_decode_inputs(cfg: DecodeConfig) -> DecodeInputs:
+    lens = list(cfg.lens) if cfg.lens else None
+    width = -(-cfg.len_max // cfg.page_size)
+    return decode_inputs(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.page_size, cfg.seed, lens=lens,
+                         len_min=cfg.len_min, len_max=cfg.len_max, max_pages_per_seq=width)
+
+
+def to_torch(x: np.ndarray, dtype: str, device="cuda"):
+    """Upload a float32 array as a torch tensor of ``dtype`` ("f32" or "bf16"), exactly."""
+    import torch
+
+    if dtype == "bf16":
+        bits = bf16_bits(x).view(np.int16)
+        t = torch.from_numpy(bits).view(torch.bfloat16)
+    elif dtype == "f32":
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    else:
+        raise ValueError(dtype)
+    return t.to(device).contiguous()
