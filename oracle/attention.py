@@ -164,7 +164,7 @@ def merge(o_parts, m_parts, l_parts):
     shift = np.where(np.isfinite(m), m, 0.0)
     w = np.where(live, l_parts * np.exp(np.where(live, m_parts, 0.0) - shift[None, :]), 0.0)
     l = w.sum(axis=0)
-    num = (w[:, :, None] * o_parts).sum(axis=0)
+    num = (w[:, :, None] * np.where(live[:, :, None], o_parts, 0.0)).sum(axis=0)
     safe_l = np.where(l > 0, l, 1.0)
     out = np.where(l[:, None] > 0, num / safe_l[:, None], 0.0)
     return out, m, l

@@ -277,6 +277,11 @@ def test_empty_row_conventions():
     assert np.all(o == 0) and m[0] == -np.inf and l[0] == 0
     o, m, l = oracle.merge(np.zeros((2, 1, 3)), np.full((2, 1), -np.inf), np.zeros((2, 1)))
     assert np.all(o == 0) and m[0] == -np.inf and l[0] == 0
+    # an empty partial carries no weight, whatever its O holds
+    o, m, l = oracle.merge(np.array([[[1.0, 2.0]], [[np.nan, np.nan]]]), np.array([[0.5], [-np.inf]]),
+                           np.array([[2.0], [0.0]]))
+    np.testing.assert_array_equal(o, [[1.0, 2.0]])
+    assert m[0] == 0.5 and l[0] == 2.0
 
 
 def test_closed_forms_small_n():
