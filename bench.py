@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact tiled attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  1. fa_fwd on causal multi-head prefill, bf16, B=2, H=32, N=8192, d=128 (K scaled by 2);
+  2. fa_decode_splitk (split-K paged decode + partial merge) on B=8 sequences, 32 query
+     heads over 8 KV heads, d=128, lengths uniform in [16384, 32768], 16-token pages.
+Inputs are generated once (seeded) and are resident in HBM before timing starts.
+
+Prints ONE JSON line. `value` is the forward's algorithmic TFLOP/s (4*d per admissible
+(query, key) pair, causal tiles skipped by the method are not counted) over the timed
+steps; the decode's algorithmic HBM GB/s (K and V read once per KV head, plus q, o, the
+block table and the lengths) is reported next to it. Kernel durations come from HIP
+events recorded on the stream the kernels are launched on. `cpu_baseline` times the
+float64 CPU oracle on a bounded sample of the same forward workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s & % MFMA peak; decode HBM GB/s & % peak (1×MI355X)"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--fwd-config", type=int, default=3, choices=[2, 3, 4])
+    ap.add_argument("--decode-splits", type=int, default=0, help="0 = the library's plan")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=2,
+                    help="heads of the forward workload the oracle is timed on")
+    ap.add_argument("--only", choices=["fwd", "decode"], default=None,
+                    help="time one kernel only (profiling runs)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter scaling)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the path has no multi-GPU component in this build "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_tiled_attention_24_amd as fa
+    from exact_tiled_attention_24_amd import inputs as gen
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    fa.load_library()  # fails loudly if the HIP library is missing
+    props = torch.cuda.get_device_properties(dev)
+
+    # ---- inputs, resident in HBM ----
+    fcfg = gen.CONFIGS[args.fwd_config]
+    fx = gen.config_fwd_inputs(fcfg)
+    q = gen.to_torch(fx.q, "bf16", dev)
+    k = gen.to_torch(fx.k, "bf16", dev)
+    v = gen.to_torch(fx.v, "bf16", dev)
+    o = torch.empty_like(q)
+    fwd_flops = fcfg.flops()
+
+    dcfg = gen.CONFIGS[5]
+    dx = gen.config_decode_inputs(dcfg)
+    dq = gen.to_torch(dx.q, "bf16", dev)
+    kc = gen.to_torch(dx.k_cache, "bf16", dev)
+    vc = gen.to_torch(dx.v_cache, "bf16", dev)
+    table = torch.from_numpy(dx.block_table).to(dev)
+    lens = torch.from_numpy(dx.lens.astype(np.int32)).to(dev)
+    do = torch.empty_like(dq)
+    ws_bytes = fa.fa_decode_workspace_bytes(dcfg.B, dcfg.Hq, dcfg.d, 16, dcfg.len_max,
+                                            args.decode_splits)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    splits = args.decode_splits or fa.fa_decode_plan_splits(dcfg.B, dcfg.Hkv, 16, dcfg.len_max)
+    dec_bytes = (dx.kv_bytes() + dq.numel() * 2 + do.numel() * 2
+                 + 4 * int(sum(-(-int(L) // 16) for L in dx.lens)) + 4 * dcfg.B)
+    del dx.k_cache, dx.v_cache
+
+    def run_fwd():
+        fa.fa_fwd(q, k, v, scale=fx.scale, causal=fcfg.causal, out=o)
+
+    def run_decode():
+        fa.fa_decode_splitk(dq, kc, vc, table, lens, dcfg.len_max, scale=dx.scale,
+                            num_splits=args.decode_splits, out=do, workspace=ws)
+
+    copy_src = copy_dst = None
+    if args.copy_mib:
+        copy_src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        copy_dst = torch.empty_like(copy_src)
+
+    stream = torch.cuda.current_stream(dev)
+    do_fwd = args.only in (None, "fwd")
+    do_dec = args.only in (None, "decode")
+    for _ in range(args.warmup):
+        if do_fwd:
+            run_fwd()
+        if do_dec:
+            run_decode()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        e = ev[s]
+        e[0].record(stream)
+        if do_fwd:
+            run_fwd()
+        e[1].record(stream)
+        e[2].record(stream)
+        if do_dec:
+            run_decode()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if copy_src is not None:
+        for _ in range(3):
+            copy_dst.copy_(copy_src)
+        torch.cuda.synchronize()
+
+    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+
+    fwd_tflops = fwd_flops / (fwd_ms.mean() * 1e-3) / 1e12 if do_fwd else None
+    dec_gbps = dec_bytes / (dec_ms.mean() * 1e-3) / 1e9 if do_dec else None
+    traffic = load_traffic()
+
+    result = {
+        "metric": METRIC,
+        "value": round(fwd_tflops, 2) if fwd_tflops else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16-rounded; no dataset)",
+        "config": {
+            "workload": f"fwd: {fcfg.name}; decode: {dcfg.name}",
+            "fwd": {"B": fcfg.B, "Hq": fcfg.Hq, "Hkv": fcfg.Hkv, "N": fcfg.N, "d": fcfg.d,
+                    "causal": fcfg.causal, "algorithmic_flops": fwd_flops},
+            "decode": {"B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv, "d": dcfg.d, "page": 16,
+                       "seq_lens_sum": int(dx.lens.sum()), "splits": splits,
+                       "algorithmic_bytes": dec_bytes},
+            "device": props.name, "cus": props.multi_processor_count,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(fwd_tflops, 2) if fwd_tflops else None,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4) if fwd_tflops else None,
+            "traffic": traffic.get("fwd"),
+            "kernel": "fwd_bf16_kernel<128>",
+            "avg_launch_ms": round(float(fwd_ms.mean()), 5) if do_fwd else None,
+        },
+        "decode": {
+            "value": round(dec_gbps, 1) if dec_gbps else None,
+            "unit": "GB/s",
+            "tokens_per_s": round(dcfg.B / (dec_ms.mean() * 1e-3), 1) if do_dec else None,
+            "kv_tokens_per_s": round(float(dx.lens.sum()) / (dec_ms.mean() * 1e-3), 1) if do_dec else None,
+            "roofline": {
+                "bound": "hbm",
+                "achieved": round(dec_gbps, 1) if dec_gbps else None,
+                "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s",
+                "frac": round(dec_gbps / PEAK_HBM_GBPS, 4) if dec_gbps else None,
+                "traffic": traffic.get("decode"),
+                "avg_call_ms": round(float(dec_ms.mean()), 5) if do_dec else None,
+            },
+        },
+        "fwd_tokens_per_s": round(fcfg.B * fcfg.N / (fwd_ms.mean() * 1e-3), 1) if do_fwd else None,
+    }
+    if not args.no_cpu_baseline and do_fwd:
+        result["cpu_baseline"] = cpu_baseline(fx, fcfg, args.cpu_heads)
+    print(json.dumps(result), flush=True)
+
+
+def load_traffic():
+    """HBM bytes per launch from committed counter summaries, if present and current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return {}
+    try:
+        with open(path) as f:
+            return json.load(f)
+    except (OSError, ValueError):
+        return {}
+
+
+def cpu_baseline(fx, fcfg, heads):
+    """Time the float64 oracle on `heads` whole heads of the forward workload."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        cores = os.cpu_count() or 1
+    G = fcfg.Hq // fcfg.Hkv
+    t0 = time.perf_counter()
+    for i in range(heads):
+        b, h = divmod(i, fcfg.Hq)
+        oracle.attention_head(fx.q[b, h], fx.k[b, h // G], fx.v[b, h // G], fx.scale, fcfg.causal)
+    dt = time.perf_counter() - t0
+    flops = fcfg.flops() / (fcfg.B * fcfg.Hq) * heads
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{heads} of {fcfg.B * fcfg.Hq} heads of the forward workload "
+                      f"(causal N={fcfg.N}, d={fcfg.d}), float64 numpy"}
+
+
+if __name__ == "__main__":
+    main()

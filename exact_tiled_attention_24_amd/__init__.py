@@ -1,2 +1,214 @@
-"""Exact tiled attention for MI355X (gfx950): FlashAttention forward, paged split-K decode
-and (m, l, O) partial merge as hand-written HIP kernels behind a C ABI (libfa.so)."""
+"""Exact tiled attention for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libfa.so`` (declared in ``include/fa.h``): it checks tensor
+shapes, dtypes and devices, allocates outputs through torch, and passes raw device pointers
+and the current HIP stream to the C ABI. Every step of the computation runs in the HIP
+kernels; there is no fallback. If the library is missing or fails to load, every call
+raises.
+
+Entry points (same names as the C ABI):
+    fa_fwd(q, k, v, scale=None, causal=False, out=None, return_stats=False)
+    fa_decode_splitk(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, ...)
+    fa_merge(o_parts, m_parts, l_parts, out_dtype=torch.float32, return_stats=False)
+    fa_decode_workspace_bytes(...), fa_decode_plan_splits(...), fa_status_string(code)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARGUMENT = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_WORKSPACE_TOO_SMALL = 3
+FA_ERR_HIP = 4
+FA_F32 = 0
+FA_BF16 = 1
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {fa_status_string(code)}")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so and declare its C signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m exact_tiled_attention_24_amd.build` "
+            "(the HIP library is required, there is no fallback)")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.fa_fwd.restype = i32
+    lib.fa_decode_splitk.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                     i32, i32, f32, i32, vp, sz, vp]
+    lib.fa_decode_splitk.restype = i32
+    lib.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_decode_plan_splits.argtypes = [i32, i32, i32, i32]
+    lib.fa_decode_plan_splits.restype = i32
+    lib.fa_merge.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.fa_merge.restype = i32
+    lib.fa_status_string.argtypes = [i32]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def fa_status_string(code: int) -> str:
+    return load_library().fa_status_string(int(code)).decode()
+
+
+def _check(code: int, where: str) -> None:
+    if code != FA_OK:
+        raise FaError(code, where)
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    dev = ts[0].device
+    for t in ts:
+        if t is not None and t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+
+
+def fa_fwd(q, k, v, scale=None, causal=False, out=None, return_stats=False):
+    """Tiled attention forward. q: [B, Hq, N, d]; k, v: [B, Hkv, N, d] (bf16 or f32).
+
+    Returns O [B, Hq, N, d] in q's dtype, or (O, m, l) with float32 [B, Hq, N] statistics in
+    natural-log units when ``return_stats``.
+    """
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    Hkv = k.shape[1]
+    o = torch.empty_like(q) if out is None else out
+    m = l = None
+    if return_stats:
+        m = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+        l = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _require_gpu(q, k, v, o, m, l)
+    if o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        code = lib.fa_fwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(m), _ptr(l),
+                          B, Hq, Hkv, N, d, scale, 1 if causal else 0, _stream(q.device))
+    _check(code, "fa_fwd")
+    return (o, m, l) if return_stats else o
+
+
+def fa_decode_workspace_bytes(B, Hq, d, page_size, max_seq_len, num_splits=0) -> int:
+    return int(load_library().fa_decode_workspace_bytes(B, Hq, d, page_size, max_seq_len,
+                                                         num_splits))
+
+
+def fa_decode_plan_splits(B, Hkv, page_size, max_seq_len) -> int:
+    return int(load_library().fa_decode_plan_splits(B, Hkv, page_size, max_seq_len))
+
+
+def fa_decode_splitk(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale=None,
+                     num_splits=0, out=None, workspace=None):
+    """Single-query decode over a paged KV cache, split across the KV sequence.
+
+    q: [B, Hq, d] bf16; k_cache, v_cache: [num_pages, Hkv, page_size, d] bf16;
+    block_table: int32 [B, max_pages_per_seq]; seq_lens: int32 [B] (both on the GPU).
+    Returns O [B, Hq, d] bf16. ``workspace`` (uint8, on the GPU) is allocated if omitted.
+    """
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B, Hq, d]; caches [num_pages, Hkv, page_size, d]")
+    B, Hq, d = q.shape
+    num_pages, Hkv, page_size, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("head dimension mismatch between q and the cache")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages_per_seq] and seq_lens [B]")
+    o = torch.empty_like(q) if out is None else out
+    need = fa_decode_workspace_bytes(B, Hq, d, page_size, int(max_seq_len), int(num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _require_gpu(q, k_cache, v_cache, block_table, seq_lens, o, workspace)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        code = lib.fa_decode_splitk(
+            _dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(seq_lens), _ptr(o), B, Hq, Hkv, d, page_size, num_pages, block_table.shape[1],
+            int(max_seq_len), scale, int(num_splits), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(code, "fa_decode_splitk")
+    return o
+
+
+def fa_merge(o_parts, m_parts, l_parts, out_dtype=None, return_stats=False, out=None):
+    """Merge S partials: o_parts float32 [S, R, d], m_parts / l_parts float32 [S, R]."""
+    torch = _torch()
+    lib = load_library()
+    if o_parts.dim() != 3 or m_parts.shape != o_parts.shape[:2] or l_parts.shape != m_parts.shape:
+        raise ValueError("o_parts must be [S, R, d] and m_parts, l_parts [S, R]")
+    for t in (o_parts, m_parts, l_parts):
+        if t.dtype != torch.float32:
+            raise TypeError("partials must be float32")
+    S, R, d = o_parts.shape
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    o = torch.empty((R, d), dtype=out_dtype, device=o_parts.device) if out is None else out
+    m = l = None
+    if return_stats:
+        m = torch.empty((R,), dtype=torch.float32, device=o_parts.device)
+        l = torch.empty((R,), dtype=torch.float32, device=o_parts.device)
+    _require_gpu(o_parts, m_parts, l_parts, o, m, l)
+    with torch.cuda.device(o_parts.device):
+        code = lib.fa_merge(_dtype_code(o), _ptr(o_parts), _ptr(m_parts), _ptr(l_parts), _ptr(o),
+                            _ptr(m), _ptr(l), S, R, d, _stream(o_parts.device))
+    _check(code, "fa_merge")
+    return (o, m, l) if return_stats else o

@@ -1,0 +1,319 @@
+// decode.hip - single-query attention over a paged KV cache, split across the KV sequence.
+//
+// Method: "FlashAttention" (shubhamtatvamasi.com), "Decode is a different problem": with one
+// query row per sequence there is no reuse on the query side and only batch x KV-head
+// units of parallelism, so the KV sequence is split into chunks processed by separate
+// workgroups; each chunk yields a partial (m, l, O) that is merged afterwards with the
+// online-softmax rule. The cache is read through a block table (the paged variants of the
+// family table on the same page, and its PagedAttention answer).
+//
+// CDNA4 design. The kernel is bound by HBM bandwidth (about 4 FLOP per byte of K/V), so it
+// is built around memory-level parallelism rather than the matrix cores:
+//  * grid = (chunk, sequence x KV head); one workgroup of 4 waves per chunk; wave w takes
+//    pages w, w+4, ... of its chunk. The G query heads that share a KV head are served by
+//    the same pass over the K/V bytes (each byte of the cache is read once per KV head).
+//  * lane l owns token slot l/8 of each 8-token half page and the 16 head dimensions
+//    16*(l%8) .. +15, so a page is four 16-byte loads of K and four of V per lane, and
+//    every load instruction covers contiguous 2 KiB halves of the page.
+//  * the block-table entries of a wave's pages are fetched once into a VGPR and read back
+//    with v_readlane, so every page address is a scalar; the next page is prefetched into
+//    registers while the current one is consumed.
+//  * q.k partial dot products use v_dot2_f32_bf16 and are summed over the 8 lanes of a token
+//    with three DPP steps. Each lane keeps its own running (m, l, O) for its token slot with
+//    a lazily moved reference maximum: the accumulator is rescaled only when a score exceeds
+//    the reference by more than 2^8, which is exact up to rounding because the final
+//    division by l cancels the reference.
+//  * at the end the lanes' states are merged across token slots, then across waves through
+//    LDS, and one normalised float32 partial (m in log2 units, l, O) per (chunk, query head)
+//    is written to the workspace. A second kernel merges the chunks (merge.hip).
+#include "fa_internal.hpp"
+#include "gfx950.hpp"
+
+namespace fa {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kPage = 16;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kTau = 8.f;  // lazy-rescale threshold, log2 units
+
+__device__ __forceinline__ float dpp_sum8(float x) {
+    // all-reduce over the 8 consecutive lanes of a half row
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false));
+    return x;
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+struct PageRegs {
+    u32x4 k[4];  // [half page][2 x 16 bytes]
+    u32x4 v[4];
+};
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ table,
+    const int32_t* __restrict__ lens, float* __restrict__ ws_o, float* __restrict__ ws_m,
+    float* __restrict__ ws_l, int Hq, int Hkv, int num_pages, int max_pages, int len_cap,
+    float scale_log2, int chunk_pages) {
+    __shared__ float sm_o[kWaves][G][kD];
+    __shared__ float sm_m[kWaves][G];
+    __shared__ float sm_l[kWaves][G];
+
+    const int split = blockIdx.x;
+    const int bk = blockIdx.y;
+    const int b = bk / Hkv;
+    const int kvh = bk - b * Hkv;
+    const int R = gridDim.y / Hkv * Hq;  // B * Hq
+    const int row0 = b * Hq + kvh * G;
+
+    int L = lens[b];
+    L = L < 0 ? 0 : (L > len_cap ? len_cap : L);
+    const int npages = (L + kPage - 1) / kPage;
+    const int p_begin = split * chunk_pages;
+    const int p_end = min_(npages, p_begin + chunk_pages);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int t8 = lane >> 3;
+    const int qs = lane & 7;
+
+    float acc[G][16];
+    float mref[G], lsum[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        mref[g] = -INFINITY;
+        lsum[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[g][e] = 0.f;
+    }
+
+    if (p_begin < p_end) {
+        uint32_t qw[G][8];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const u32x4* src =
+                reinterpret_cast<const u32x4*>(q + (size_t)(row0 + g) * kD + 16 * qs);
+            const u32x4 a = src[0], c = src[1];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                qw[g][w] = a[w];
+                qw[g][4 + w] = c[w];
+            }
+        }
+
+        // pages of this wave: p_begin + wave + 4*i, i < n_mine
+        const int n_mine = (p_end - p_begin - wave + kWaves - 1) / kWaves;
+        const size_t kv_stride = (size_t)Hkv * kPage * kD;  // elements per physical page
+        const size_t head_off = (size_t)kvh * kPage * kD;
+        const int tok_off = t8 * kD + 16 * qs;             // element offset inside a half page
+        const int32_t* trow = table + (size_t)b * max_pages;
+
+        int entry = -1;
+        auto phys_of = [&](int i) -> int {
+            // block-table entries are fetched 64 at a time and broadcast with readlane
+            const int slot = i & 63;
+            if (slot == 0) {
+                const int pi = p_begin + wave + kWaves * (i + lane);
+                entry = (i + lane < n_mine) ? trow[pi] : -1;
+            }
+            return __builtin_amdgcn_readlane(entry, slot);
+        };
+        auto load_page = [&](int phys, PageRegs& r) {
+            if (phys < 0 || phys >= num_pages) {  // never dereferenced; contributes nothing
+#pragma unroll
+                for (int i = 0; i < 4; ++i) r.k[i] = r.v[i] = u32x4{0, 0, 0, 0};
+                return;
+            }
+            const size_t base = (size_t)phys * kv_stride + head_off + tok_off;
+            const uint16_t* kp = kc + base;
+            const uint16_t* vp = vc + base;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                r.k[2 * half] = *reinterpret_cast<const u32x4*>(kp + half * 8 * kD);
+                r.k[2 * half + 1] = *reinterpret_cast<const u32x4*>(kp + half * 8 * kD + 8);
+                r.v[2 * half] = *reinterpret_cast<const u32x4*>(vp + half * 8 * kD);
+                r.v[2 * half + 1] = *reinterpret_cast<const u32x4*>(vp + half * 8 * kD + 8);
+            }
+        };
+
+        PageRegs cur;
+        int phys_cur = n_mine > 0 ? phys_of(0) : -1;
+        if (n_mine > 0) load_page(phys_cur, cur);
+
+        for (int i = 0; i < n_mine; ++i) {
+            PageRegs nxt;
+            int phys_nxt = -1;
+            if (i + 1 < n_mine) {
+                phys_nxt = phys_of(i + 1);
+                load_page(phys_nxt, nxt);
+            }
+            const int pidx = p_begin + wave + kWaves * i;
+            const bool ok = phys_cur >= 0 && phys_cur < num_pages;
+            if (ok) {
+                const bool tail = (pidx + 1) * kPage > L;
+                bool valid[2];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    valid[half] = pidx * kPage + 8 * half + t8 < L;
+                    if (tail && !valid[half]) {
+                        cur.k[2 * half] = u32x4{0, 0, 0, 0};
+                        cur.k[2 * half + 1] = u32x4{0, 0, 0, 0};
+                        cur.v[2 * half] = u32x4{0, 0, 0, 0};
+                        cur.v[2 * half + 1] = u32x4{0, 0, 0, 0};
+                    }
+                }
+                float s[2][G];
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        float d0 = 0.f;
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) d0 = dot2_bf16(cur.k[2 * half][w], qw[g][w], d0);
+#pragma unroll
+                        for (int w = 0; w < 4; ++w)
+                            d0 = dot2_bf16(cur.k[2 * half + 1][w], qw[g][4 + w], d0);
+                        s[half][g] = d0;
+                    }
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const float t = dpp_sum8(s[half][g]) * scale_log2;
+                        s[half][g] = (tail && !valid[half]) ? -INFINITY : t;
+                    }
+
+                float pr[2][G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const float smax = fmaxf(s[0][g], s[1][g]);
+                    if (smax > mref[g] + kTau) {
+                        const float alpha = exp2_hw(mref[g] - smax);
+                        lsum[g] *= alpha;
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) acc[g][e] *= alpha;
+                        mref[g] = smax;
+                    }
+#pragma unroll
+                    for (int half = 0; half < 2; ++half)
+                        pr[half][g] = (s[half][g] == -INFINITY) ? 0.f : exp2_hw(s[half][g] - mref[g]);
+                    lsum[g] += pr[0][g] + pr[1][g];
+                }
+
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int w = 0; w < 8; ++w) {
+                        const uint32_t word = cur.v[2 * half + (w >> 2)][w & 3];
+                        const float v0 = bf16_lo(word), v1 = bf16_hi(word);
+#pragma unroll
+                        for (int g = 0; g < G; ++g) {
+                            acc[g][2 * w] = __builtin_fmaf(pr[half][g], v0, acc[g][2 * w]);
+                            acc[g][2 * w + 1] = __builtin_fmaf(pr[half][g], v1, acc[g][2 * w + 1]);
+                        }
+                    }
+            }
+            if (i + 1 < n_mine) {
+                cur = nxt;
+                phys_cur = phys_nxt;
+            }
+        }
+    }
+
+    // ---- merge the 8 token slots of the wave (lanes with equal qs) ----
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float mw = mref[g];
+        mw = fmaxf(mw, __shfl_xor(mw, 8));
+        mw = fmaxf(mw, __shfl_xor(mw, 16));
+        mw = fmaxf(mw, __shfl_xor(mw, 32));
+        const float f = (mref[g] == -INFINITY) ? 0.f : exp2_hw(mref[g] - mw);
+        float lw = lsum[g] * f;
+        lw += __shfl_xor(lw, 8);
+        lw += __shfl_xor(lw, 16);
+        lw += __shfl_xor(lw, 32);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            float x = acc[g][e] * f;
+            x += __shfl_xor(x, 8);
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
+            acc[g][e] = x;
+        }
+        if (t8 == 0) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sm_o[wave][g][16 * qs + e] = acc[g][e];
+        }
+        if (lane == 0) {
+            sm_m[wave][g] = mw;
+            sm_l[wave][g] = lw;
+        }
+    }
+    __syncthreads();
+
+    // ---- merge the waves and write this chunk's normalised partial ----
+    for (int idx = tid; idx < G * kD; idx += kThreads) {
+        const int g = idx / kD;
+        const int d = idx - g * kD;
+        float m = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+            if (sm_l[w][g] > 0.f) m = fmaxf(m, sm_m[w][g]);
+        float lt = 0.f, ot = 0.f;
+        if (m != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float wt = sm_l[w][g] > 0.f ? sm_l[w][g] * exp2_hw(sm_m[w][g] - m) : 0.f;
+                lt += wt;
+                ot = __builtin_fmaf(wt, sm_o[w][g][d], ot);
+            }
+        }
+        const size_t prow = (size_t)split * R + row0 + g;
+        ws_o[prow * kD + d] = lt > 0.f ? ot / lt : 0.f;
+        if (d == 0) {
+            ws_m[prow] = lt > 0.f ? m : -INFINITY;
+            ws_l[prow] = lt;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, void* o,
+                              int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
+                              int len_cap, float scale, int splits, int chunk_pages,
+                              float* ws_o, float* ws_m, float* ws_l, hipStream_t stream) {
+    (void)d;
+    const dim3 grid((unsigned)splits, (unsigned)(B * Hkv));
+    const float sl2 = scale * kLog2e;
+    auto qp = static_cast<const uint16_t*>(q);
+    auto kp = static_cast<const uint16_t*>(k_cache);
+    auto vp = static_cast<const uint16_t*>(v_cache);
+    const int G = Hq / Hkv;
+#define FA_DECODE_LAUNCH(GG)                                                                     \
+    hipLaunchKernelGGL(decode_bf16_kernel<GG>, grid, dim3(kThreads), 0, stream, qp, kp, vp,      \
+                       block_table, seq_lens, ws_o, ws_m, ws_l, Hq, Hkv, num_pages,             \
+                       max_pages_per_seq, len_cap, sl2, chunk_pages)
+    switch (G) {
+        case 1: FA_DECODE_LAUNCH(1); break;
+        case 2: FA_DECODE_LAUNCH(2); break;
+        case 4: FA_DECODE_LAUNCH(4); break;
+        default: FA_DECODE_LAUNCH(8); break;
+    }
+#undef FA_DECODE_LAUNCH
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_merge(ws_o, ws_m, ws_l, o, 1, nullptr, nullptr, splits, B * Hq, kD, 1, stream);
+}
+
+}  // namespace fa

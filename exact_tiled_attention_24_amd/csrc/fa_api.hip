@@ -1,0 +1,164 @@
+// fa_api.hip - the C ABI declared in include/fa.h: argument validation, split planning and
+// kernel dispatch. Validation happens before any HIP call, so a rejected request neither
+// touches the device nor needs one.
+#include <math.h>
+
+#include "fa.h"
+#include "fa_internal.hpp"
+
+namespace {
+
+constexpr int kDecodePage = 16;
+constexpr int kDecodeD = 128;
+constexpr int kDecodeTargetWGs = 4 * fa::kPlanCUs;  // enough chunks to fill every CU a few times
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+
+struct DecodePlan {
+    int splits;        // chunks actually launched for the longest sequence
+    int chunk_pages;   // pages per chunk
+    int len_cap;       // lengths are clamped to this
+    int bound;         // upper bound of `splits` over every Hkv >= 1 and shorter tables
+};
+
+// Chunks for the longest sequence: enough workgroups to fill the CUs several times, since
+// with few (sequence, KV head) pairs most CUs would otherwise idle; never more chunks than
+// pages. A fixed plan keeps results deterministic.
+DecodePlan plan_decode(int B, int Hkv, int max_pages_per_seq, int max_seq_len, int num_splits) {
+    DecodePlan p;
+    const long long cap = (long long)max_pages_per_seq * kDecodePage;
+    p.len_cap = (int)(max_seq_len < cap ? max_seq_len : cap);
+    const int pages = (p.len_cap + kDecodePage - 1) / kDecodePage;
+    int s;
+    if (num_splits > 0) {
+        s = num_splits;
+    } else {
+        const long long units = (long long)B * Hkv;
+        s = units > 0 ? (int)((kDecodeTargetWGs + units - 1) / units) : 1;
+    }
+    if (s > pages) s = pages;
+    if (s < 1) s = 1;
+    p.bound = s;
+    p.chunk_pages = pages > 0 ? (pages + s - 1) / s : 1;
+    p.splits = pages > 0 ? (pages + p.chunk_pages - 1) / p.chunk_pages : 1;
+    return p;
+}
+
+size_t decode_ws_bytes(int B, int Hq, int d, int splits) {
+    return (size_t)splits * (size_t)B * (size_t)Hq * ((size_t)d + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+    switch (s) {
+        case FA_OK: return "FA_OK: success";
+        case FA_ERR_INVALID_ARGUMENT: return "FA_ERR_INVALID_ARGUMENT: invalid argument";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: no kernel for this request";
+        case FA_ERR_WORKSPACE_TOO_SMALL: return "FA_ERR_WORKSPACE_TOO_SMALL: workspace too small";
+        case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error at launch";
+    }
+    return "unknown fa_status";
+}
+
+fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void* o,
+                 float* m_out, float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
+                 int causal, void* stream) {
+    if (dt != FA_F32 && dt != FA_BF16) return FA_ERR_INVALID_ARGUMENT;
+    if (B < 0 || Hq < 0 || Hkv < 0 || N < 0) return FA_ERR_INVALID_ARGUMENT;
+    if (!scale_ok(scale)) return FA_ERR_INVALID_ARGUMENT;
+    if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0)) return FA_ERR_INVALID_ARGUMENT;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || Hq == 0 || N == 0) return FA_OK;
+    if (!q || !k || !v || !o) return FA_ERR_INVALID_ARGUMENT;
+    if ((long long)N * d >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    const long long rows_per_wg = dt == FA_BF16 ? 128 : 64;
+    if (((long long)N + rows_per_wg - 1) / rows_per_wg * B * Hq >= (1LL << 31))
+        return FA_ERR_UNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dt == FA_BF16) {
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+            return FA_ERR_INVALID_ARGUMENT;
+        e = fa::launch_fwd_bf16(q, k, v, o, m_out, l_out, B, Hq, Hkv, N, d, scale, causal ? 1 : 0,
+                                st);
+    } else {
+        e = fa::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                               static_cast<const float*>(v), static_cast<float*>(o), m_out, l_out,
+                               B, Hq, Hkv, N, d, scale, causal ? 1 : 0, st);
+    }
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_decode_plan_splits(int B, int Hkv, int page_size, int max_seq_len) {
+    if (B < 0 || Hkv < 1 || page_size != kDecodePage || max_seq_len < 0) return 0;
+    const int pages = (max_seq_len + kDecodePage - 1) / kDecodePage;
+    return plan_decode(B, Hkv, pages, max_seq_len, 0).splits;
+}
+
+size_t fa_decode_workspace_bytes(int B, int Hq, int d, int page_size, int max_seq_len,
+                                 int num_splits) {
+    if (B < 0 || Hq < 1 || d < 1 || page_size != kDecodePage || max_seq_len < 0 || num_splits < 0)
+        return 0;
+    // The split count falls as B * Hkv or the table width grows, and the launched count never
+    // exceeds the pre-rounding count, so planning with Hkv = 1 and a table wide enough for
+    // max_seq_len bounds the splits of every valid call with these sizes.
+    const int pages = (max_seq_len + kDecodePage - 1) / kDecodePage;
+    const DecodePlan p = plan_decode(B, 1, pages, max_seq_len, num_splits);
+    return decode_ws_bytes(B, Hq, d, p.bound);
+}
+
+fa_status fa_decode_splitk(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* seq_lens, void* o, int B,
+                           int Hq, int Hkv, int d, int page_size, int num_pages,
+                           int max_pages_per_seq, int max_seq_len, float scale, int num_splits,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    if (dt != FA_F32 && dt != FA_BF16) return FA_ERR_INVALID_ARGUMENT;
+    if (B < 0 || Hq < 1 || Hkv < 1 || d < 1 || page_size < 1 || num_pages < 0 ||
+        max_pages_per_seq < 0 || max_seq_len < 0 || num_splits < 0)
+        return FA_ERR_INVALID_ARGUMENT;
+    if (Hq % Hkv != 0) return FA_ERR_INVALID_ARGUMENT;
+    if (!scale_ok(scale)) return FA_ERR_INVALID_ARGUMENT;
+    const int G = Hq / Hkv;
+    if (dt != FA_BF16 || d != kDecodeD || page_size != kDecodePage ||
+        (G != 1 && G != 2 && G != 4 && G != 8))
+        return FA_ERR_UNSUPPORTED;
+    if (B == 0) return FA_OK;
+    if (!q || !o || !block_table || !seq_lens || !workspace) return FA_ERR_INVALID_ARGUMENT;
+    if (num_pages > 0 && (!k_cache || !v_cache)) return FA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+        !aligned16(workspace))
+        return FA_ERR_INVALID_ARGUMENT;
+    if ((long long)B * Hkv >= 65536) return FA_ERR_UNSUPPORTED;
+    const DecodePlan p = plan_decode(B, Hkv, max_pages_per_seq, max_seq_len, num_splits);
+    const size_t need = decode_ws_bytes(B, Hq, d, p.splits);
+    if (workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
+    float* ws_o = static_cast<float*>(workspace);
+    float* ws_m = ws_o + (size_t)p.splits * B * Hq * d;
+    float* ws_l = ws_m + (size_t)p.splits * B * Hq;
+    const hipError_t e = fa::launch_decode_bf16(
+        q, k_cache, v_cache, block_table, seq_lens, o, B, Hq, Hkv, d, num_pages,
+        max_pages_per_seq, p.len_cap, scale, p.splits, p.chunk_pages, ws_o, ws_m, ws_l,
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_merge(fa_dtype out_dt, const float* o_parts, const float* m_parts,
+                   const float* l_parts, void* o, float* m_out, float* l_out, int S, int R, int d,
+                   void* stream) {
+    if (out_dt != FA_F32 && out_dt != FA_BF16) return FA_ERR_INVALID_ARGUMENT;
+    if (S < 1 || R < 0 || d < 1) return FA_ERR_INVALID_ARGUMENT;
+    if (d > 1024) return FA_ERR_UNSUPPORTED;
+    if (R == 0) return FA_OK;
+    if (!o_parts || !m_parts || !l_parts || !o) return FA_ERR_INVALID_ARGUMENT;
+    if ((long long)S * R * d >= (1LL << 40)) return FA_ERR_UNSUPPORTED;
+    const hipError_t e = fa::launch_merge(o_parts, m_parts, l_parts, o, out_dt == FA_BF16 ? 1 : 0,
+                                          m_out, l_out, S, R, d, 0,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,37 @@
+// fa_internal.hpp - launchers shared between the C ABI layer and the kernel files.
+// Every launcher assumes arguments were validated by the caller (fa_api.hip) and only
+// enqueues kernels on `stream`; it returns hipGetLastError() after the launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Number of compute units the split plan targets (MI355X: 256 CUs in 8 XCDs).
+constexpr int kPlanCUs = 256;
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* m_out,
+                           float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
+                           int causal, hipStream_t stream);
+
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* m_out,
+                          float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
+                          int causal, hipStream_t stream);
+
+// Split-K paged decode: writes float32 partials (log2-domain m) for `splits` chunks of
+// `chunk_pages` pages per (sequence, KV head) into the workspace, then merges them into o.
+hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, void* o,
+                              int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
+                              int len_cap, float scale, int splits, int chunk_pages,
+                              float* ws_o, float* ws_m, float* ws_l, hipStream_t stream);
+
+// Row-wise merge of S partials. log2_units != 0: m is in log2 units (internal workspace);
+// otherwise natural-log units (public fa_merge). out_bf16 selects the output type.
+hipError_t launch_merge(const float* o_parts, const float* m_parts, const float* l_parts, void* o,
+                        int out_bf16, float* m_out, float* l_out, int S, int R, int d,
+                        int log2_units, hipStream_t stream);
+
+}  // namespace fa

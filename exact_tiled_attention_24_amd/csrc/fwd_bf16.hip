@@ -1,0 +1,303 @@
+// fwd_bf16.hip - tiled attention forward, bf16 in / bf16 out, on the gfx950 matrix cores.
+//
+// Method: "FlashAttention" (shubhamtatvamasi.com), "The trick: tiles and an online softmax":
+// Q is split into row blocks and K/V into column blocks; each score tile lives only on chip
+// and is folded into a running row maximum m, running sum l and rescaled accumulator O, and
+// the block's output is O / l. Scheduling follows the FlashAttention-2 row of the family
+// table on the same page (parallel over query blocks; normalise once at the end). Causal
+// tiles strictly above the diagonal are never loaded ("The trick", streaming demo).
+//
+// CDNA4 design (one workgroup = 4 waves = 128 query rows; one K/V tile = 64 keys):
+//  * Each wave owns 32 query rows and computes the TRANSPOSED score tile S^T = K Q^T with
+//    v_mfma_f32_32x32x16_bf16, so every lane holds the scores of ONE query row: the row
+//    maximum and row sum are in-lane reductions plus one exchange with lane l ^ 32.
+//  * The S^T accumulator is converted to bf16 in registers and used directly as the B
+//    operand of O^T += V^T P^T. K rows are fetched in a permuted order (bits 2 and 3 of the
+//    row index swapped) so that the accumulator's register order already equals the key
+//    order the second MFMA expects; no LDS round trip for P.
+//  * K is staged in LDS row-major, V transposed ([d][key]); both with an XOR swizzle of the
+//    16-byte chunk index so the MFMA operand reads are bank-conflict free. The next tile is
+//    prefetched into registers while the current one is consumed (double-buffered LDS, one
+//    barrier per tile).
+//  * Scores are kept in the log2 domain: p = exp2(s * scale * log2(e) - m), one FMA and one
+//    v_exp_f32 per score. The O rescale is skipped when no row maximum moved.
+//  * Grid: one workgroup per (query block, head). The linear order puts the heaviest causal
+//    query blocks first, and heads sharing a KV head (GQA) and all query blocks of one head
+//    on the same XCD (workgroups are dealt round-robin over the 8 XCDs), so K/V tiles are
+//    re-read from that XCD's L2.
+#include "fa_internal.hpp"
+#include "gfx950.hpp"
+
+namespace fa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBr = 32 * kWaves;  // query rows per workgroup
+constexpr int kBc = 64;           // keys per tile
+
+// Row permutation within each 16-row group: swap bits 2 and 3.
+__device__ __forceinline__ int kappa(int m) {
+    return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+template <int D>
+struct Tile {
+    static constexpr int kChunks = D / 8;                          // 16-byte chunks per K row
+    static constexpr int kKBytes = kBc * D * 2;
+    static constexpr int kVBytes = D * kBc * 2;
+    static constexpr int kStage = kKBytes + kVBytes;
+    static constexpr int kKLoads = kBc * kChunks / kThreads;       // 16-byte loads per thread
+    static constexpr int kVKeys = kBc * kChunks / kThreads;        // keys per thread (V)
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, float* __restrict__ m_out, float* __restrict__ l_out, int B, int Hq,
+    int Hkv, int N, float scale_log2, int causal, int nqb) {
+    using T = Tile<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::kStage];
+
+    // ---- work item: heaviest query block first; GQA groups and heads XCD-local ----
+    const int BH = B * Hq;
+    const int rank = blockIdx.x / BH;
+    const int p = blockIdx.x - rank * BH;
+    const int qb = causal ? (nqb - 1 - rank) : rank;
+    const int G = Hq / Hkv;
+    const int nKV = B * Hkv;
+    const int kvg = p % nKV;
+    const int gi = p / nKV;
+    const int b = kvg / Hkv;
+    const int kvh = kvg - b * Hkv;
+    const int h = kvh * G + gi;
+
+    const size_t qoff = ((size_t)(b * Hq + h) * N) * D;
+    const size_t koff = ((size_t)(b * Hkv + kvh) * N) * D;
+    const uint16_t* qh = q + qoff;
+    const uint16_t* kh = k + koff;
+    const uint16_t* vh = v + koff;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+
+    const int row0 = qb * kBr + wave * 32;  // first query row of this wave
+    const int qrow = row0 + l32;            // the query row this lane's column holds
+
+    // ---- Q^T fragments (B operand), kept in registers for the whole kernel ----
+    bf16x8 qf[D / 16];
+    {
+        const uint16_t* src = qh + (size_t)min_(qrow, N - 1) * D + 8 * hh;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            qf[kk] = *reinterpret_cast<const bf16x8*>(src + 16 * kk);
+    }
+
+    f32x16 acc_o[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) acc_o[i] = f32x16{};
+    float m_run = -INFINITY;  // running max of scale*log2(e)*s for row qrow
+    float l_part = 0.f;       // running sum over this lane's half of every tile
+
+    const int kv_end = causal ? min_(N, qb * kBr + kBr) : N;
+    const int n_tiles = (kv_end + kBc - 1) / kBc;
+
+    // ---- global -> register staging of one K/V tile ----
+    u32x4 kreg[T::kKLoads];
+    u32x4 vreg[T::kVKeys];
+    auto load_tile = [&](int j) {
+        const int kv0 = j * kBc;
+#pragma unroll
+        for (int i = 0; i < T::kKLoads; ++i) {
+            const int c = tid + kThreads * i;
+            const int r = c / T::kChunks;
+            const int ch = c - r * T::kChunks;
+            const int key = min_(kv0 + r, N - 1);
+            kreg[i] = *reinterpret_cast<const u32x4*>(kh + (size_t)key * D + ch * 8);
+        }
+        const int dc = tid % T::kChunks;
+        const int kg = tid / T::kChunks;
+#pragma unroll
+        for (int i = 0; i < T::kVKeys; ++i) {
+            const int key = min_(kv0 + kg * T::kVKeys + i, N - 1);
+            vreg[i] = *reinterpret_cast<const u32x4*>(vh + (size_t)key * D + dc * 8);
+        }
+    };
+    auto store_tile = [&](int buf) {
+        unsigned char* ks = smem + buf * T::kStage;
+        unsigned char* vs = ks + T::kKBytes;
+#pragma unroll
+        for (int i = 0; i < T::kKLoads; ++i) {
+            const int c = tid + kThreads * i;
+            const int r = c / T::kChunks;
+            const int ch = c - r * T::kChunks;
+            const int sw = kappa(r & 15) & (T::kChunks - 1);
+            *reinterpret_cast<u32x4*>(ks + r * (D * 2) + ((ch ^ sw) << 4)) = kreg[i];
+        }
+        // V transposed: thread holds kVKeys consecutive keys x 8 consecutive d.
+        const int dc = tid % T::kChunks;
+        const int kg = tid / T::kChunks;
+        const int key0 = kg * T::kVKeys;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int d = dc * 8 + e;
+            const int chunk = key0 >> 3;
+            unsigned char* dst = vs + d * (kBc * 2) + ((chunk ^ (d & 7)) << 4) + (key0 & 7) * 2;
+            uint32_t w[T::kVKeys / 2];
+#pragma unroll
+            for (int i = 0; i < T::kVKeys / 2; ++i) {
+                const uint32_t a = vreg[2 * i][e >> 1];
+                const uint32_t c2 = vreg[2 * i + 1][e >> 1];
+                w[i] = (e & 1) ? ((a >> 16) | (c2 & 0xffff0000u)) : ((a & 0xffffu) | (c2 << 16));
+            }
+            if constexpr (T::kVKeys == 4) {
+                *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+            } else {
+                *reinterpret_cast<uint32_t*>(dst) = w[0];
+            }
+        }
+    };
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int j = 0; j < n_tiles; ++j) {
+        const bool has_next = j + 1 < n_tiles;
+        if (has_next) load_tile(j + 1);
+
+        const int kv0 = j * kBc;
+        const bool active = !causal || kv0 <= row0 + 31;
+        if (active) {
+            const unsigned char* ks = smem + (j & 1) * T::kStage;
+            const unsigned char* vs = ks + T::kKBytes;
+
+            // S^T = K Q^T for two 32-key blocks.
+            f32x16 s[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int krow = 32 * kb + kappa(l32);
+                const int sw = (l32 & 15) & (T::kChunks - 1);
+                const unsigned char* base = ks + krow * (D * 2);
+                f32x16 acc = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) {
+                    const bf16x8 a =
+                        *reinterpret_cast<const bf16x8*>(base + (((2 * kk + hh) ^ sw) << 4));
+                    acc = mfma_32x32x16(a, qf[kk], acc);
+                }
+                s[kb] = acc;
+            }
+
+            // Mask: causal diagonal tiles and the ragged key tail.
+            const bool need_mask = (causal && kv0 + kBc - 1 > row0) || (kv0 + kBc > N);
+            if (need_mask) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kv0 + 32 * kb + 16 * (r >> 3) + 8 * hh + (r & 7);
+                        const bool bad = key >= N || (causal && key > qrow);
+                        s[kb][r] = bad ? -INFINITY : s[kb][r];
+                    }
+            }
+
+            // Online softmax (log2 domain).
+            float mx = s[0][0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+            mx = pair32_max(mx);
+            const float m_new = fmaxf(m_run, mx * scale_log2);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = exp2_hw(m_run - m_use);
+            m_run = m_new;
+
+            uint32_t pk[2][8];
+            float rs = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const float p0 = exp2_hw(__builtin_fmaf(s[kb][r], scale_log2, -m_use));
+                    const float p1 = exp2_hw(__builtin_fmaf(s[kb][r + 1], scale_log2, -m_use));
+                    rs += p0 + p1;
+                    pk[kb][r >> 1] = pack_bf16x2(p0, p1);
+                }
+            l_part = l_part * alpha + rs;
+
+            if (__any(alpha != 1.f)) {
+#pragma unroll
+                for (int i = 0; i < D / 32; ++i) acc_o[i] *= alpha;
+            }
+
+            // O^T += V^T P^T.
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    u32x4 pw = {pk[kb][4 * t], pk[kb][4 * t + 1], pk[kb][4 * t + 2], pk[kb][4 * t + 3]};
+                    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+                    const int chunk = 4 * kb + 2 * t + hh;
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {
+                        const int d = 32 * db + l32;
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                            vs + d * (kBc * 2) + ((chunk ^ (d & 7)) << 4));
+                        acc_o[db] = mfma_32x32x16(a, pb, acc_o[db]);
+                    }
+                }
+        }
+
+        if (has_next) store_tile((j + 1) & 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O / l, bf16, and the optional row statistics ----
+    const float l_tot = pair32_sum(l_part);
+    if (qrow < N) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        uint16_t* dst = o + qoff + (size_t)qrow * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * db + 8 * g + 4 * hh;
+                u32x2 w = {pack_bf16x2(acc_o[db][4 * g] * inv, acc_o[db][4 * g + 1] * inv),
+                           pack_bf16x2(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv)};
+                *reinterpret_cast<u32x2*>(dst + d) = w;
+            }
+        if (hh == 0) {
+            const size_t ridx = (size_t)(b * Hq + h) * N + qrow;
+            if (m_out) m_out[ridx] = (l_tot > 0.f) ? m_run * kLn2 : -INFINITY;
+            if (l_out) l_out[ridx] = l_tot;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* m_out,
+                           float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
+                           int causal, hipStream_t stream) {
+    const int nqb = (N + kBr - 1) / kBr;
+    const long long grid = (long long)nqb * B * Hq;
+    const float sl2 = scale * kLog2e;
+    auto qp = static_cast<const uint16_t*>(q);
+    auto kp = static_cast<const uint16_t*>(k);
+    auto vp = static_cast<const uint16_t*>(v);
+    auto op = static_cast<uint16_t*>(o);
+    if (d == 128)
+        hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                           qp, kp, vp, op, m_out, l_out, B, Hq, Hkv, N, sl2, causal, nqb);
+    else
+        hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                           qp, kp, vp, op, m_out, l_out, B, Hq, Hkv, N, sl2, causal, nqb);
+    return hipGetLastError();
+}
+
+}  // namespace fa

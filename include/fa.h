@@ -1,0 +1,132 @@
+/*
+ * fa.h - C ABI of libfa.so: exact tiled attention on AMD Instinct MI355X (gfx950).
+ *
+ * Three operations, each exact attention O = softmax(scale * Q K^T + M) V computed without
+ * ever writing the N x N score matrix to device memory:
+ *
+ *   fa_fwd            tiled forward with the online softmax (running max m, running sum l,
+ *                     rescaled accumulator O); "FlashAttention" (shubhamtatvamasi.com),
+ *                     "The trick: tiles and an online softmax", and "FlashAttention,
+ *                     explained." (vibeengines.com), the forward-pass statement.
+ *   fa_decode_splitk  single-query decode over a paged KV cache read through a block table,
+ *                     with the KV sequence split across workgroups and the partial (m, l, O)
+ *                     results merged; "FlashAttention", "Decode is a different problem" and
+ *                     the FlashAttention-family table (Flash-Decoding, paged variants).
+ *   fa_merge          merge of partial (m, l, O) results over disjoint key sets with the
+ *                     online-softmax rescale; "FlashAttention", "Decode is a different problem".
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library allocates
+ *     and frees nothing; the decode workspace is passed in by the caller.
+ *   - Tensors are dense and row-major (C-contiguous) in the shapes stated per function.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls enqueue work
+ *     on it and return; they never synchronise the device.
+ *   - Arguments are validated on the host before any HIP call; a rejected call launches
+ *     nothing and returns FA_ERR_INVALID_ARGUMENT or FA_ERR_UNSUPPORTED. A failed launch
+ *     returns FA_ERR_HIP. Nothing is thrown across the ABI.
+ *   - m is reported in natural-log units: m = max_j (scale * q.k_j); l = sum_j exp(s_j - m).
+ *     A row with no admissible key yields O = 0, m = -inf, l = 0.
+ *   - Results are deterministic: the same inputs give bitwise-identical outputs.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARGUMENT = 1,   /* NULL pointer, negative size, bad scale, ... */
+    FA_ERR_UNSUPPORTED = 2,        /* valid request this build has no kernel for */
+    FA_ERR_WORKSPACE_TOO_SMALL = 3,
+    FA_ERR_HIP = 4                 /* the HIP runtime reported an error at launch */
+} fa_status;
+
+typedef enum {
+    FA_F32 = 0,   /* IEEE binary32 */
+    FA_BF16 = 1   /* bfloat16 (round-to-nearest-even on output) */
+} fa_dtype;
+
+/*
+ * fa_fwd - tiled attention forward (prefill).
+ *
+ *   q, o : [B, Hq, N, d]   in `dt`
+ *   k, v : [B, Hkv, N, d]  in `dt`; query head h reads key/value head h / (Hq / Hkv)
+ *   m_out, l_out : optional float32 [B, Hq, N] row statistics (NULL = not written)
+ *
+ * causal != 0 admits key j for query i iff j <= i (diagonal included); tiles entirely above
+ * the diagonal are never loaded. The 1/sqrt(d) scale of the pages is passed as `scale`
+ * (must be finite and > 0).
+ * dt = FA_BF16: bf16 inputs, float32 accumulation and softmax, bf16 output.
+ * dt = FA_F32: float32 throughout.
+ * Supported: d in {64, 128}; Hq % Hkv == 0; N * d < 2^31. B, Hq or N equal to 0 is a
+ * valid empty call (nothing is launched).
+ */
+fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void* o,
+                 float* m_out, float* l_out, int B, int Hq, int Hkv, int N, int d,
+                 float scale, int causal, void* stream);
+
+/*
+ * fa_decode_splitk - one query token per sequence against its paged KV cache.
+ *
+ *   q, o        : [B, Hq, d] bf16
+ *   k_cache,
+ *   v_cache     : [num_pages, Hkv, page_size, d] bf16; token t of sequence b lives in
+ *                 physical page block_table[b][t / page_size], slot t % page_size
+ *   block_table : int32 [B, max_pages_per_seq], device memory
+ *   seq_lens    : int32 [B], device memory; every key of the sequence is admissible
+ *   max_seq_len : host-side upper bound of seq_lens, used to plan the KV split
+ *   num_splits  : 0 = automatic; otherwise the number of KV chunks the longest sequence is
+ *                 split into (clamped to [1, pages of the longest sequence])
+ *   workspace   : device scratch of at least fa_decode_workspace_bytes(...) bytes holding
+ *                 the float32 partial (m, l, O) of every chunk; contents on entry are ignored
+ *
+ * Caller preconditions that are not checked on the device: seq_lens[b] <= max_seq_len, and
+ * block_table[b][p] in [0, num_pages) for p < ceil(seq_lens[b] / page_size). The kernel
+ * clamps each length to min(max_seq_len, max_pages_per_seq * page_size) and never
+ * dereferences a table entry outside [0, num_pages) (such a page contributes nothing), so
+ * a violated precondition gives a wrong result, never an out-of-bounds access. Table
+ * entries past a sequence's last page are never read. A sequence of length 0 gets O = 0.
+ * Supported: dt = FA_BF16; d = 128; page_size = 16; 1 <= Hq / Hkv <= 8; Hq % Hkv == 0.
+ */
+fa_status fa_decode_splitk(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* seq_lens, void* o,
+                           int B, int Hq, int Hkv, int d, int page_size, int num_pages,
+                           int max_pages_per_seq, int max_seq_len, float scale, int num_splits,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_decode_splitk needs for these sizes (0 for an invalid request). */
+size_t fa_decode_workspace_bytes(int B, int Hq, int d, int page_size, int max_seq_len,
+                                 int num_splits);
+
+/* The number of KV chunks the automatic plan gives the longest sequence (0 if invalid). */
+int fa_decode_plan_splits(int B, int Hkv, int page_size, int max_seq_len);
+
+/*
+ * fa_merge - merge S partial results over disjoint key sets, row by row.
+ *
+ *   o_parts : float32 [S, R, d], each partial normalised (O_s = sum p v / l_s)
+ *   m_parts, l_parts : float32 [S, R], natural-log units as above
+ *   o       : [R, d] in `out_dt` (FA_F32 or FA_BF16)
+ *   m_out, l_out : optional float32 [R] merged statistics (NULL = not written)
+ *
+ * With m = max_s m_s and w_s = l_s * exp(m_s - m): l = sum_s w_s, O = sum_s w_s O_s / l.
+ * A partial with l_s = 0 carries no weight. Supported: S >= 1, 1 <= d <= 1024.
+ * R == 0 is a valid empty call.
+ */
+fa_status fa_merge(fa_dtype out_dt, const float* o_parts, const float* m_parts,
+                   const float* l_parts, void* o, float* m_out, float* l_out, int S, int R,
+                   int d, void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* fa_status_string(fa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

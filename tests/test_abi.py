@@ -1,0 +1,165 @@
+"""The C ABI of libfa.so on the host (CPU only, no kernel launches).
+
+Checks that the library loads, exports every function include/fa.h declares, and rejects
+bad requests with the documented status codes. Validation runs before any HIP call, so none
+of these calls touches a device.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_tiled_attention_24_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fa.LIB_PATH),
+                                reason="libfa.so not built (run the package build first)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("fa_fwd", "fa_decode_splitk", "fa_merge", "fa_status_string",
+              "fa_decode_workspace_bytes", "fa_decode_plan_splits"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in fa.h but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)", out))
+    assert set(declared_functions()) <= exported
+    # C linkage: no mangled names for the entry points
+    assert not any(s.startswith("_Z") and "fa_fwd" in s for s in out.split())
+
+
+def test_status_strings():
+    for code in range(5):
+        assert fa.fa_status_string(code).startswith("FA_")
+    assert "unknown" in fa.fa_status_string(99)
+
+
+NULL = None
+DEV = ctypes.c_void_p(0x1000)  # an aligned, never dereferenced fake pointer
+MIS = ctypes.c_void_p(0x1002)  # misaligned
+
+
+def fwd(lib, dt=1, q=DEV, k=DEV, v=DEV, o=DEV, B=1, Hq=2, Hkv=1, N=8, d=64, scale=0.125, causal=1):
+    return lib.fa_fwd(dt, q, k, v, o, None, None, B, Hq, Hkv, N, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(dt=7), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(B=-1), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(N=-5), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(Hq=3, Hkv=2), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(Hkv=0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(o=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(k=MIS), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(N=1 << 24, d=128), fa.FA_ERR_UNSUPPORTED),
+    # empty problems are valid no-ops, even with NULL pointers
+    (dict(B=0, q=NULL, k=NULL, v=NULL, o=NULL), fa.FA_OK),
+    (dict(N=0, q=NULL), fa.FA_OK),
+    (dict(Hq=0, Hkv=0), fa.FA_OK),
+])
+def test_fwd_validation(kwargs, code):
+    assert fwd(fa.load_library(), **kwargs) == code
+
+
+def decode(lib, dt=1, q=DEV, kc=DEV, vc=DEV, table=DEV, lens=DEV, o=DEV, B=2, Hq=8, Hkv=2, d=128,
+           page=16, num_pages=10, max_pages=5, max_len=80, scale=0.08, splits=0, ws=DEV,
+           ws_bytes=1 << 30):
+    return lib.fa_decode_splitk(dt, q, kc, vc, table, lens, o, B, Hq, Hkv, d, page, num_pages,
+                                max_pages, max_len, scale, splits, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(dt=5), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(dt=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(page=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=2), fa.FA_ERR_UNSUPPORTED),   # group of 3 query heads per KV head
+    (dict(Hq=7, Hkv=2), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(Hq=32, Hkv=2), fa.FA_ERR_UNSUPPORTED),  # group of 16
+    (dict(B=-1), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(num_pages=-1), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(splits=-2), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(max_len=-1), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(table=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(lens=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(ws=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(kc=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(q=MIS), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(ws_bytes=16), fa.FA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(B=0, q=NULL, o=NULL), fa.FA_OK),
+])
+def test_decode_validation(kwargs, code):
+    assert decode(fa.load_library(), **kwargs) == code
+
+
+def test_decode_workspace_and_plan():
+    # the auto plan fills the chip with (sequence, KV head, chunk) workgroups
+    s = fa.fa_decode_plan_splits(8, 8, 16, 32768)
+    assert 1 <= s <= 2048
+    assert fa.fa_decode_plan_splits(1, 1, 16, 16) == 1  # never more chunks than pages
+    assert fa.fa_decode_plan_splits(8, 8, 32, 100) == 0  # unsupported page size
+    need = fa.fa_decode_workspace_bytes(8, 32, 128, 16, 32768, 0)
+    assert need >= s * 8 * 32 * 130 * 4
+    assert fa.fa_decode_workspace_bytes(8, 32, 128, 16, 32768, 5) == 5 * 8 * 32 * 130 * 4
+    assert fa.fa_decode_workspace_bytes(8, 32, 128, 16, 32768, -1) == 0
+    # the exact workspace is accepted by validation (rejected by nothing but a bad argument)
+    lib = fa.load_library()
+    exact = fa.fa_decode_workspace_bytes(2, 8, 128, 16, 80, 3)
+    assert decode(lib, splits=3, ws_bytes=exact - 1) == fa.FA_ERR_WORKSPACE_TOO_SMALL
+
+
+def merge(lib, dt=0, op=DEV, mp=DEV, lp=DEV, o=DEV, S=4, R=8, d=128):
+    return lib.fa_merge(dt, op, mp, lp, o, None, None, S, R, d, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(dt=9), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(S=0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(R=-1), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(d=0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(d=2048), fa.FA_ERR_UNSUPPORTED),
+    (dict(op=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(o=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(R=0, op=NULL, o=NULL), fa.FA_OK),
+])
+def test_merge_validation(kwargs, code):
+    assert merge(fa.load_library(), **kwargs) == code
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, q, q)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        fa.load_library(str(tmp_path / "libfa.so"))

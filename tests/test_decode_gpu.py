@@ -1,0 +1,135 @@
+"""fa_decode_splitk on the GPU against the float64 oracle (parity tests, through the C ABI)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import exact_tiled_attention_24_amd as fa
+from exact_tiled_attention_24_amd import inputs as gen
+from helpers import assert_close, cuda_device, log_case, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return cuda_device()
+
+
+def upload(x: gen.DecodeInputs, dev):
+    import torch
+
+    return dict(
+        q=gen.to_torch(x.q, "bf16", dev),
+        k_cache=gen.to_torch(x.k_cache, "bf16", dev),
+        v_cache=gen.to_torch(x.v_cache, "bf16", dev),
+        block_table=torch.from_numpy(x.block_table).to(dev),
+        seq_lens=torch.from_numpy(x.lens.astype(np.int32)).to(dev),
+    )
+
+
+def run_decode(t, max_seq_len, scale, num_splits=0):
+    import torch
+
+    o = fa.fa_decode_splitk(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["seq_lens"],
+                            max_seq_len, scale=scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o
+
+
+SMALL = [
+    # B, Hq, Hkv, lens
+    (3, 8, 8, [1, 16, 17]),
+    (4, 8, 4, [15, 100, 255, 256]),
+    (3, 16, 4, [1000, 4097, 33]),
+    (2, 16, 2, [2000, 5]),
+    (5, 32, 8, [16, 31, 1, 640, 2049]),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"B{c[0]}-Hq{c[1]}-Hkv{c[2]}")
+@pytest.mark.parametrize("splits", [0, 1, 2, 7])
+def test_decode_small(case, splits, dev):
+    B, Hq, Hkv, lens = case
+    seed = 200 + SMALL.index(case)
+    log_case(f"fa_decode_splitk small {case} splits={splits} seed={seed}")
+    x = gen.decode_inputs(B, Hq, Hkv, 128, 16, seed=seed, lens=lens,
+                          max_pages_per_seq=-(-max(lens) // 16) + 3)
+    t = upload(x, dev)
+    o = run_decode(t, x.max_seq_len, x.scale, splits)
+    o_ref, _, _ = oracle.decode(x.q, x.k_seqs, x.v_seqs, x.scale)
+    assert_close(to_np(o), o_ref, "bf16", "decode O")
+
+
+def test_decode_config5_full(dev):
+    import torch
+
+    cfg = gen.CONFIGS[5]
+    log_case(f"fa_decode_splitk config: {cfg.name}")
+    x = gen.config_decode_inputs(cfg)
+    t = upload(x, dev)
+    o = run_decode(t, cfg.len_max, x.scale)
+    o2 = run_decode(t, cfg.len_max, x.scale)
+    assert torch.equal(o, o2), "two runs differ: the kernel is not deterministic"
+    o_ref, _, _ = oracle.decode(x.q, x.k_seqs, x.v_seqs, x.scale)
+    assert_close(to_np(o), o_ref, "bf16", "config 5 O")
+    for s in (1, 7):
+        log_case(f"fa_decode_splitk config 5 num_splits={s}")
+        assert_close(to_np(run_decode(t, cfg.len_max, x.scale, s)), o_ref, "bf16", f"splits={s}")
+    del t, o, o2
+    torch.cuda.empty_cache()
+
+
+def test_decode_physical_page_order_does_not_matter(dev):
+    """Moving pages to other physical slots (and fixing the table) gives bitwise the same O."""
+    import torch
+
+    log_case("fa_decode_splitk page permutation")
+    x = gen.decode_inputs(4, 16, 4, 128, 16, seed=301, lens=[700, 1, 64, 333])
+    t1 = upload(x, dev)
+    o1 = run_decode(t1, x.max_seq_len, x.scale)
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(x.num_pages)  # old slot -> new slot
+    k2 = np.empty_like(x.k_cache)
+    v2 = np.empty_like(x.v_cache)
+    k2[perm] = x.k_cache
+    v2[perm] = x.v_cache
+    table2 = np.where(x.block_table >= 0, perm[np.maximum(x.block_table, 0)], -1).astype(np.int32)
+    x2 = gen.DecodeInputs(x.lens, x.q, x.k_seqs, x.v_seqs, k2, v2, table2, 16, x.scale)
+    o2 = run_decode(upload(x2, dev), x.max_seq_len, x.scale)
+    assert torch.equal(o1, o2)
+
+
+def test_decode_zero_length_sequence(dev):
+    log_case("fa_decode_splitk zero length")
+    x = gen.decode_inputs(3, 8, 2, 128, 16, seed=302, lens=[0, 40, 0], max_pages_per_seq=4)
+    o = to_np(run_decode(upload(x, dev), 40, x.scale))
+    assert np.all(o[0] == 0) and np.all(o[2] == 0)
+    o_ref, _, _ = oracle.decode(x.q, x.k_seqs, x.v_seqs, x.scale)
+    assert_close(o[1], o_ref[1], "bf16", "decode O")
+
+
+def test_decode_equals_last_row_of_causal_prefill(dev):
+    """The one decode query is the newest token: same result as the last prefill row."""
+    import torch
+
+    log_case("fa_decode_splitk vs fa_fwd last row")
+    L, Hq, Hkv = 777, 8, 2
+    xf = gen.fwd_inputs(1, Hq, Hkv, L, 128, seed=303, dtype="bf16", causal=True)
+    o_f = fa.fa_fwd(gen.to_torch(xf.q, "bf16", dev), gen.to_torch(xf.k, "bf16", dev),
+                    gen.to_torch(xf.v, "bf16", dev), causal=True)
+    xd = gen.decode_inputs(1, Hq, Hkv, 128, 16, seed=303, lens=[L])
+    # overwrite the drawn sequence with the prefill's K/V and last query row
+    npg = -(-L // 16)
+    for cache, seq in ((xd.k_cache, xf.k[0]), (xd.v_cache, xf.v[0])):
+        padded = np.full((Hkv, npg * 16, 128), np.nan, np.float32)
+        padded[:, :L] = seq
+        cache[xd.block_table[0, :npg]] = padded.reshape(Hkv, npg, 16, 128).transpose(1, 0, 2, 3)
+    xd.q[0] = xf.q[0, :, L - 1]
+    o_d = run_decode(upload(xd, dev), L, xd.scale)
+    torch.cuda.synchronize()
+    last = to_np(o_f)[0, :, L - 1]
+    got = to_np(o_d)[0]
+    np.testing.assert_allclose(got, last, atol=2e-2, rtol=1e-2)
+    ref, _, _ = oracle.attention(xf.q[:, :, L - 1:], xf.k, xf.v, xf.scale, causal=False)
+    assert_close(got, ref[0, :, 0], "bf16", "decode vs oracle")
