@@ -70,36 +70,47 @@ def main():
     fa.load_library()  # fails loudly if the HIP library is missing
     props = torch.cuda.get_device_properties(dev)
 
+    do_fwd = args.only in (None, "fwd")
+    do_dec = args.only in (None, "decode")
+
     # ---- inputs, resident in HBM ----
     fcfg = gen.CONFIGS[args.fwd_config]
-    fx = gen.config_fwd_inputs(fcfg)
-    q = gen.to_torch(fx.q, "bf16", dev)
-    k = gen.to_torch(fx.k, "bf16", dev)
-    v = gen.to_torch(fx.v, "bf16", dev)
-    o = torch.empty_like(q)
-    fwd_flops = fcfg.flops()
-
     dcfg = gen.CONFIGS[5]
-    dx = gen.config_decode_inputs(dcfg)
-    dq = gen.to_torch(dx.q, "bf16", dev)
-    kc = gen.to_torch(dx.k_cache, "bf16", dev)
-    vc = gen.to_torch(dx.v_cache, "bf16", dev)
-    table = torch.from_numpy(dx.block_table).to(dev)
-    lens = torch.from_numpy(dx.lens.astype(np.int32)).to(dev)
-    do = torch.empty_like(dq)
-    ws_bytes = fa.fa_decode_workspace_bytes(dcfg.B, dcfg.Hq, dcfg.d, 16, dcfg.len_max,
-                                            args.decode_splits)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    splits = args.decode_splits or fa.fa_decode_plan_splits(dcfg.B, dcfg.Hkv, 16, dcfg.len_max)
-    dec_bytes = (dx.kv_bytes() + dq.numel() * 2 + do.numel() * 2
-                 + 4 * int(sum(-(-int(L) // 16) for L in dx.lens)) + 4 * dcfg.B)
-    del dx.k_cache, dx.v_cache
+    fwd_flops = fcfg.flops()
+    fx = None
+    if do_fwd or not args.no_cpu_baseline:
+        fx = gen.config_fwd_inputs(fcfg)
+    if do_fwd:
+        q = gen.to_torch(fx.q, "bf16", dev)
+        k = gen.to_torch(fx.k, "bf16", dev)
+        v = gen.to_torch(fx.v, "bf16", dev)
+        o = torch.empty_like(q)
+
+    dec_bytes, splits, lens_sum = None, None, None
+    if do_dec:
+        dx = gen.config_decode_inputs(dcfg)
+        dq = gen.to_torch(dx.q, "bf16", dev)
+        kc = gen.to_torch(dx.k_cache, "bf16", dev)
+        vc = gen.to_torch(dx.v_cache, "bf16", dev)
+        table = torch.from_numpy(dx.block_table).to(dev)
+        lens = torch.from_numpy(dx.lens.astype(np.int32)).to(dev)
+        do = torch.empty_like(dq)
+        ws_bytes = fa.fa_decode_workspace_bytes(dcfg.B, dcfg.Hq, dcfg.d, 16, dcfg.len_max,
+                                                args.decode_splits)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        splits = args.decode_splits or fa.fa_decode_plan_splits(dcfg.B, dcfg.Hkv, 16,
+                                                                dcfg.len_max)
+        lens_sum = int(dx.lens.sum())
+        dec_bytes = (dx.kv_bytes() + dq.numel() * 2 + do.numel() * 2
+                     + 4 * int(sum(-(-int(L) // 16) for L in dx.lens)) + 4 * dcfg.B)
+        dec_scale = dx.scale
+        del dx
 
     def run_fwd():
         fa.fa_fwd(q, k, v, scale=fx.scale, causal=fcfg.causal, out=o)
 
     def run_decode():
-        fa.fa_decode_splitk(dq, kc, vc, table, lens, dcfg.len_max, scale=dx.scale,
+        fa.fa_decode_splitk(dq, kc, vc, table, lens, dcfg.len_max, scale=dec_scale,
                             num_splits=args.decode_splits, out=do, workspace=ws)
 
     copy_src = copy_dst = None
@@ -108,8 +119,6 @@ def main():
         copy_dst = torch.empty_like(copy_src)
 
     stream = torch.cuda.current_stream(dev)
-    do_fwd = args.only in (None, "fwd")
-    do_dec = args.only in (None, "decode")
     for _ in range(args.warmup):
         if do_fwd:
             run_fwd()
@@ -161,7 +170,7 @@ def main():
             "fwd": {"B": fcfg.B, "Hq": fcfg.Hq, "Hkv": fcfg.Hkv, "N": fcfg.N, "d": fcfg.d,
                     "causal": fcfg.causal, "algorithmic_flops": fwd_flops},
             "decode": {"B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv, "d": dcfg.d, "page": 16,
-                       "seq_lens_sum": int(dx.lens.sum()), "splits": splits,
+                       "seq_lens_sum": lens_sum, "splits": splits,
                        "algorithmic_bytes": dec_bytes},
             "device": props.name, "cus": props.multi_processor_count,
         },
@@ -179,7 +188,7 @@ def main():
             "value": round(dec_gbps, 1) if dec_gbps else None,
             "unit": "GB/s",
             "tokens_per_s": round(dcfg.B / (dec_ms.mean() * 1e-3), 1) if do_dec else None,
-            "kv_tokens_per_s": round(float(dx.lens.sum()) / (dec_ms.mean() * 1e-3), 1) if do_dec else None,
+            "kv_tokens_per_s": round(lens_sum / (dec_ms.mean() * 1e-3), 1) if do_dec else None,
             "roofline": {
                 "bound": "hbm",
                 "achieved": round(dec_gbps, 1) if dec_gbps else None,
@@ -192,7 +201,7 @@ def main():
         },
         "fwd_tokens_per_s": round(fcfg.B * fcfg.N / (fwd_ms.mean() * 1e-3), 1) if do_fwd else None,
     }
-    if not args.no_cpu_baseline and do_fwd:
+    if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(fx, fcfg, args.cpu_heads)
     print(json.dumps(result), flush=True)
 

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
     const int p_end = min_(npages, p_begin + chunk_pages);
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
     const int lane = tid & 63;
     const int t8 = lane >> 3;
     const int qs = lane & 7;
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
         for (int e = 0; e < 16; ++e) acc[g][e] = 0.f;
     }
 
-    if (p_begin < p_end) {
+    if (p_begin < p_end && num_pages > 0) {
         uint32_t qw[G][8];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -109,31 +109,24 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
                 qw[g][4 + w] = c[w];
             }
         }
+        // Complete the q loads before the page loop (see the note in fwd_bf16.hip).
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int w = 0; w < 8; ++w) asm volatile("" : "+v"(qw[g][w]));
 
         // pages of this wave: p_begin + wave + 4*i, i < n_mine
         const int n_mine = (p_end - p_begin - wave + kWaves - 1) / kWaves;
         const size_t kv_stride = (size_t)Hkv * kPage * kD;  // elements per physical page
-        const size_t head_off = (size_t)kvh * kPage * kD;
-        const int tok_off = t8 * kD + 16 * qs;             // element offset inside a half page
+        const size_t head_off = (size_t)kvh * kPage * kD + t8 * kD + 16 * qs;
         const int32_t* trow = table + (size_t)b * max_pages;
 
-        int entry = -1;
-        auto phys_of = [&](int i) -> int {
-            // block-table entries are fetched 64 at a time and broadcast with readlane
-            const int slot = i & 63;
-            if (slot == 0) {
-                const int pi = p_begin + wave + kWaves * (i + lane);
-                entry = (i + lane < n_mine) ? trow[pi] : -1;
-            }
-            return __builtin_amdgcn_readlane(entry, slot);
-        };
+        // Loads are issued unconditionally (an invalid table entry reads page 0 and is
+        // masked out arithmetically), so every page costs the same 8 loads and the waits
+        // before consuming a buffer are exact.
         auto load_page = [&](int phys, PageRegs& r) {
-            if (phys < 0 || phys >= num_pages) {  // never dereferenced; contributes nothing
-#pragma unroll
-                for (int i = 0; i < 4; ++i) r.k[i] = r.v[i] = u32x4{0, 0, 0, 0};
-                return;
-            }
-            const size_t base = (size_t)phys * kv_stride + head_off + tok_off;
+            const bool ok = phys >= 0 && phys < num_pages;
+            const size_t base = (size_t)(ok ? phys : 0) * kv_stride + head_off;
             const uint16_t* kp = kc + base;
             const uint16_t* vp = vc + base;
 #pragma unroll
@@ -144,87 +137,99 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
                 r.v[2 * half + 1] = *reinterpret_cast<const u32x4*>(vp + half * 8 * kD + 8);
             }
         };
-
-        PageRegs cur;
-        int phys_cur = n_mine > 0 ? phys_of(0) : -1;
-        if (n_mine > 0) load_page(phys_cur, cur);
-
-        for (int i = 0; i < n_mine; ++i) {
-            PageRegs nxt;
-            int phys_nxt = -1;
-            if (i + 1 < n_mine) {
-                phys_nxt = phys_of(i + 1);
-                load_page(phys_nxt, nxt);
-            }
+        // Consumes one page. Invalid tokens (past the sequence end, or an invalid table entry)
+        // get s = -inf and their V is replaced by 0 at use; the loaded registers are never
+        // overwritten, so no wait is needed beyond the page's own loads.
+        auto process = [&](const PageRegs& cur, int phys, int i) {
             const int pidx = p_begin + wave + kWaves * i;
-            const bool ok = phys_cur >= 0 && phys_cur < num_pages;
-            if (ok) {
-                const bool tail = (pidx + 1) * kPage > L;
-                bool valid[2];
+            const bool page_ok = phys >= 0 && phys < num_pages;
+            const bool tail = !page_ok || (pidx + 1) * kPage > L;  // wave-uniform
+            bool valid[2];
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    valid[half] = pidx * kPage + 8 * half + t8 < L;
-                    if (tail && !valid[half]) {
-                        cur.k[2 * half] = u32x4{0, 0, 0, 0};
-                        cur.k[2 * half + 1] = u32x4{0, 0, 0, 0};
-                        cur.v[2 * half] = u32x4{0, 0, 0, 0};
-                        cur.v[2 * half + 1] = u32x4{0, 0, 0, 0};
-                    }
-                }
-                float s[2][G];
+            for (int half = 0; half < 2; ++half)
+                valid[half] = page_ok && pidx * kPage + 8 * half + t8 < L;
+            float s[2][G];
 #pragma unroll
-                for (int half = 0; half < 2; ++half)
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        float d0 = 0.f;
-#pragma unroll
-                        for (int w = 0; w < 4; ++w) d0 = dot2_bf16(cur.k[2 * half][w], qw[g][w], d0);
-#pragma unroll
-                        for (int w = 0; w < 4; ++w)
-                            d0 = dot2_bf16(cur.k[2 * half + 1][w], qw[g][4 + w], d0);
-                        s[half][g] = d0;
-                    }
-#pragma unroll
-                for (int half = 0; half < 2; ++half)
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        const float t = dpp_sum8(s[half][g]) * scale_log2;
-                        s[half][g] = (tail && !valid[half]) ? -INFINITY : t;
-                    }
-
-                float pr[2][G];
+            for (int half = 0; half < 2; ++half)
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const float smax = fmaxf(s[0][g], s[1][g]);
-                    if (smax > mref[g] + kTau) {
-                        const float alpha = exp2_hw(mref[g] - smax);
-                        lsum[g] *= alpha;
+                    float d0 = 0.f;
 #pragma unroll
-                        for (int e = 0; e < 16; ++e) acc[g][e] *= alpha;
-                        mref[g] = smax;
-                    }
+                    for (int w = 0; w < 4; ++w) d0 = dot2_bf16(cur.k[2 * half][w], qw[g][w], d0);
 #pragma unroll
-                    for (int half = 0; half < 2; ++half)
-                        pr[half][g] = (s[half][g] == -INFINITY) ? 0.f : exp2_hw(s[half][g] - mref[g]);
-                    lsum[g] += pr[0][g] + pr[1][g];
+                    for (int w = 0; w < 4; ++w)
+                        d0 = dot2_bf16(cur.k[2 * half + 1][w], qw[g][4 + w], d0);
+                    s[half][g] = d0;
+                }
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const float t = dpp_sum8(s[half][g]) * scale_log2;
+                    s[half][g] = (tail && !valid[half]) ? -INFINITY : t;
                 }
 
+            float pr[2][G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float smax = fmaxf(s[0][g], s[1][g]);
+                if (smax > mref[g] + kTau) {
+                    const float alpha = exp2_hw(mref[g] - smax);
+                    lsum[g] *= alpha;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[g][e] *= alpha;
+                    mref[g] = smax;
+                }
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+                    pr[half][g] = (s[half][g] == -INFINITY) ? 0.f : exp2_hw(s[half][g] - mref[g]);
+                lsum[g] += pr[0][g] + pr[1][g];
+            }
+
+            auto accumulate = [&](bool masked) {
 #pragma unroll
                 for (int half = 0; half < 2; ++half)
 #pragma unroll
                     for (int w = 0; w < 8; ++w) {
                         const uint32_t word = cur.v[2 * half + (w >> 2)][w & 3];
-                        const float v0 = bf16_lo(word), v1 = bf16_hi(word);
+                        float v0 = bf16_lo(word), v1 = bf16_hi(word);
+                        if (masked) {
+                            v0 = valid[half] ? v0 : 0.f;
+                            v1 = valid[half] ? v1 : 0.f;
+                        }
 #pragma unroll
                         for (int g = 0; g < G; ++g) {
                             acc[g][2 * w] = __builtin_fmaf(pr[half][g], v0, acc[g][2 * w]);
                             acc[g][2 * w + 1] = __builtin_fmaf(pr[half][g], v1, acc[g][2 * w + 1]);
                         }
                     }
-            }
-            if (i + 1 < n_mine) {
-                cur = nxt;
-                phys_cur = phys_nxt;
+            };
+            if (tail)
+                accumulate(true);
+            else
+                accumulate(false);
+        };
+
+        for (int g0 = 0; g0 < n_mine; g0 += 64) {
+            // block-table entries of up to 64 pages, broadcast later with v_readlane
+            const int cnt = min_(64, n_mine - g0);
+            int entry = lane < cnt ? trow[p_begin + wave + kWaves * (g0 + lane)] : -1;
+            asm volatile("" : "+v"(entry));
+            // Ping-pong page buffers. Every iteration issues both prefetches (re-reading the
+            // current page when there is no next one, an L2 hit), so the number of loads in
+            // flight is the same on every path and each buffer is waited for exactly.
+            PageRegs ra, rb;
+            int pa = __builtin_amdgcn_readlane(entry, 0);
+            load_page(pa, ra);
+            for (int i = 0; i < cnt; i += 2) {
+                const bool has_b = i + 1 < cnt;
+                const int pb = has_b ? __builtin_amdgcn_readlane(entry, min_(i + 1, 63)) : pa;
+                load_page(pb, rb);
+                process(ra, pa, g0 + i);
+                const int pn = i + 2 < cnt ? __builtin_amdgcn_readlane(entry, min_(i + 2, 63)) : pb;
+                load_page(pn, ra);
+                if (has_b) process(rb, pb, g0 + i + 1);
+                pa = pn;
             }
         }
     }
@@ -272,9 +277,10 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
         if (m != -INFINITY) {
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
-                const float wt = sm_l[w][g] > 0.f ? sm_l[w][g] * exp2_hw(sm_m[w][g] - m) : 0.f;
-                lt += wt;
-                ot = __builtin_fmaf(wt, sm_o[w][g][d], ot);
+                // sm_o and sm_l are unnormalised sums relative to the wave's own maximum
+                const float rs = sm_l[w][g] > 0.f ? exp2_hw(sm_m[w][g] - m) : 0.f;
+                lt = __builtin_fmaf(rs, sm_l[w][g], lt);
+                ot = __builtin_fmaf(rs, sm_o[w][g][d], ot);
             }
         }
         const size_t prow = (size_t)split * R + row0 + g;

@@ -16,15 +16,15 @@
 //    row index swapped) so that the accumulator's register order already equals the key
 //    order the second MFMA expects; no LDS round trip for P.
 //  * K is staged in LDS row-major, V transposed ([d][key]); both with an XOR swizzle of the
-//    16-byte chunk index so the MFMA operand reads are bank-conflict free. The next tile is
+//    16-byte chunk index so that the MFMA operand reads and the staging writes are free of
+//    bank conflicts on gfx950's LDS (64 banks of 4 bytes, 128 bytes per cycle). The next tile is
 //    prefetched into registers while the current one is consumed (double-buffered LDS, one
 //    barrier per tile).
 //  * Scores are kept in the log2 domain: p = exp2(s * scale * log2(e) - m), one FMA and one
 //    v_exp_f32 per score. The O rescale is skipped when no row maximum moved.
-//  * Grid: one workgroup per (query block, head). The linear order puts the heaviest causal
-//    query blocks first, and heads sharing a KV head (GQA) and all query blocks of one head
-//    on the same XCD (workgroups are dealt round-robin over the 8 XCDs), so K/V tiles are
-//    re-read from that XCD's L2.
+//  * Grid: one workgroup per (query block, head). Each XCD gets a contiguous run of work
+//    items ordered by KV head, so it streams about one head's K/V at a time from its own
+//    L2; query heads sharing a KV head (GQA) run together; heaviest causal blocks first.
 #include "fa_internal.hpp"
 #include "gfx950.hpp"
 
@@ -35,6 +35,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;  // query rows per workgroup
 constexpr int kBc = 64;           // keys per tile
+constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
 
 // Row permutation within each 16-row group: swap bits 2 and 3.
 __device__ __forceinline__ int kappa(int m) {
@@ -48,8 +49,15 @@ struct Tile {
     static constexpr int kVBytes = D * kBc * 2;
     static constexpr int kStage = kKBytes + kVBytes;
     static constexpr int kKLoads = kBc * kChunks / kThreads;       // 16-byte loads per thread
-    static constexpr int kVKeys = kBc * kChunks / kThreads;        // keys per thread (V)
+    static constexpr int kVQuads = D / 4;                          // 4-column groups per V row
+    static constexpr int kVKeys = kBc * kVQuads / kThreads;        // keys per thread (V): 8 or 4
 };
+
+// XOR swizzle of the 16-byte chunk index of row d of the transposed V tile. Under the LDS
+// banking measured on gfx950 (64 banks of 4 bytes, 128 bytes per cycle) it keeps both the
+// MFMA operand reads (8 consecutive rows per cycle) and the transposed writes (rows
+// 4q + j for 8 consecutive q per cycle) conflict free.
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 2) & 7) ^ ((d & 3) << 1); }
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
@@ -59,15 +67,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     using T = Tile<D>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::kStage];
 
-    // ---- work item: heaviest query block first; GQA groups and heads XCD-local ----
-    const int BH = B * Hq;
-    const int rank = blockIdx.x / BH;
-    const int p = blockIdx.x - rank * BH;
-    const int qb = causal ? (nqb - 1 - rank) : rank;
+    // ---- work item ----
+    // Items are ordered (KV group, query block from the last to the first, head in group).
+    // Workgroups are dealt round-robin over the 8 XCDs, so XCD x receives ids x, x+8, ...;
+    // mapping its i-th workgroup to item x*per_xcd + i gives every XCD one contiguous run of
+    // items: it works through about one KV head at a time (K/V stay in its L2), the query
+    // heads sharing that KV head run side by side, and within a head the heaviest causal
+    // query blocks come first.
     const int G = Hq / Hkv;
-    const int nKV = B * Hkv;
-    const int kvg = p % nKV;
-    const int gi = p / nKV;
+    const int per_unit = nqb * G;
+    const int total = B * Hkv * per_unit;
+    const int per_xcd = (total + kXcds - 1) / kXcds;
+    const int item = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    if (item >= total) return;
+    const int kvg = item / per_unit;
+    const int rem = item - kvg * per_unit;
+    const int qb = causal ? (nqb - 1 - rem / G) : rem / G;
+    const int gi = rem - (rem / G) * G;
     const int b = kvg / Hkv;
     const int kvh = kvg - b * Hkv;
     const int h = kvh * G + gi;
@@ -79,7 +95,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const uint16_t* vh = v + koff;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
@@ -95,6 +111,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         for (int kk = 0; kk < D / 16; ++kk)
             qf[kk] = *reinterpret_cast<const bf16x8*>(src + 16 * kk);
     }
+    // Complete the Q loads here: the empty asm redefines the fragments, so the wait for the
+    // loads lands before the loop. Otherwise the loop header merges "possibly pending" state
+    // from before the loop and every tile's MFMAs wait on that tile's K/V prefetch instead.
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(qf[kk]));
 
     f32x16 acc_o[D / 32];
 #pragma unroll
@@ -107,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
     // ---- global -> register staging of one K/V tile ----
     u32x4 kreg[T::kKLoads];
-    u32x4 vreg[T::kVKeys];
+    u32x2 vreg[T::kVKeys];
     auto load_tile = [&](int j) {
         const int kv0 = j * kBc;
 #pragma unroll
@@ -118,12 +139,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             const int key = min_(kv0 + r, N - 1);
             kreg[i] = *reinterpret_cast<const u32x4*>(kh + (size_t)key * D + ch * 8);
         }
-        const int dc = tid % T::kChunks;
-        const int kg = tid / T::kChunks;
+        // V: thread holds kVKeys consecutive keys x 4 consecutive columns (8-byte loads;
+        // 32 or 16 consecutive lanes cover one whole row)
+        const int dq = tid % T::kVQuads;
+        const int kg = tid / T::kVQuads;
 #pragma unroll
         for (int i = 0; i < T::kVKeys; ++i) {
             const int key = min_(kv0 + kg * T::kVKeys + i, N - 1);
-            vreg[i] = *reinterpret_cast<const u32x4*>(vh + (size_t)key * D + dc * 8);
+            vreg[i] = *reinterpret_cast<const u32x2*>(vh + (size_t)key * D + dq * 4);
         }
     };
     auto store_tile = [&](int buf) {
@@ -137,26 +160,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             const int sw = kappa(r & 15) & (T::kChunks - 1);
             *reinterpret_cast<u32x4*>(ks + r * (D * 2) + ((ch ^ sw) << 4)) = kreg[i];
         }
-        // V transposed: thread holds kVKeys consecutive keys x 8 consecutive d.
-        const int dc = tid % T::kChunks;
-        const int kg = tid / T::kChunks;
+        // V transposed: row d of the [d][key] tile gets this thread's kVKeys keys.
+        const int dq = tid % T::kVQuads;
+        const int kg = tid / T::kVQuads;
         const int key0 = kg * T::kVKeys;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int d = dc * 8 + e;
-            const int chunk = key0 >> 3;
-            unsigned char* dst = vs + d * (kBc * 2) + ((chunk ^ (d & 7)) << 4) + (key0 & 7) * 2;
+        for (int j = 0; j < 4; ++j) {
+            const int d = dq * 4 + j;
             uint32_t w[T::kVKeys / 2];
 #pragma unroll
             for (int i = 0; i < T::kVKeys / 2; ++i) {
-                const uint32_t a = vreg[2 * i][e >> 1];
-                const uint32_t c2 = vreg[2 * i + 1][e >> 1];
-                w[i] = (e & 1) ? ((a >> 16) | (c2 & 0xffff0000u)) : ((a & 0xffffu) | (c2 << 16));
+                const uint32_t a = vreg[2 * i][j >> 1];
+                const uint32_t c2 = vreg[2 * i + 1][j >> 1];
+                w[i] = (j & 1) ? ((a >> 16) | (c2 & 0xffff0000u)) : ((a & 0xffffu) | (c2 << 16));
             }
-            if constexpr (T::kVKeys == 4) {
-                *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+            unsigned char* dst = vs + d * (kBc * 2) + (((key0 >> 3) ^ vt_swz(d)) << 4) + (key0 & 7) * 2;
+            if constexpr (T::kVKeys == 8) {
+                *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
             } else {
-                *reinterpret_cast<uint32_t*>(dst) = w[0];
+                *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
             }
         }
     };
@@ -247,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                     for (int db = 0; db < D / 32; ++db) {
                         const int d = 32 * db + l32;
                         const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                            vs + d * (kBc * 2) + ((chunk ^ (d & 7)) << 4));
+                            vs + d * (kBc * 2) + ((chunk ^ vt_swz(d)) << 4));
                         acc_o[db] = mfma_32x32x16(a, pb, acc_o[db]);
                     }
                 }
@@ -285,7 +307,8 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
                            int causal, hipStream_t stream) {
     const int nqb = (N + kBr - 1) / kBr;
-    const long long grid = (long long)nqb * B * Hq;
+    const long long items = (long long)nqb * B * Hq;
+    const long long grid = (items + kXcds - 1) / kXcds * kXcds;
     const float sl2 = scale * kLog2e;
     auto qp = static_cast<const uint16_t*>(q);
     auto kp = static_cast<const uint16_t*>(k);

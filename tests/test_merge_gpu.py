@@ -35,7 +35,7 @@ def make_partials(S, R, d, seed, empty_frac=0.0):
     return o_p, m_p, l_p
 
 
-@pytest.mark.parametrize("S,R,d,empty", [(1, 7, 128, 0.0), (3, 50, 64, 0.0), (32, 256, 128, 0.3),
+@pytest.mark.parametrize("S,R,d,empty", [(1, 7, 128, 0.0), (3, 50, 64, 0.0), (32, 256, 128, 0.3), (3, 11, 99, 0.2),
                                          (5, 9, 100, 0.5), (3000, 4, 128, 0.1)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_merge_random(S, R, d, empty, out, dev):
