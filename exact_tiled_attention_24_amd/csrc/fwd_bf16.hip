@@ -21,7 +21,8 @@
 //    prefetched into registers while the current one is consumed (double-buffered LDS, one
 //    barrier per tile).
 //  * Scores are kept in the log2 domain: p = exp2(s * scale * log2(e) - m), one FMA and one
-//    v_exp_f32 per score. The O rescale is skipped when no row maximum moved.
+//    v_exp_f32 per score. The exponent reference moves only when a row maximum beats it by
+//    more than 2^8, so the O rescale is rare.
 //  * Grid: one workgroup per (query block, head). Each XCD gets a contiguous run of work
 //    items ordered by KV head, so it streams about one head's K/V at a time from its own
 //    L2; query heads sharing a KV head (GQA) run together; heaviest causal blocks first.
@@ -36,6 +37,9 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;  // query rows per workgroup
 constexpr int kBc = 64;           // keys per tile
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr float kLazy = 8.f;      // reference-max slack (log2 units) before O is rescaled
+// Word 3 of a raw (untyped, unswizzled) buffer resource descriptor on gfx9-family GPUs.
+constexpr int kBufferDword3 = 0x00020000;
 
 // Row permutation within each 16-row group: swap bits 2 and 3.
 __device__ __forceinline__ int kappa(int m) {
@@ -121,59 +125,62 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) acc_o[i] = f32x16{};
     float m_run = -INFINITY;  // running max of scale*log2(e)*s for row qrow
+    float m_ref = -INFINITY;  // reference the exponentials are taken against (<= m_run)
     float l_part = 0.f;       // running sum over this lane's half of every tile
 
     const int kv_end = causal ? min_(N, qb * kBr + kBr) : N;
     const int n_tiles = (kv_end + kBc - 1) / kBc;
 
     // ---- global -> register staging of one K/V tile ----
+    // Buffer loads: each tile gets a scalar resource descriptor (base = the tile's first key,
+    // size = the keys left in the head), and every thread reads at offsets fixed for the
+    // whole kernel, so a load costs no vector address arithmetic. Keys past the head's end
+    // read as zero through the descriptor's range check (and are masked anyway).
     u32x4 kreg[T::kKLoads];
     u32x2 vreg[T::kVKeys];
+    const int k_r0 = tid / T::kChunks;               // K: rows k_r0 + (kThreads/kChunks)*i
+    const int k_ch = tid % T::kChunks;
+    const int v_dq = tid % T::kVQuads;                // V: keys v_kg*kVKeys + i, columns 4*v_dq..
+    const int v_kg = tid / T::kVQuads;
+    constexpr int kRowsPerLoad = kThreads / T::kChunks;
+    int k_boff[T::kKLoads];
+#pragma unroll
+    for (int i = 0; i < T::kKLoads; ++i) k_boff[i] = ((k_r0 + i * kRowsPerLoad) * D + k_ch * 8) * 2;
+    const int v_boff = (v_kg * T::kVKeys * D + v_dq * 4) * 2;
     auto load_tile = [&](int j) {
         const int kv0 = j * kBc;
+        const int bytes = min_(N - kv0, kBc) * D * 2;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(kh + (size_t)kv0 * D), (short)0, bytes, kBufferDword3);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(vh + (size_t)kv0 * D), (short)0, bytes, kBufferDword3);
 #pragma unroll
-        for (int i = 0; i < T::kKLoads; ++i) {
-            const int c = tid + kThreads * i;
-            const int r = c / T::kChunks;
-            const int ch = c - r * T::kChunks;
-            const int key = min_(kv0 + r, N - 1);
-            kreg[i] = *reinterpret_cast<const u32x4*>(kh + (size_t)key * D + ch * 8);
-        }
-        // V: thread holds kVKeys consecutive keys x 4 consecutive columns (8-byte loads;
-        // 32 or 16 consecutive lanes cover one whole row)
-        const int dq = tid % T::kVQuads;
-        const int kg = tid / T::kVQuads;
+        for (int i = 0; i < T::kKLoads; ++i)
+            kreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_boff[i], 0, 0));
 #pragma unroll
-        for (int i = 0; i < T::kVKeys; ++i) {
-            const int key = min_(kv0 + kg * T::kVKeys + i, N - 1);
-            vreg[i] = *reinterpret_cast<const u32x2*>(vh + (size_t)key * D + dq * 4);
-        }
+        for (int i = 0; i < T::kVKeys; ++i)
+            vreg[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, v_boff + i * D * 2, 0, 0));
     };
     auto store_tile = [&](int buf) {
         unsigned char* ks = smem + buf * T::kStage;
         unsigned char* vs = ks + T::kKBytes;
 #pragma unroll
         for (int i = 0; i < T::kKLoads; ++i) {
-            const int c = tid + kThreads * i;
-            const int r = c / T::kChunks;
-            const int ch = c - r * T::kChunks;
+            const int r = k_r0 + i * kRowsPerLoad;
             const int sw = kappa(r & 15) & (T::kChunks - 1);
-            *reinterpret_cast<u32x4*>(ks + r * (D * 2) + ((ch ^ sw) << 4)) = kreg[i];
+            *reinterpret_cast<u32x4*>(ks + r * (D * 2) + ((k_ch ^ sw) << 4)) = kreg[i];
         }
-        // V transposed: row d of the [d][key] tile gets this thread's kVKeys keys.
-        const int dq = tid % T::kVQuads;
-        const int kg = tid / T::kVQuads;
-        const int key0 = kg * T::kVKeys;
+        // V transposed: row d of the [d][key] tile gets this thread's kVKeys keys; each
+        // word pairs two keys of one column (one v_perm_b32).
+        const int key0 = v_kg * T::kVKeys;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int d = dq * 4 + j;
+            const int d = v_dq * 4 + j;
+            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
             uint32_t w[T::kVKeys / 2];
 #pragma unroll
-            for (int i = 0; i < T::kVKeys / 2; ++i) {
-                const uint32_t a = vreg[2 * i][j >> 1];
-                const uint32_t c2 = vreg[2 * i + 1][j >> 1];
-                w[i] = (j & 1) ? ((a >> 16) | (c2 & 0xffff0000u)) : ((a & 0xffffu) | (c2 << 16));
-            }
+            for (int i = 0; i < T::kVKeys / 2; ++i)
+                w[i] = __builtin_amdgcn_perm(vreg[2 * i + 1][j >> 1], vreg[2 * i][j >> 1], sel);
             unsigned char* dst = vs + d * (kBc * 2) + (((key0 >> 3) ^ vt_swz(d)) << 4) + (key0 & 7) * 2;
             if constexpr (T::kVKeys == 8) {
                 *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
@@ -233,11 +240,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-            mx = pair32_max(mx);
-            const float m_new = fmaxf(m_run, mx * scale_log2);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = exp2_hw(m_run - m_use);
-            m_run = m_new;
+            mx = pair32_max(mx) * scale_log2;
+            m_run = fmaxf(m_run, mx);
+            // Lazy rescale: p is taken relative to a reference m_ref that moves only when
+            // a row's maximum exceeds it by more than 2^8, so p <= 256 and the O rescale is
+            // rare. Exact up to rounding: the final O / l cancels the reference.
+            float alpha = 1.f;
+            const bool move = mx > m_ref + kLazy;
+            if (__any(move)) {
+                const float r_new = move ? mx : m_ref;
+                alpha = exp2_hw(m_ref - r_new);
+                m_ref = r_new;
+#pragma unroll
+                for (int i = 0; i < D / 32; ++i) acc_o[i] *= alpha;
+            }
+            const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
 
             uint32_t pk[2][8];
             float rs = 0.f;
@@ -251,11 +268,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                     pk[kb][r >> 1] = pack_bf16x2(p0, p1);
                 }
             l_part = l_part * alpha + rs;
-
-            if (__any(alpha != 1.f)) {
-#pragma unroll
-                for (int i = 0; i < D / 32; ++i) acc_o[i] *= alpha;
-            }
 
             // O^T += V^T P^T.
 #pragma unroll
@@ -296,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         if (hh == 0) {
             const size_t ridx = (size_t)(b * Hq + h) * N + qrow;
             if (m_out) m_out[ridx] = (l_tot > 0.f) ? m_run * kLn2 : -INFINITY;
-            if (l_out) l_out[ridx] = l_tot;
+            if (l_out) l_out[ridx] = (l_tot > 0.f) ? l_tot * exp2_hw(m_ref - m_run) : 0.f;
         }
     }
 }
