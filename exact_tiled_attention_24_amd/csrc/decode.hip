@@ -9,7 +9,7 @@
 //
 // CDNA4 design. The kernel is bound by HBM bandwidth (about 4 FLOP per byte of K/V), so it
 // is built around memory-level parallelism rather than the matrix cores:
-//  * grid = (chunk, sequence x KV head); one workgroup of 4 waves per chunk; wave w takes
+//  * grid = (sequence x KV head, chunk); one workgroup of 4 waves per chunk; wave w takes
 //    pages w, w+4, ... of its chunk. The G query heads that share a KV head are served by
 //    the same pass over the K/V bytes (each byte of the cache is read once per KV head).
 //  * lane l owns token slot l/8 of each 8-token half page and the 16 head dimensions
@@ -67,18 +67,24 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
     __shared__ float sm_m[kWaves][G];
     __shared__ float sm_l[kWaves][G];
 
-    const int split = blockIdx.x;
-    const int bk = blockIdx.y;
+    // x = sequence x KV head (KV head fastest: the KV heads of one page sit next to each
+    // other in memory and are streamed side by side), y = chunk
+    const int split = blockIdx.y;
+    const int bk = blockIdx.x;
     const int b = bk / Hkv;
     const int kvh = bk - b * Hkv;
-    const int R = gridDim.y / Hkv * Hq;  // B * Hq
+    const int R = gridDim.x / Hkv * Hq;  // B * Hq
     const int row0 = b * Hq + kvh * G;
 
     int L = lens[b];
     L = L < 0 ? 0 : (L > len_cap ? len_cap : L);
     const int npages = (L + kPage - 1) / kPage;
-    const int p_begin = split * chunk_pages;
-    const int p_end = min_(npages, p_begin + chunk_pages);
+    // This sequence gets ceil(npages / chunk_pages) chunks of near-equal size (they differ by
+    // at most one page), so the workgroups of one launch carry balanced work; splits past
+    // the sequence's chunk count are empty.
+    const int n_chunks = (npages + chunk_pages - 1) / chunk_pages;
+    const int p_begin = split < n_chunks ? (int)((long long)split * npages / n_chunks) : npages;
+    const int p_end = split < n_chunks ? (int)((long long)(split + 1) * npages / n_chunks) : npages;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -300,7 +306,7 @@ hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_
                               int len_cap, float scale, int splits, int chunk_pages,
                               float* ws_o, float* ws_m, float* ws_l, hipStream_t stream) {
     (void)d;
-    const dim3 grid((unsigned)splits, (unsigned)(B * Hkv));
+    const dim3 grid((unsigned)(B * Hkv), (unsigned)splits);
     const float sl2 = scale * kLog2e;
     auto qp = static_cast<const uint16_t*>(q);
     auto kp = static_cast<const uint16_t*>(k_cache);

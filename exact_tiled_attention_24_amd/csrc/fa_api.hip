@@ -2,6 +2,8 @@
 // kernel dispatch. Validation happens before any HIP call, so a rejected request neither
 // touches the device nor needs one.
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "fa.h"
 #include "fa_internal.hpp"
@@ -10,7 +12,17 @@ namespace {
 
 constexpr int kDecodePage = 16;
 constexpr int kDecodeD = 128;
-constexpr int kDecodeTargetWGs = 4 * fa::kPlanCUs;  // enough chunks to fill every CU a few times
+constexpr int kDecodeTargetWGs = 2 * fa::kPlanCUs;  // one round of 4-wave chunks
+
+// Forward kernel choice: the 32-rows-per-wave tiled kernel unless FA_FWD_KERNEL=pipe selects
+// the software-pipelined one (a tuning override, read once).
+bool use_pipelined_fwd() {
+    static const int choice = [] {
+        const char* e = getenv("FA_FWD_KERNEL");
+        return (e && strcmp(e, "pipe") == 0) ? 1 : 0;
+    }();
+    return choice != 0;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
@@ -45,6 +57,7 @@ DecodePlan plan_decode(int B, int Hkv, int max_pages_per_seq, int max_seq_len, i
     return p;
 }
 
+// Partials: O [S][B*Hq][d], then m [S][B*Hq], then l [S][B*Hq], all float32.
 size_t decode_ws_bytes(int B, int Hq, int d, int splits) {
     return (size_t)splits * (size_t)B * (size_t)Hq * ((size_t)d + 2) * sizeof(float);
 }
@@ -83,8 +96,11 @@ fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void*
     if (dt == FA_BF16) {
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
             return FA_ERR_INVALID_ARGUMENT;
-        e = fa::launch_fwd_bf16(q, k, v, o, m_out, l_out, B, Hq, Hkv, N, d, scale, causal ? 1 : 0,
-                                st);
+        e = use_pipelined_fwd()
+                ? fa::launch_fwd_bf16_pipe(q, k, v, o, m_out, l_out, B, Hq, Hkv, N, d, scale,
+                                           causal ? 1 : 0, st)
+                : fa::launch_fwd_bf16(q, k, v, o, m_out, l_out, B, Hq, Hkv, N, d, scale,
+                                      causal ? 1 : 0, st);
     } else {
         e = fa::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                static_cast<const float*>(v), static_cast<float*>(o), m_out, l_out,
@@ -132,7 +148,7 @@ fa_status fa_decode_splitk(fa_dtype dt, const void* q, const void* k_cache, cons
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
         !aligned16(workspace))
         return FA_ERR_INVALID_ARGUMENT;
-    if ((long long)B * Hkv >= 65536) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * Hkv >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
     const DecodePlan p = plan_decode(B, Hkv, max_pages_per_seq, max_seq_len, num_splits);
     const size_t need = decode_ws_bytes(B, Hq, d, p.splits);
     if (workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
