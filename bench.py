@@ -42,20 +42,147 @@ def parse():
     ap.add_argument("--fwd-config", type=int, default=3, choices=[2, 3, 4])
     ap.add_argument("--decode-splits", type=int, default=0, help="0 = the library's plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=2,
+    ap.add_argument("--cpu-heads", type=int, default=64,
                     help="heads of the forward workload the oracle is timed on")
     ap.add_argument("--only", choices=["fwd", "decode"], default=None,
                     help="time one kernel only (profiling runs)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DB", "WRITE_DB"), default=None,
+                    help="write profiles/traffic.json from FETCH_SIZE and WRITE_SIZE rocprofv3 "
+                         "databases of runs made with --copy-mib, and exit (no GPU needed)")
+    ap.add_argument("--summarize", nargs="+", metavar="DB", default=None,
+                    help="print per-kernel averages (duration, counters) of rocprofv3 result "
+                         "databases as markdown and exit (no GPU needed)")
+    ap.add_argument("--kernel", default=None, help="with --summarize: only kernels whose name contains one of these "
+                         "comma-separated fragments")
     return ap.parse_args()
+
+
+def summarize(paths, kernel=None):
+    """Per-kernel averages from rocprofv3 SQLite result databases, as markdown tables.
+
+    `kernel`: comma-separated name fragments; keep only kernels whose name contains one.
+    """
+    import collections
+    import sqlite3
+
+    def short(name):
+        name = name.replace("(anonymous namespace)::", "")
+        return name.removeprefix("void ").split("(")[0]
+
+    keep = [k for k in (kernel or "").split(",") if k]
+
+    def wanted(name):
+        return not keep or any(k in name for k in keep)
+
+    for path in paths:
+        con = sqlite3.connect(path)
+        tables = {r[0] for r in con.execute("select name from sqlite_master")}
+        print(f"\n#### {os.path.basename(path)}\n")
+        if "counters_collection" in tables and con.execute(
+                "select count(*) from counters_collection").fetchone()[0]:
+            vals = collections.defaultdict(lambda: collections.defaultdict(list))
+            disp = collections.defaultdict(dict)
+            for name, counter, value, did, dur in con.execute(
+                    "select kernel_name, counter_name, value, dispatch_id, duration "
+                    "from counters_collection"):
+                vals[short(name)][counter].append(value)
+                disp[short(name)][did] = dur
+            print("| kernel | dispatches | mean ns | counter | mean per dispatch |\n"
+                  "|---|---|---|---|---|")
+            for kname, cs in vals.items():
+                if not wanted(kname):
+                    continue
+                d = disp[kname]
+                for counter, v in sorted(cs.items()):
+                    print(f"| `{kname}` | {len(d)} | {sum(d.values()) / len(d):.0f} | {counter} | "
+                          f"{sum(v) / len(v):.6g} |")
+        else:
+            rows = con.execute(
+                "select name, count(*), avg(duration), min(duration), max(duration), grid_x, "
+                "grid_y, workgroup_x, vgpr_count, accum_vgpr_count, sgpr_count, lds_size, "
+                "scratch_size from kernels group by name").fetchall()
+            print("| kernel | calls | mean ns | min ns | max ns | grid | wg | vgpr/agpr/sgpr | "
+                  "lds B | scratch B |\n|---|---|---|---|---|---|---|---|---|---|")
+            for r in sorted(rows, key=lambda r: -r[2] * r[1]):
+                if not wanted(short(r[0])):
+                    continue
+                print(f"| `{short(r[0])}` | {r[1]} | {r[2]:.0f} | {r[3]} | {r[4]} | "
+                      f"{r[5]}x{r[6]} | {r[7]} | {r[8]}/{r[9]}/{r[10]} | {r[11]} | {r[12]} |")
+
+
+# Kernels whose HBM traffic is reported, with the source file each is compiled from.
+TRAFFIC_KERNELS = {
+    "fwd": ("fwd_bf16_kernel", "exact_tiled_attention_24_amd/csrc/fwd_bf16.hip"),
+    "decode": ("decode_bf16_kernel", "exact_tiled_attention_24_amd/csrc/decode.hip"),
+}
+COPY_KERNEL = "copyBuffer"
+
+
+def source_digest(rel):
+    import hashlib
+
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_values(path, counter):
+    """Per-dispatch values of `counter`: a list of (kernel name, value)."""
+    import sqlite3
+
+    con = sqlite3.connect(path)
+    return con.execute("select kernel_name, value from counters_collection "
+                       "where counter_name = ?", (counter,)).fetchall()
+
+
+def write_traffic(fetch_db, write_db, copy_mib):
+    """HBM bytes per launch: raw counter KiB scaled by what the counter reads for a copy.
+
+    The copy of `copy_mib` MiB reads and writes exactly copy_mib MiB; the ratio of that to
+    what FETCH_SIZE / WRITE_SIZE report for it is the scale applied to the kernels.
+    """
+    fetch = counter_values(fetch_db, "FETCH_SIZE")
+    write = counter_values(write_db, "WRITE_SIZE")
+
+    def pick(table, key, largest=False):
+        vals = [v for name, v in table if key in name]
+        if not vals:
+            raise SystemExit(f"no dispatch of a kernel named *{key}* in the counter database")
+        if largest:  # the timed copy, not the small staging copies of the set-up
+            vals = [v for v in vals if v >= 0.5 * max(vals)]
+        return sum(vals) / len(vals), len(vals)
+
+    exact_kib = copy_mib * 1024.0
+    f_copy, _ = pick(fetch, COPY_KERNEL, largest=True)
+    w_copy, _ = pick(write, COPY_KERNEL, largest=True)
+    f_scale, w_scale = exact_kib / f_copy, exact_kib / w_copy
+    doc = {"copy_mib": copy_mib, "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
+    for key, (kname, src) in TRAFFIC_KERNELS.items():
+        f_kib, nf = pick(fetch, kname)
+        w_kib, nw = pick(write, kname)
+        doc[key] = {"kernel": kname, "source": src, "source_sha256_16": source_digest(src),
+                    "dispatches": [nf, nw], "fetch_kib_raw": round(f_kib, 1),
+                    "write_kib_raw": round(w_kib, 1),
+                    "bytes": int(round((f_kib * f_scale + w_kib * w_scale) * 1024))}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(doc, f, indent=1)
+        f.write("\n")
+    print(json.dumps(doc, indent=1))
 
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from, args.copy_mib or 1024)
+        return
+    if args.summarize:
+        summarize(args.summarize, args.kernel)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the path has no multi-GPU component in this build "
-              "(run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: the attention path here has no multi-GPU "
+              "component (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -207,15 +334,20 @@ def main():
 
 
 def load_traffic():
-    """HBM bytes per launch from committed counter summaries, if present and current."""
+    """Measured HBM bytes per launch, per kernel; None where the kernel's source has changed
+    since the counters were taken (or no counters were taken)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
-        return {}
     try:
         with open(path) as f:
-            return json.load(f)
+            doc = json.load(f)
     except (OSError, ValueError):
         return {}
+    out = {}
+    for key, (_, src) in TRAFFIC_KERNELS.items():
+        ent = doc.get(key)
+        if ent and ent.get("source_sha256_16") == source_digest(src):
+            out[key] = ent["bytes"]
+    return out
 
 
 def cpu_baseline(fx, fcfg, heads):

@@ -91,7 +91,8 @@ fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void*
  * dereferences a table entry outside [0, num_pages) (such a page contributes nothing), so
  * a violated precondition gives a wrong result, never an out-of-bounds access. Table
  * entries past a sequence's last page are never read. A sequence of length 0 gets O = 0.
- * Supported: dt = FA_BF16; d = 128; page_size = 16; 1 <= Hq / Hkv <= 8; Hq % Hkv == 0.
+ * Supported: dt = FA_BF16; d = 128; page_size = 16; Hq / Hkv in {1, 2, 4, 8} (other exact
+ * ratios return FA_ERR_UNSUPPORTED); Hq % Hkv != 0 is FA_ERR_INVALID_ARGUMENT.
  */
 fa_status fa_decode_splitk(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_table, const int32_t* seq_lens, void* o,
