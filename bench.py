@@ -114,7 +114,7 @@ def summarize(paths, kernel=None):
 
 # Kernels whose HBM traffic is reported, with the source file each is compiled from.
 TRAFFIC_KERNELS = {
-    "fwd": ("fwd_bf16_kernel", "exact_tiled_attention_24_amd/csrc/fwd_bf16.hip"),
+    "fwd": ("fwd_bf16_sp_kernel", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
     "decode": ("decode_bf16_kernel", "exact_tiled_attention_24_amd/csrc/decode.hip"),
 }
 COPY_KERNEL = "copyBuffer"
@@ -308,7 +308,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4) if fwd_tflops else None,
             "traffic": traffic.get("fwd"),
-            "kernel": "fwd_bf16_kernel<128>",
+            "kernel": "fwd_bf16_sp_kernel<128>",
             "avg_launch_ms": round(float(fwd_ms.mean()), 5) if do_fwd else None,
         },
         "decode": {

@@ -14,14 +14,16 @@ constexpr int kDecodePage = 16;
 constexpr int kDecodeD = 128;
 constexpr int kDecodeTargetWGs = 2 * fa::kPlanCUs;  // one round of 4-wave chunks
 
-// Forward kernel choice: the 32-rows-per-wave tiled kernel unless FA_FWD_KERNEL=pipe selects
-// the software-pipelined one (a tuning override, read once).
-bool use_pipelined_fwd() {
-    static const int choice = [] {
-        const char* e = getenv("FA_FWD_KERNEL");
-        return (e && strcmp(e, "pipe") == 0) ? 1 : 0;
-    }();
-    return choice != 0;
+// Forward kernel choice. Default: the software-pipelined 8-wave kernel for d = 128, the
+// 4-wave tiled kernel for d = 64 (measured faster there: with half the MFMAs per score the
+// tiled kernel's two independent workgroups per CU hide the softmax better). The environment
+// variable FA_FWD_KERNEL=tiled|sp overrides it (a tuning switch, read at every call).
+enum FwdKernel { kFwdAuto = 0, kFwdTiled = 1, kFwdSoftPipe = 2 };
+FwdKernel fwd_kernel_override() {
+    const char* e = getenv("FA_FWD_KERNEL");
+    if (e && strcmp(e, "tiled") == 0) return kFwdTiled;
+    if (e && strcmp(e, "sp") == 0) return kFwdSoftPipe;
+    return kFwdAuto;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -96,9 +98,11 @@ fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void*
     if (dt == FA_BF16) {
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
             return FA_ERR_INVALID_ARGUMENT;
-        e = use_pipelined_fwd()
-                ? fa::launch_fwd_bf16_pipe(q, k, v, o, m_out, l_out, B, Hq, Hkv, N, d, scale,
-                                           causal ? 1 : 0, st)
+        FwdKernel kern = fwd_kernel_override();
+        if (kern == kFwdAuto) kern = d == 128 ? kFwdSoftPipe : kFwdTiled;
+        e = kern == kFwdSoftPipe
+                ? fa::launch_fwd_bf16_sp(q, k, v, o, m_out, l_out, B, Hq, Hkv, N, d, scale,
+                                         causal ? 1 : 0, st)
                 : fa::launch_fwd_bf16(q, k, v, o, m_out, l_out, B, Hq, Hkv, N, d, scale,
                                       causal ? 1 : 0, st);
     } else {

@@ -16,10 +16,11 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
                            int causal, hipStream_t stream);
 
-// Software-pipelined variant: 64 query rows per wave, one wave per SIMD.
-hipError_t launch_fwd_bf16_pipe(const void* q, const void* k, const void* v, void* o,
-                                float* m_out, float* l_out, int B, int Hq, int Hkv, int N, int d,
-                                float scale, int causal, hipStream_t stream);
+// Software-pipelined: 8 waves, 256 query rows; MFMAs of neighbouring half tiles overlap
+// each half tile's softmax within every wave.
+hipError_t launch_fwd_bf16_sp(const void* q, const void* k, const void* v, void* o, float* m_out,
+                              float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
+                              int causal, hipStream_t stream);
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* m_out,
                           float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,

@@ -52,5 +52,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 template <typename T>
 __device__ __forceinline__ T min_(T a, T b) { return a < b ? a : b; }
+template <typename T>
+__device__ __forceinline__ T max_(T a, T b) { return a > b ? a : b; }
 
 }  // namespace fa

@@ -60,6 +60,23 @@ def test_fwd_small_shapes(case, dev):
     np.testing.assert_allclose(to_np(l), l_ref, rtol=1e-5 if dtype == "f32" else 2e-3)
 
 
+@pytest.mark.parametrize("kernel", ["tiled", "sp"])
+@pytest.mark.parametrize("case", [c for c in SMALL if c[0] == "bf16"], ids=lambda c: "-".join(map(str, c)))
+def test_fwd_each_bf16_kernel(case, kernel, dev, monkeypatch):
+    """Both bf16 forward kernels (the library picks one per head size; FA_FWD_KERNEL forces
+    either) against the oracle on the same cases."""
+    dtype, B, Hq, Hkv, N, d, causal = case
+    seed = 100 + SMALL.index(case)
+    log_case(f"fa_fwd kernel={kernel} {case} seed={seed}")
+    monkeypatch.setenv("FA_FWD_KERNEL", kernel)
+    x = gen.fwd_inputs(B, Hq, Hkv, N, d, seed=seed, dtype=dtype, causal=causal)
+    o, m, l = run_fwd(x, dev)
+    o_ref, m_ref, l_ref = oracle.attention(x.q, x.k, x.v, x.scale, causal)
+    assert_close(to_np(o), o_ref, dtype, "O")
+    np.testing.assert_allclose(to_np(m), m_ref, atol=1e-3, rtol=0)
+    np.testing.assert_allclose(to_np(l), l_ref, rtol=2e-3)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_fwd_worked_example(dtype, dev):
     """The worked example of "FlashAttention, explained.": row [2, 1, 3, 0] against four keys.
