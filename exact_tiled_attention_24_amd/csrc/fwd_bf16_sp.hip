@@ -46,11 +46,18 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;  // query rows per workgroup
 constexpr int kBc = 64;           // keys per tile (two 32-key half tiles)
-constexpr int kStages = 3;
+constexpr int kPadOffset = 1 << 30;  // buffer offset beyond every tile descriptor's range
+constexpr int kStages = 4;       // LDS stages of K and of V
 constexpr int kXcds = 8;
 constexpr float kLazy = 8.f;
-constexpr int kAhead = 5;         // LDS operand reads kept in flight
+constexpr int kAhead = 4;         // LDS operand reads kept in flight
 constexpr int kBufferDword3 = 0x00020000;
+
+// Pointers into LDS (address space 3): 32-bit, so an operand base is one VGPR.
+typedef const __attribute__((address_space(3))) unsigned char* lds_cptr;
+typedef const __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 __device__ __forceinline__ int kappa(int m) {
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -65,17 +72,17 @@ __device__ __forceinline__ void barrier_lds() {
 
 template <int D>
 struct Tile {
-    static constexpr int kChunks = D / 8;                             // 16-byte chunks per K row
     static constexpr int kKRow = D * 2 + 16;                          // padded K row, bytes
-    static constexpr int kVRow = kBc * 2 + 16;                        // padded V^T row, bytes
-    static constexpr int kKBytes = kBc * kKRow;
-    static constexpr int kVBytes = D * kVRow;
-    static constexpr int kStageBytes = kKBytes + kVBytes;
-    static constexpr int kKLoads = kBc * kChunks / kThreads;          // b128 K loads per thread
-    static constexpr int kRowsPerLoad = kThreads / kChunks;
-    static constexpr int kVKeys = kBc * (D / 4) / kThreads;           // V keys per thread
-    static constexpr int kVGroups = kBc / kVKeys;                     // key groups per V tile
-    static constexpr int kStageOps = kKLoads + 4 + 1;                 // see stage_op
+    // padded V row, bytes: the 64 B pad puts the four rows a transposing read touches per
+    // cycle in four different 64 B bank windows
+    static constexpr int kVRow = D * 2 + 64;
+    static constexpr int kKStage = kBc * kKRow;
+    static constexpr int kVStage = kBc * kVRow;
+    static constexpr int kVBase = kStages * kKStage;                  // V stages follow K's
+    static constexpr int kKChunks = kKStage / 1024;                   // 1 KiB DMA chunks
+    static constexpr int kVChunks = kVStage / 1024;
+    static constexpr int kDmaPerWave = (kKChunks + kVChunks + kWaves - 1) / kWaves;
+    static_assert(kKStage % 1024 == 0 && kVStage % 1024 == 0, "stages are whole DMA chunks");
 };
 
 template <int D>
@@ -84,7 +91,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
     uint16_t* __restrict__ o, float* __restrict__ m_out, float* __restrict__ l_out, int B, int Hq,
     int Hkv, int N, float scale_log2, int causal, int nqb) {
     using T = Tile<D>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * T::kStageBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * (T::kKStage + T::kVStage)];
+    lds_cptr const lds = (lds_cptr)smem;  // generic -> LDS address space
+    const unsigned lds_addr = (unsigned)(size_t)lds;  // LDS byte address of smem
 
     // ---- work item: XCD-contiguous runs ordered (KV group, query block heaviest first,
     // head in group); see fwd_bf16.hip ----
@@ -134,117 +143,134 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
     const int kv_end = causal ? min_(N, qb * kBr + kBr) : N;
     const int n_tiles = (kv_end + kBc - 1) / kBc;
 
-    // ---- staging: every thread moves kKLoads 16-byte chunks of each K tile and kVKeys keys
-    // x 4 columns of each V tile (register-staged buffer loads, issued a tile ahead) ----
-    u32x4 kreg[T::kKLoads];
-    u32x2 vreg[T::kVKeys];
-    const int k_gofs = ((tid / T::kChunks) * D + (tid % T::kChunks) * 8) * 2;
-    const int k_lofs = (tid / T::kChunks) * T::kKRow + (tid % T::kChunks) * 16;
-    // V: keys v_kg * kVKeys + i of columns 4 v_dq .. 4 v_dq + 3; the key group varies fastest
-    // across lanes, so a transposed store of one column by consecutive lanes fills
-    // consecutive bytes of one V^T row.
-    const int v_kg = tid % T::kVGroups;
-    const int v_dq = tid / T::kVGroups;
-    const int v_gofs = (v_kg * T::kVKeys * D + v_dq * 4) * 2;
-    const int v_lofs = T::kKBytes + (4 * v_dq) * T::kVRow + v_kg * T::kVKeys * 2;
-    // Descriptor of tile j of one head's K or V (rows past N read as zero). The row count
-    // goes through readfirstlane: the clamp selects to a vector instruction, and a
-    // descriptor word in a VGPR would force a per-lane loop around every buffer load.
-    auto tile_rsrc = [&](const uint16_t* base, int j) {
-        const int kv0 = j * kBc;
-        const int rows = __builtin_amdgcn_readfirstlane(max_(0, min_(N - kv0, kBc)));
-        return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)min_(kv0, N) * D),
-                                                 (short)0, rows * D * 2, kBufferDword3);
-    };
-    auto load_k = [&](int j) {
-        const __amdgpu_buffer_rsrc_t r = tile_rsrc(kh, j);
+    // ---- staging: buffer loads straight into LDS (no registers). A tile's K stage (64
+    // padded rows) and V stage (64 padded rows, row-major) are cut into 1 KiB chunks; one
+    // DMA instruction of a wave fills one chunk, lane i the chunk's bytes 16 i .. 16 i + 15.
+    // Wave w issues the chunks w, w + 8, ... of the list (K chunks, then V chunks; the list is
+    // padded to a multiple of 8 by repeating its last chunk, which rewrites the same bytes),
+    // so every wave issues kDmaPerWave loads per tile and one vmcnt count waits for a tile.
+    // A lane that lands on row padding gets an offset past any descriptor's range, so it
+    // fetches nothing (and writes zeros that are never read). Rows past N read as zero through
+    // the descriptor's range. ----
+    // Each wave's operation i targets the same chunk of every tile: its per-lane source
+    // offset (relative to the tile, already advanced by the 3 tiles K runs ahead or the 2 of
+    // V) and its LDS offset (relative to the stage) are fixed here. The descriptors span the
+    // head's rows up to the end of this work item's last tile, so loads issued past the end
+    // fetch nothing and fill zeros (as do the negative tile offsets of the prologue).
+    int dma_src[T::kDmaPerWave];
+    unsigned dma_dst[T::kDmaPerWave];
 #pragma unroll
-        for (int i = 0; i < T::kKLoads; ++i)
-            kreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    r, k_gofs + i * T::kRowsPerLoad * D * 2, 0, 0));
+    for (int i = 0; i < T::kDmaPerWave; ++i) {
+        const int c = min_(wave + kWaves * i, T::kKChunks + T::kVChunks - 1);
+        const bool is_k = c < T::kKChunks;
+        const int row_b = is_k ? T::kKRow : T::kVRow;
+        const int slot = 1024 * (is_k ? c : c - T::kKChunks) + 16 * lane;
+        const int row = slot / row_b, col = slot - row * row_b;
+        dma_src[i] = (col < D * 2 ? row * D * 2 + col : kPadOffset) + (is_k ? 3 : 2) * kBc * D * 2;
+        dma_dst[i] = lds_addr + (is_k ? 0u : unsigned(T::kVBase)) + 1024u * (is_k ? c : c - T::kKChunks);
+    }
+    const int row_end = min_(N, n_tiles * kBc);
+    // (readfirstlane: the clamp selects to a vector instruction, and a descriptor word in a
+    // VGPR would force a per-lane loop around every buffer load)
+    const int head_bytes = __builtin_amdgcn_readfirstlane(row_end * D * 2);
+    const __amdgpu_buffer_rsrc_t rsrc_k =
+        __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, head_bytes, kBufferDword3);
+    const __amdgpu_buffer_rsrc_t rsrc_v =
+        __builtin_amdgcn_make_buffer_rsrc((void*)vh, (short)0, head_bytes, kBufferDword3);
+    // DMA operation i of tile step j: K of tile j + 3 and V of tile j + 2. Written as
+    // assembly: the compiler's own form makes it wait for every outstanding load to LDS
+    // before each transposing read (it cannot tell the stages apart); the waits here are
+    // explicit. Operations whose chunks are all K (or all V) for every wave need no select.
+    auto dma_op = [&](int j, int i) {
+        constexpr int kK = T::kKChunks;
+        const bool all_k = kWaves * i + kWaves - 1 < kK, all_v = kWaves * i >= kK;
+        const bool is_k = all_k || (!all_v && wave + kWaves * i < kK);
+        const unsigned stage = is_k ? unsigned(((j + 3) & (kStages - 1)) * T::kKStage)
+                                    : unsigned(((j + 2) & (kStages - 1)) * T::kVStage);
+        const __amdgpu_buffer_rsrc_t r = is_k ? rsrc_k : rsrc_v;
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"(dma_src[i] + j * (kBc * D * 2)), "s"(r), "{m0}"(dma_dst[i] + stage)
+                     : "memory");
     };
-    auto load_v = [&](int j) {
-        const __amdgpu_buffer_rsrc_t r = tile_rsrc(vh, j);
+    auto dma_tile = [&](int j) {
 #pragma unroll
-        for (int i = 0; i < T::kVKeys; ++i)
-            vreg[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, v_gofs + i * D * 2, 0, 0));
+        for (int i = 0; i < T::kDmaPerWave; ++i) dma_op(j, i);
     };
-    auto store_k_part = [&](int st, int i) {
-        *reinterpret_cast<u32x4*>(smem + st * T::kStageBytes + k_lofs + i * T::kRowsPerLoad * T::kKRow) =
-            kreg[i];
+    // LDS DMA is not tracked by the compiler's waits: wait for all but the newest tile's
+    // loads (vmcnt counts this wave's vector loads in issue order), then the barrier.
+    auto wait_dma_tile = [&]() {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(T::kDmaPerWave) : "memory");
     };
-    // column c of this thread's V keys, transposed: key pairs joined with one v_perm_b32 each
-    auto store_v_col = [&](int st, int c) {
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t w[T::kVKeys / 2];
-#pragma unroll
-        for (int i = 0; i < T::kVKeys / 2; ++i)
-            w[i] = __builtin_amdgcn_perm(vreg[2 * i + 1][c >> 1], vreg[2 * i][c >> 1], sel);
-        unsigned char* dst = smem + st * T::kStageBytes + v_lofs + c * T::kVRow;
-        if constexpr (T::kVKeys == 4) *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
-        else *reinterpret_cast<uint32_t*>(dst) = w[0];
-    };
-    // Staging of tile j's end, as kStageOps small operations that the pipelined step spreads
-    // over its slots: K of tile j+2 and V of tile j+1 into their stages, then the loads of K
-    // of tile j+3 and V of tile j+2 into the freed registers.
-    auto stage_op = [&](int j, int op) {
-        if (op < T::kKLoads) store_k_part((j + 2) % kStages, op);
-        else if (op < T::kKLoads + 4) store_v_col((j + 1) % kStages, op - T::kKLoads);
-        else {
-            load_k(j + 3);
-            load_v(j + 2);
-        }
-    };
+    auto wait_dma_all = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
-    // Operand addresses: one per-lane base each, the rest immediate.
+    // Operand addresses: one per-lane base each, the rest immediate. K: lane (l32, hh)
+    // reads 16 bytes of row kappa(l32). V: the V^T operand comes from row-major V through
+    // ds_read_b64_tr_b16, which transposes within each 16-lane group: when source lane
+    // q + 4e (q, e < 4) reads 4 elements at V[k0 + e][d0 + 4q], lane j of the group receives
+    // V[k0 .. k0 + 3][d0 + j]. Two such reads give a lane its 8 consecutive keys of one head
+    // dimension, as the MFMA's A operand wants (lane l: d = l % 32, keys 8 (l / 32) ..).
     const int k_rofs = kappa(l32) * T::kKRow + hh * 16;
-    const int v_rofs = T::kKBytes + l32 * T::kVRow + hh * 16;
+    const int v_rofs = T::kVBase + (8 * (lane >> 5) + ((lane & 15) >> 2)) * T::kVRow +
+                       (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
-    // S^T = K Q^T of half tile (stage st, half kb) into s.
+    // S^T = K Q^T of half tile (K stage st, half kb) into s.
     auto compute_s = [&](f32x16& s, int st, int kb) {
-        const unsigned char* ks = smem + st * T::kStageBytes + k_rofs + 32 * kb * T::kKRow;
+        const lds_cptr ks = lds + st * T::kKStage + k_rofs + 32 * kb * T::kKRow;
         s = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + 32 * kk);
+            const bf16x8 a = *reinterpret_cast<const lds_bf16x8*>(ks + 32 * kk);
             s = mfma_32x32x16(a, qf[kk], s);
         }
     };
-    // O^T += V^T P^T of half tile (stage st, half kb) with probabilities pk.
+    // V^T operand for key group t (16 keys) and head-dimension block db, from the V stage
+    // half at vb (base already includes v_rofs and the half's key offset).
+    auto vfrag = [&](lds_cptr vb, int t, int db) -> bf16x8 {
+        const lds_cptr p = vb + 16 * t * T::kVRow + 64 * db;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * T::kVRow));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // O^T += V^T P^T of half tile (V stage st, half kb) with probabilities pk.
     auto compute_pv = [&](const u32x4 (&pk)[2], int st, int kb) {
-        const unsigned char* vs = smem + st * T::kStageBytes + v_rofs;
+        const lds_cptr vb = lds + st * T::kVStage + v_rofs + 32 * kb * T::kVRow;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[t]);
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    vs + 32 * db * T::kVRow + (4 * kb + 2 * t) * 16);
-                acc_o[db] = mfma_32x32x16(a, pb, acc_o[db]);
-            }
+            for (int db = 0; db < D / 32; ++db) acc_o[db] = mfma_32x32x16(vfrag(vb, t, db), pb, acc_o[db]);
         }
     };
     // Lazy O rescale, after the step's MFMAs (which added the previous half tile).
-    auto rescale = [&](float alpha) {
-        if (__any(alpha != 1.f)) {
+    auto rescale = [&](bool move, float alpha) {
+        if (__any(move)) {
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) acc_o[i] *= alpha;
         }
     };
-    // MFMA operand of slot `sl` of step hi: even slots are the S^T MFMAs of half tile hi+1
-    // (K, head dimensions 16 (sl/2) ..), odd slots the O MFMAs of half tile hi-1 (V^T, key
-    // group t, head-dimension block db).
-    auto frag = [&](int hi, int sl) -> bf16x8 {
+    // Operand bases of step hi: K rows of half tile hi+1 and V rows of half tile hi-1.
+    // Each goes through an empty asm so the compiler keeps it as one opaque register and
+    // addresses every fragment as base + immediate (left to itself it re-associates the
+    // stage offsets into bases with negative offsets, which cost an add per read).
+    struct Bases {
+        lds_cptr k, v;
+    };
+    auto bases = [&](int hi) {
+        Bases b;
+        const int st_k = ((hi + 1) >> 1) % kStages, kb_k = (hi + 1) & 1;
+        const int st_v = ((hi - 1 + 2 * kStages) >> 1) % kStages, kb_v = (hi - 1) & 1;
+        b.k = lds + st_k * T::kKStage + k_rofs + 32 * kb_k * T::kKRow;
+        b.v = lds + st_v * T::kVStage + v_rofs + 32 * kb_v * T::kVRow;
+        asm volatile("" : "+v"(b.k), "+v"(b.v));
+        return b;
+    };
+    // MFMA operand of slot `sl`: even slots are the S^T MFMAs (K, head dimensions
+    // 16 (sl/2) ..), odd slots the O MFMAs (V^T, key group t, head-dimension block db).
+    auto frag = [&](const Bases& b, int sl) -> bf16x8 {
         const int i = sl >> 1;
-        if ((sl & 1) == 0) {
-            const int st = ((hi + 1) >> 1) % kStages, kb = (hi + 1) & 1;
-            return *reinterpret_cast<const bf16x8*>(smem + st * T::kStageBytes + k_rofs +
-                                                    32 * kb * T::kKRow + 32 * i);
-        }
-        const int st = ((hi - 1) >> 1) % kStages, kb = (hi - 1) & 1;
-        const int t = i / (D / 32), db = i % (D / 32);
-        return *reinterpret_cast<const bf16x8*>(smem + st * T::kStageBytes + v_rofs + 4 * kb * 16 +
-                                                32 * db * T::kVRow + 2 * t * 16);
+        if ((sl & 1) == 0) return *reinterpret_cast<const lds_bf16x8*>(b.k + 32 * i);
+        return vfrag(b.v, i / (D / 32), i % (D / 32));
     };
 
     // One pipeline step. Its MFMAs are O^T += V^T P^T of half tile hi-1 (probabilities
@@ -257,8 +283,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
     // last slots, so the next step starts without waiting, even across a barrier: its
     // operands were staged before the previous barrier).
     // (with_pv false: half tile 0, whose step has no O update; its odd slots stay empty.)
-    // stage_j >= 0: this step also carries the staging of tile stage_j (stage_op 0, 1, ...
-    // in its odd slots).
+    // stage_j >= 0: this step also issues the loads of K of tile stage_j + 3 and V of tile
+    // stage_j + 2 (one DMA per odd slot).
     auto step = [&](int hi, f32x16& s_cur, f32x16& s_next, const u32x4 (&pk_prev)[2],
                     u32x4 (&pk_cur)[2], auto masked, bf16x8 (&fr)[kAhead], auto with_pv,
                     int stage_j) {
@@ -268,51 +294,69 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
         constexpr int kPhasesPerSlot = 16 / kSlots;
         static_assert(kAhead <= kSlots, "read-ahead deeper than a step");
 
-        // softmax state of this half tile
-        float m_a = 0.f, m_b = 0.f, mx = 0.f, alpha = 1.f, m_use = 0.f, rs = 0.f;
-        auto phase = [&](int ph) {
-            if (ph < 2) {
-                if constexpr (decltype(masked)::value) {
-                    const int kv0 = 32 * hi;
-                    const int lim = (causal ? min_(qrow, N - 1) : N - 1) - kv0 - 8 * hh;
+        // Softmax of this half tile, cut into 16 phases (one per slot for d = 128) and
+        // software-pipelined so that the instructions of one phase do not wait on each other:
+        // the row maximum is a depth-3 tree of max3; the scores go through exp2 one pair per
+        // phase, and each pair is packed to bf16 one phase later and added to the row sum one
+        // phase after that.
+        float t0 = 0.f, t1 = 0.f, t2 = 0.f, t3 = 0.f, t4 = 0.f, mx = 0.f, alpha = 1.f;
+        bool move = false;
+        float e0[8], e1[8];  // exp2 of score pair k (held until packed)
+        uint32_t wk[8];      // packed pair k (held until summed)
+        auto mask_scores = [&]() {
+            const int kv0 = 32 * hi;
+            // key of register r is kv0 + 16 (r >> 3) + 8 hh + (r & 7); masked: key > qrow
+            // (causal) or key >= N, i.e. c > lim
+            const int lim = (causal ? min_(qrow, N - 1) : N - 1) - kv0 - 8 * hh;
 #pragma unroll
-                    for (int r = 8 * ph; r < 8 * ph + 8; ++r) {
-                        const int c = 16 * (r >> 3) + (r & 7);
-                        s_cur[r] = c > lim ? -INFINITY : s_cur[r];
-                    }
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int c = 16 * (r >> 3) + (r & 7);
+                s_cur[r] = c > lim ? -INFINITY : s_cur[r];
             }
+        };
+        // pair k: exp2 in phase ph_e + k, packed one phase later, summed one phase after that
+        auto pair_stages = [&](int ph, int ph_e) {
+            const int ke = ph - ph_e, kp = ke - 1, ks = ke - 2;
+            if (ks >= 0 && ks < 8)
+                l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wk[ks]),
+                                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), l_part, false);
+            if (kp >= 0 && kp < 8) {
+                wk[kp] = pack_bf16x2(e0[kp], e1[kp]);
+                pk_cur[kp >> 2][kp & 3] = wk[kp];
+            }
+            if (ke >= 0 && ke < 8) {
+                e0[ke] = exp2_hw(__builtin_fmaf(s_cur[2 * ke], scale_log2, -m_ref));
+                e1[ke] = exp2_hw(__builtin_fmaf(s_cur[2 * ke + 1], scale_log2, -m_ref));
+            }
+        };
+        auto phase = [&](int ph) {
             if (ph == 0) {
-                m_a = fmaxf(fmaxf(s_cur[0], s_cur[1]), s_cur[2]);
-                m_b = fmaxf(fmaxf(s_cur[3], s_cur[4]), s_cur[5]);
-            } else if (ph < 3) {
-                const int r = 6 + 4 * (ph - 1);
-                m_a = fmaxf(fmaxf(m_a, s_cur[r]), s_cur[r + 1]);
-                m_b = fmaxf(fmaxf(m_b, s_cur[r + 2]), s_cur[r + 3]);
+                if constexpr (decltype(masked)::value) mask_scores();
+                t0 = vmax(vmax(s_cur[0], s_cur[1]), s_cur[2]);
+                t1 = vmax(vmax(s_cur[3], s_cur[4]), s_cur[5]);
+                t2 = vmax(vmax(s_cur[6], s_cur[7]), s_cur[8]);
+            } else if (ph == 1) {
+                t3 = vmax(vmax(s_cur[9], s_cur[10]), s_cur[11]);
+                t4 = vmax(vmax(s_cur[12], s_cur[13]), s_cur[14]);
+            } else if (ph == 2) {
+                t0 = vmax(vmax(t0, t1), t2);
+                t3 = vmax(vmax(t3, t4), s_cur[15]);
             } else if (ph == 3) {
-                m_a = fmaxf(fmaxf(m_a, s_cur[14]), s_cur[15]);
-                mx = pair32_max(fmaxf(m_a, m_b)) * scale_log2;
+                mx = pair32_vmax(vmax(t0, t3)) * scale_log2;
             } else if (ph == 4) {
-                m_run = fmaxf(m_run, mx);
-                const bool move = mx > m_ref + kLazy;
+                // (the first half tile always holds a key every row sees, key 0, so its mx is
+                // finite: m_ref leaves -inf there, with alpha = 0 on a zero O and row sum)
+                m_run = vmax(m_run, mx);
+                move = mx > m_ref + kLazy;
                 const float r_new = move ? mx : m_ref;
                 alpha = move ? exp2_hw(m_ref - r_new) : 1.f;
                 m_ref = r_new;
-                m_use = (r_new == -INFINITY) ? 0.f : r_new;
-            } else if (ph < 13) {
-                const int k2 = ph - 5;  // score pair
-                const float p0 = exp2_hw(__builtin_fmaf(s_cur[2 * k2], scale_log2, -m_use));
-                const float p1 = exp2_hw(__builtin_fmaf(s_cur[2 * k2 + 1], scale_log2, -m_use));
-                const uint32_t w = pack_bf16x2(p0, p1);
-                // row sum of the bf16 weights the O MFMA multiplies (one v_dot2 per pair)
-                rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
-                                                     __builtin_bit_cast(bf16x2, 0x3f803f80u), rs, false);
-                pk_cur[k2 >> 2][k2 & 3] = w;
-            } else if (ph == 13) {
-                l_part = l_part * alpha + rs;
+                l_part *= alpha;
             }
+            pair_stages(ph, 5);
         };
 
+        const Bases b_cur = bases(hi), b_next = bases(hi + 1);
         bf16x8 cur[kSlots];
 #pragma unroll
         for (int sl = 0; sl < kAhead; ++sl) cur[sl] = fr[sl];
@@ -321,9 +365,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
 #pragma unroll
         for (int sl = 0; sl < kSlots; ++sl) {
             if (sl + kAhead < kSlots) {
-                if (kPV || ((sl + kAhead) & 1) == 0) cur[sl + kAhead] = frag(hi, sl + kAhead);
+                if (kPV || ((sl + kAhead) & 1) == 0) cur[sl + kAhead] = frag(b_cur, sl + kAhead);
             } else {
-                fr[sl + kAhead - kSlots] = frag(hi + 1, sl + kAhead - kSlots);
+                fr[sl + kAhead - kSlots] = frag(b_next, sl + kAhead - kSlots);
             }
             if ((sl & 1) == 0) {
                 s_next = mfma_32x32x16(cur[sl], qf[sl >> 1], s_next);
@@ -334,16 +378,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
             }
 #pragma unroll
             for (int ph = sl * kPhasesPerSlot; ph < (sl + 1) * kPhasesPerSlot; ++ph) phase(ph);
-            // staging op o sits in slot 1 + o (kSlots - 2) / kStageOps
+            // DMA i sits in slot 1 + 2 i
 #pragma unroll
-            for (int op = 0; op < T::kStageOps; ++op)
-                if (sl == 1 + op * (kSlots - 2) / T::kStageOps && stage_j >= 0) stage_op(stage_j, op);
+            for (int i = 0; i < T::kDmaPerWave; ++i)
+                if (sl == 1 + 2 * i && stage_j >= 0) dma_op(stage_j, i);
             __builtin_amdgcn_sched_barrier(0);
         }
         // The probabilities are first used by the next step; without this the compiler sinks
         // their exponentials past the rescale branch, away from the MFMAs they overlap.
         asm volatile("" : "+v"(pk_cur[0]), "+v"(pk_cur[1]), "+v"(l_part));
-        rescale(alpha);
+        rescale(move, alpha);
     };
     using Masked = std::true_type;
     using Plain = std::false_type;
@@ -357,24 +401,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
     u32x4 pa[2], pb[2];
     bf16x8 fr[kAhead];
 
-    // ---- prologue: K0, K1 and V0 staged; K2 and V1 in registers; scores of half tile 0 ----
-    load_k(0);
-    load_v(0);
-#pragma unroll
-    for (int i = 0; i < T::kKLoads; ++i) store_k_part(0, i);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) store_v_col(0, c);
-    load_k(1);
-#pragma unroll
-    for (int i = 0; i < T::kKLoads; ++i) store_k_part(1, i);
-    load_k(2);
-    load_v(1);
+    // ---- prologue: K0..K2 and V0, V1 staged; scores of half tile 0 ----
+    dma_tile(-3);  // K0 (and zeros for V of tile -1, in the stage V3 takes later)
+    dma_tile(-2);  // K1, V0
+    dma_tile(-1);  // K2, V1
+    wait_dma_all();
     barrier_lds();
     compute_s(sa, 0, 0);
 
-    // ---- tile 0: half 0 has no O update yet; its first step stages K2 / V1 ----
+    // ---- tile 0: half 0 has no O update yet; its first step issues K3 / V2 ----
 #pragma unroll
-    for (int sl = 0; sl < kAhead; ++sl) fr[sl] = (sl & 1) ? bf16x8{} : frag(0, sl);
+    for (int sl = 0; sl < kAhead; ++sl) fr[sl] = (sl & 1) ? bf16x8{} : frag(bases(0), sl);
     if (n_plain > 0) {
         step(0, sa, sb, pb, pa, Plain{}, fr, std::false_type{}, 0);
         step(1, sb, sa, pa, pb, Plain{}, fr, std::true_type{}, -1);
@@ -382,17 +419,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
         step(0, sa, sb, pb, pa, Masked{}, fr, std::false_type{}, 0);
         step(1, sb, sa, pa, pb, Masked{}, fr, std::true_type{}, -1);
     }
+    wait_dma_tile();
     barrier_lds();
 
     // ---- tiles 1 .. n_tiles-1. Tile j reads K_j (half 1), K_{j+1} (half 0), V_{j-1}
-    // (half 1) and V_j (half 0). During its first step it writes K_{j+2} and V_{j+1} to the
-    // stages of K_{j-1} and V_{j-2}, both last read during tile j-1, before the previous
-    // barrier, and first read after the barrier that ends tile j.
+    // (half 1) and V_j (half 0). Its first step issues the loads of K_{j+3} and V_{j+2}
+    // into the stages of K_{j-1} and V_{j-2}, both last read during tile j-1, before the
+    // previous barrier; they have until the barrier that ends tile j+1 to land (the wait
+    // before each barrier leaves only the newest tile's loads in flight).
     // (Do-while loops with the exit test at the bottom keep the accumulators in one set of
     // registers.) ----
     auto tile = [&](int j, auto masked) {
         step(2 * j, sa, sb, pb, pa, masked, fr, std::true_type{}, j);
         step(2 * j + 1, sb, sa, pa, pb, masked, fr, std::true_type{}, -1);
+        wait_dma_tile();
         barrier_lds();
     };
     int j = 1;
@@ -408,6 +448,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
     }
     // last half tile's O update (its S^T step computed a score block past the end, unused)
     compute_pv(pb, (n_tiles - 1) % kStages, 1);
+    wait_dma_all();  // no load may still be writing LDS when the workgroup ends
 
     // ---- epilogue: O / l, bf16, optional row statistics ----
     const float l_tot = pair32_sum(l_part);

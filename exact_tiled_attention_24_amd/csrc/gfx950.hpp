@@ -41,6 +41,14 @@ __device__ __forceinline__ float pair32_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// Maximum that propagates NaN instead of quieting its inputs first (v_maximum3_f32 on
+// gfx950): max/fmaxf on values the compiler cannot prove canonical (MFMA results, lane
+// swaps) cost an extra instruction per input.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float pair32_vmax(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float pair32_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
