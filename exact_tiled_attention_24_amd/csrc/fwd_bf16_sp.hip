@@ -177,25 +177,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
         __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, head_bytes, kBufferDword3);
     const __amdgpu_buffer_rsrc_t rsrc_v =
         __builtin_amdgcn_make_buffer_rsrc((void*)vh, (short)0, head_bytes, kBufferDword3);
-    // DMA operation i of tile step j: K of tile j + 3 and V of tile j + 2. Written as
-    // assembly: the compiler's own form makes it wait for every outstanding load to LDS
-    // before each transposing read (it cannot tell the stages apart); the waits here are
-    // explicit. Operations whose chunks are all K (or all V) for every wave need no select.
-    auto dma_op = [&](int j, int i) {
+    // DMA operation i of tile step j (stage phase P = j mod 4): K of tile j + 3 and V of
+    // tile j + 2. Written as assembly: the compiler's own form makes it wait for every
+    // outstanding load to LDS before each transposing read (it cannot tell the stages
+    // apart); the waits here are explicit. Operations whose chunks are all K (or all V) for
+    // every wave need no select.
+    auto dma_op = [&](int j, int i, int P) {  // (P is a constant at every call)
         constexpr int kK = T::kKChunks;
         const bool all_k = kWaves * i + kWaves - 1 < kK, all_v = kWaves * i >= kK;
         const bool is_k = all_k || (!all_v && wave + kWaves * i < kK);
-        const unsigned stage = is_k ? unsigned(((j + 3) & (kStages - 1)) * T::kKStage)
-                                    : unsigned(((j + 2) & (kStages - 1)) * T::kVStage);
+        const unsigned stage = is_k ? unsigned(((P + 3) & (kStages - 1)) * T::kKStage)
+                                    : unsigned(((P + 2) & (kStages - 1)) * T::kVStage);
         const __amdgpu_buffer_rsrc_t r = is_k ? rsrc_k : rsrc_v;
         asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                      :
                      : "v"(dma_src[i] + j * (kBc * D * 2)), "s"(r), "{m0}"(dma_dst[i] + stage)
                      : "memory");
     };
-    auto dma_tile = [&](int j) {
+    auto dma_tile = [&](int j, int P) {
 #pragma unroll
-        for (int i = 0; i < T::kDmaPerWave; ++i) dma_op(j, i);
+        for (int i = 0; i < T::kDmaPerWave; ++i) dma_op(j, i, P);
     };
     // LDS DMA is not tracked by the compiler's waits: wait for all but the newest tile's
     // loads (vmcnt counts this wave's vector loads in issue order), then the barrier.
@@ -204,19 +205,34 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
     };
     auto wait_dma_all = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
-    // Operand addresses: one per-lane base each, the rest immediate. K: lane (l32, hh)
-    // reads 16 bytes of row kappa(l32). V: the V^T operand comes from row-major V through
+    // Operand addresses: a per-lane base plus an immediate. K: lane (l32, hh) reads 16 bytes
+    // of row kappa(l32). V: the V^T operand comes from row-major V through
     // ds_read_b64_tr_b16, which transposes within each 16-lane group: when source lane
     // q + 4e (q, e < 4) reads 4 elements at V[k0 + e][d0 + 4q], lane j of the group receives
     // V[k0 .. k0 + 3][d0 + j]. Two such reads give a lane its 8 consecutive keys of one head
     // dimension, as the MFMA's A operand wants (lane l: d = l % 32, keys 8 (l / 32) ..).
-    const int k_rofs = kappa(l32) * T::kKRow + hh * 16;
-    const int v_rofs = T::kVBase + (8 * (lane >> 5) + ((lane & 15) >> 2)) * T::kVRow +
-                       (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+    // Stages are compile-time (the tile loop is unrolled over the four stages), so every
+    // operand address is one of three loop-invariant bases plus an immediate (the offset
+    // field holds 16 bits: the V stages need a second base for stages 2 and 3). The bases
+    // go through an empty asm so that the compiler keeps them opaque rather than
+    // re-associating the offsets into per-read additions.
+    lds_cptr base_k = lds + kappa(l32) * T::kKRow + hh * 16;
+    lds_cptr base_v = lds + T::kVBase + (8 * (lane >> 5) + ((lane & 15) >> 2)) * T::kVRow +
+                      (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+    lds_cptr base_v2 = base_v + 2 * T::kVStage;
+    asm volatile("" : "+v"(base_k), "+v"(base_v), "+v"(base_v2));
+    static_assert(3 * T::kKStage + 32 * T::kKRow + 2 * D < 65536, "K offsets fit the immediate");
+    static_assert(T::kVStage + 32 * T::kVRow + 20 * T::kVRow + 2 * D < 65536,
+                  "V offsets fit the immediate");
+    // K rows of half kb of stage st; V rows of half kb of stage st.
+    auto k_at = [&](int st, int kb) { return base_k + st * T::kKStage + 32 * kb * T::kKRow; };
+    auto v_at = [&](int st, int kb) {
+        return (st < 2 ? base_v : base_v2) + (st & 1) * T::kVStage + 32 * kb * T::kVRow;
+    };
 
     // S^T = K Q^T of half tile (K stage st, half kb) into s.
     auto compute_s = [&](f32x16& s, int st, int kb) {
-        const lds_cptr ks = lds + st * T::kKStage + k_rofs + 32 * kb * T::kKRow;
+        const lds_cptr ks = k_at(st, kb);
         s = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
@@ -224,8 +240,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
             s = mfma_32x32x16(a, qf[kk], s);
         }
     };
-    // V^T operand for key group t (16 keys) and head-dimension block db, from the V stage
-    // half at vb (base already includes v_rofs and the half's key offset).
+    // V^T operand for key group t (16 keys) and head-dimension block db, from the V rows at
+    // vb (a stage half).
     auto vfrag = [&](lds_cptr vb, int t, int db) -> bf16x8 {
         const lds_cptr p = vb + 16 * t * T::kVRow + 64 * db;
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
@@ -234,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
     };
     // O^T += V^T P^T of half tile (V stage st, half kb) with probabilities pk.
     auto compute_pv = [&](const u32x4 (&pk)[2], int st, int kb) {
-        const lds_cptr vb = lds + st * T::kVStage + v_rofs + 32 * kb * T::kVRow;
+        const lds_cptr vb = v_at(st, kb);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[t]);
@@ -244,26 +260,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
     };
     // Lazy O rescale, after the step's MFMAs (which added the previous half tile).
     auto rescale = [&](bool move, float alpha) {
-        if (__any(move)) {
+        if (__builtin_expect(__any(move), 0)) {
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) acc_o[i] *= alpha;
         }
     };
-    // Operand bases of step hi: K rows of half tile hi+1 and V rows of half tile hi-1.
-    // Each goes through an empty asm so the compiler keeps it as one opaque register and
-    // addresses every fragment as base + immediate (left to itself it re-associates the
-    // stage offsets into bases with negative offsets, which cost an add per read).
+    // Operand rows of step hi (H8 = hi mod 8, so stages are compile-time): K of half tile
+    // hi+1 and V of half tile hi-1.
     struct Bases {
         lds_cptr k, v;
     };
-    auto bases = [&](int hi) {
-        Bases b;
-        const int st_k = ((hi + 1) >> 1) % kStages, kb_k = (hi + 1) & 1;
-        const int st_v = ((hi - 1 + 2 * kStages) >> 1) % kStages, kb_v = (hi - 1) & 1;
-        b.k = lds + st_k * T::kKStage + k_rofs + 32 * kb_k * T::kKRow;
-        b.v = lds + st_v * T::kVStage + v_rofs + 32 * kb_v * T::kVRow;
-        asm volatile("" : "+v"(b.k), "+v"(b.v));
-        return b;
+    auto bases = [&](auto h8_c) {
+        constexpr int H8 = decltype(h8_c)::value;
+        constexpr int hk = (H8 + 1) & 7, hv = (H8 + 7) & 7;
+        return Bases{k_at(hk >> 1, hk & 1), v_at(hv >> 1, hv & 1)};
     };
     // MFMA operand of slot `sl`: even slots are the S^T MFMAs (K, head dimensions
     // 16 (sl/2) ..), odd slots the O MFMAs (V^T, key group t, head-dimension block db).
@@ -272,7 +282,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
         if ((sl & 1) == 0) return *reinterpret_cast<const lds_bf16x8*>(b.k + 32 * i);
         return vfrag(b.v, i / (D / 32), i % (D / 32));
     };
-
     // One pipeline step. Its MFMAs are O^T += V^T P^T of half tile hi-1 (probabilities
     // pk_prev) and S^T of half tile hi+1 (into s_next), taken alternately so consecutive MFMAs
     // are independent; beside them runs the softmax of half tile hi (s_cur -> pk_cur). The
@@ -283,12 +292,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
     // last slots, so the next step starts without waiting, even across a barrier: its
     // operands were staged before the previous barrier).
     // (with_pv false: half tile 0, whose step has no O update; its odd slots stay empty.)
-    // stage_j >= 0: this step also issues the loads of K of tile stage_j + 3 and V of tile
-    // stage_j + 2 (one DMA per odd slot).
-    auto step = [&](int hi, f32x16& s_cur, f32x16& s_next, const u32x4 (&pk_prev)[2],
-                    u32x4 (&pk_cur)[2], auto masked, bf16x8 (&fr)[kAhead], auto with_pv,
-                    int stage_j) {
+    // with_dma: this step (the first of tile j = hi / 2) also issues the loads of K of tile
+    // j + 3 and V of tile j + 2 (one DMA per odd slot).
+    auto step = [&](int hi, auto h8_c, f32x16& s_cur, f32x16& s_next, const u32x4 (&pk_prev)[2],
+                    u32x4 (&pk_cur)[2], bool masked, bf16x8 (&fr)[kAhead], auto with_pv,
+                    auto with_dma) {
+        constexpr int H8 = decltype(h8_c)::value;
         constexpr bool kPV = decltype(with_pv)::value;
+        constexpr bool kDma = decltype(with_dma)::value;
         constexpr int kS = D / 16;             // S^T MFMAs (one per 16 head dimensions)
         constexpr int kSlots = 2 * kS;         // as many O MFMAs: 2 key groups x D/32 blocks
         constexpr int kPhasesPerSlot = 16 / kSlots;
@@ -331,7 +342,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
         };
         auto phase = [&](int ph) {
             if (ph == 0) {
-                if constexpr (decltype(masked)::value) mask_scores();
+                if (__builtin_expect(masked, 0)) mask_scores();
                 t0 = vmax(vmax(s_cur[0], s_cur[1]), s_cur[2]);
                 t1 = vmax(vmax(s_cur[3], s_cur[4]), s_cur[5]);
                 t2 = vmax(vmax(s_cur[6], s_cur[7]), s_cur[8]);
@@ -356,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
             pair_stages(ph, 5);
         };
 
-        const Bases b_cur = bases(hi), b_next = bases(hi + 1);
+        const Bases b_cur = bases(h8_c), b_next = bases(std::integral_constant<int, (H8 + 1) & 7>{});
         bf16x8 cur[kSlots];
 #pragma unroll
         for (int sl = 0; sl < kAhead; ++sl) cur[sl] = fr[sl];
@@ -381,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
             // DMA i sits in slot 1 + 2 i
 #pragma unroll
             for (int i = 0; i < T::kDmaPerWave; ++i)
-                if (sl == 1 + 2 * i && stage_j >= 0) dma_op(stage_j, i);
+                if (sl == 1 + 2 * i && kDma) dma_op(hi >> 1, i, H8 >> 1);
             __builtin_amdgcn_sched_barrier(0);
         }
         // The probabilities are first used by the next step; without this the compiler sinks
@@ -389,36 +400,34 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
         asm volatile("" : "+v"(pk_cur[0]), "+v"(pk_cur[1]), "+v"(l_part));
         rescale(move, alpha);
     };
-    using Masked = std::true_type;
-    using Plain = std::false_type;
     // Tiles before n_plain need no mask in any wave of the workgroup: all their keys precede
-    // the workgroup's first query row (causal) and the end of the sequence. The remaining
-    // tiles run the masked step in every wave (a no-op mask where nothing is masked), so each
-    // loop below is a single straight path.
+    // the workgroup's first query row (causal) and the end of the sequence. The others mask
+    // in every wave (a no-op where nothing is masked), behind a uniform branch.
     const int n_plain = min_(n_tiles, causal ? (qb * kBr) / kBc : N / kBc);
 
     f32x16 sa, sb;
     u32x4 pa[2], pb[2];
     bf16x8 fr[kAhead];
 
+    using Yes = std::true_type;
+    using No = std::false_type;
+
     // ---- prologue: K0..K2 and V0, V1 staged; scores of half tile 0 ----
-    dma_tile(-3);  // K0 (and zeros for V of tile -1, in the stage V3 takes later)
-    dma_tile(-2);  // K1, V0
-    dma_tile(-1);  // K2, V1
+    dma_tile(-3, 1);  // K0 (and zeros for V of tile -1, in the stage V3 takes later)
+    dma_tile(-2, 2);  // K1, V0
+    dma_tile(-1, 3);  // K2, V1
     wait_dma_all();
     barrier_lds();
     compute_s(sa, 0, 0);
 
     // ---- tile 0: half 0 has no O update yet; its first step issues K3 / V2 ----
+    {
+        const Bases b0 = bases(std::integral_constant<int, 0>{});
 #pragma unroll
-    for (int sl = 0; sl < kAhead; ++sl) fr[sl] = (sl & 1) ? bf16x8{} : frag(bases(0), sl);
-    if (n_plain > 0) {
-        step(0, sa, sb, pb, pa, Plain{}, fr, std::false_type{}, 0);
-        step(1, sb, sa, pa, pb, Plain{}, fr, std::true_type{}, -1);
-    } else {
-        step(0, sa, sb, pb, pa, Masked{}, fr, std::false_type{}, 0);
-        step(1, sb, sa, pa, pb, Masked{}, fr, std::true_type{}, -1);
+        for (int sl = 0; sl < kAhead; ++sl) fr[sl] = (sl & 1) ? bf16x8{} : frag(b0, sl);
     }
+    step(0, std::integral_constant<int, 0>{}, sa, sb, pb, pa, n_plain == 0, fr, No{}, Yes{});
+    step(1, std::integral_constant<int, 1>{}, sb, sa, pa, pb, n_plain == 0, fr, Yes{}, No{});
     wait_dma_tile();
     barrier_lds();
 
@@ -426,28 +435,34 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
     // (half 1) and V_j (half 0). Its first step issues the loads of K_{j+3} and V_{j+2}
     // into the stages of K_{j-1} and V_{j-2}, both last read during tile j-1, before the
     // previous barrier; they have until the barrier that ends tile j+1 to land (the wait
-    // before each barrier leaves only the newest tile's loads in flight).
-    // (Do-while loops with the exit test at the bottom keep the accumulators in one set of
-    // registers.) ----
-    auto tile = [&](int j, auto masked) {
-        step(2 * j, sa, sb, pb, pa, masked, fr, std::true_type{}, j);
-        step(2 * j + 1, sb, sa, pa, pb, masked, fr, std::true_type{}, -1);
+    // before each barrier leaves only the newest tile's loads in flight). The loop is
+    // unrolled over the four stage phases (it starts at j = 1). ----
+    auto tile = [&](int j, auto phase_c) {
+        constexpr int P = decltype(phase_c)::value;
+        const bool masked = j >= n_plain;
+        step(2 * j, std::integral_constant<int, 2 * P>{}, sa, sb, pb, pa, masked, fr, Yes{}, Yes{});
+        step(2 * j + 1, std::integral_constant<int, 2 * P + 1>{}, sb, sa, pa, pb, masked, fr, Yes{}, No{});
         wait_dma_tile();
         barrier_lds();
     };
     int j = 1;
-    if (j < n_plain) {
-        do {
-            tile(j, Plain{});
-        } while (++j < n_plain);
-    }
-    if (j < n_tiles) {
-        do {
-            tile(j, Masked{});
-        } while (++j < n_tiles);
+    while (j < n_tiles) {
+        tile(j, std::integral_constant<int, 1>{});
+        if (++j >= n_tiles) break;
+        tile(j, std::integral_constant<int, 2>{});
+        if (++j >= n_tiles) break;
+        tile(j, std::integral_constant<int, 3>{});
+        if (++j >= n_tiles) break;
+        tile(j, std::integral_constant<int, 0>{});
+        ++j;
     }
     // last half tile's O update (its S^T step computed a score block past the end, unused)
-    compute_pv(pb, (n_tiles - 1) % kStages, 1);
+    switch ((n_tiles - 1) & 3) {
+        case 0: compute_pv(pb, 0, 1); break;
+        case 1: compute_pv(pb, 1, 1); break;
+        case 2: compute_pv(pb, 2, 1); break;
+        default: compute_pv(pb, 3, 1); break;
+    }
     wait_dma_all();  // no load may still be writing LDS when the workgroup ends
 
     // ---- epilogue: O / l, bf16, optional row statistics ----
