@@ -11,11 +11,10 @@
 // Schedule. A wave owns 32 query rows and walks the keys in 32-key half tiles h. Step h
 // issues, in one basic block, the MFMAs of O^T += V^T P^T for half tile h-1 and of
 // S^T = K Q^T for half tile h+1 (16 MFMAs, about 512 cycles) together with the vector work
-// that turns the scores of half tile h into probabilities (about 90 instructions). The two
+// that turns the scores of half tile h into probabilities (about 70 instructions). The two
 // streams are independent, so the SIMD runs them side by side; the scheduler is told to
 // interleave them (one MFMA, one LDS operand read, a few vector instructions, repeated).
-// Two such waves share each SIMD (8 waves, 256 query rows per workgroup), and each needs
-// only about 16 bytes of LDS operand per cycle, half of what one wave can draw.
+// Two such waves share each SIMD (8 waves, 256 query rows per workgroup).
 //
 // CDNA4 details:
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: a lane holds the scores of one query row,
@@ -23,16 +22,21 @@
 //    accumulator, converted to bf16, is directly the B operand of O^T += V^T P^T: the MFMA
 //    reads K rows in an order that swaps bits 2 and 3 of the row index, so the
 //    accumulator's register order is the key order the second MFMA needs.
-//  * K is staged in LDS row-major, V transposed ([d][key]), rows padded by 16 bytes: on
-//    gfx950's LDS (64 banks of 4 bytes) the MFMA operand reads and the staging writes are
-//    conflict free, and every operand address is one per-lane base plus an immediate.
-//  * Three LDS stages per operand: K and V of tile j+2 / j+1 are written while tiles j and
-//    j+1 are being read, with one workgroup barrier per 64-key tile. Threads 0-255 move K,
-//    256-511 move V (register-staged buffer loads, issued one tile ahead).
+//  * K and V tiles go from global memory straight into LDS (buffer loads with the LDS
+//    bit): no staging registers. Both are stored row-major with padded rows (K: +16 bytes,
+//    V: +64 bytes), which makes every operand read conflict free on gfx950's 64 banks; the
+//    V^T operand comes out of row-major V through ds_read_b64_tr_b16.
+//  * Four LDS stages per operand: K of tile j+3 and V of tile j+2 are requested while tile
+//    j is computed, with one workgroup barrier per 64-key tile. The tile loop is unrolled
+//    over the four stages, so every operand address is a loop-invariant base plus an
+//    immediate offset.
 //  * Scores in the log2 domain; the exponent reference moves only when a row maximum beats
-//    it by more than 2^8, so the O rescale (a branch after the MFMAs) is rare.
+//    it by more than 2^8, so the O rescale (a branch after the MFMAs, out of line) is rare.
+//    The row sum adds the bf16-rounded probabilities (v_dot2 on the packed pairs), i.e.
+//    exactly the weights the O MFMA uses.
 //  * Every wave runs every half tile of its workgroup (those past its own diagonal are
-//    fully masked and contribute nothing), so all waves follow one branch-free schedule.
+//    fully masked and contribute nothing), so all waves follow one schedule; masking is a
+//    uniform branch taken only on the diagonal and ragged tiles.
 //  * Grid: one workgroup per (256-row query block, head), XCD-contiguous work order.
 #include <type_traits>
 
