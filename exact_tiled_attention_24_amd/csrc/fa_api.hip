@@ -14,10 +14,9 @@ constexpr int kDecodePage = 16;
 constexpr int kDecodeD = 128;
 constexpr int kDecodeTargetWGs = 2 * fa::kPlanCUs;  // one round of 4-wave chunks
 
-// Forward kernel choice. Default: the software-pipelined 8-wave kernel for d = 128, the
-// 4-wave tiled kernel for d = 64 (measured faster there: with half the MFMAs per score the
-// tiled kernel's two independent workgroups per CU hide the softmax better). The environment
-// variable FA_FWD_KERNEL=tiled|sp overrides it (a tuning switch, read at every call).
+// Forward kernel choice. Default: the software-pipelined, persistent 8-wave kernel (faster
+// for d = 128 and d = 64 alike). The environment variable FA_FWD_KERNEL=tiled|sp selects
+// one explicitly (a tuning and testing switch, read at every call).
 enum FwdKernel { kFwdAuto = 0, kFwdTiled = 1, kFwdSoftPipe = 2 };
 FwdKernel fwd_kernel_override() {
     const char* e = getenv("FA_FWD_KERNEL");
@@ -99,7 +98,7 @@ fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void*
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
             return FA_ERR_INVALID_ARGUMENT;
         FwdKernel kern = fwd_kernel_override();
-        if (kern == kFwdAuto) kern = d == 128 ? kFwdSoftPipe : kFwdTiled;
+        if (kern == kFwdAuto) kern = kFwdSoftPipe;
         e = kern == kFwdSoftPipe
                 ? fa::launch_fwd_bf16_sp(q, k, v, o, m_out, l_out, B, Hq, Hkv, N, d, scale,
                                          causal ? 1 : 0, st)

@@ -89,24 +89,19 @@ struct Tile {
     static_assert(kKStage % 1024 == 0 && kVStage % 1024 == 0, "stages are whole DMA chunks");
 };
 
+// One work item: the 256-row query block and head that `item` names in the work list
+// (KV group, query block heaviest first, head in group). `smem` is the workgroup's LDS.
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
+__device__ __forceinline__ void fwd_item(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ m_out, float* __restrict__ l_out, int B, int Hq,
-    int Hkv, int N, float scale_log2, int causal, int nqb) {
+    int Hkv, int N, float scale_log2, int causal, int nqb, int item, unsigned char* smem) {
     using T = Tile<D>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * (T::kKStage + T::kVStage)];
     lds_cptr const lds = (lds_cptr)smem;  // generic -> LDS address space
     const unsigned lds_addr = (unsigned)(size_t)lds;  // LDS byte address of smem
 
-    // ---- work item: XCD-contiguous runs ordered (KV group, query block heaviest first,
-    // head in group); see fwd_bf16.hip ----
     const int G = Hq / Hkv;
     const int per_unit = nqb * G;
-    const int total = B * Hkv * per_unit;
-    const int per_xcd = (total + kXcds - 1) / kXcds;
-    const int item = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
-    if (item >= total) return;
     const int kvg = item / per_unit;
     const int rem = item - kvg * per_unit;
     const int qb = causal ? (nqb - 1 - rem / G) : rem / G;
@@ -467,7 +462,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
         case 2: compute_pv(pb, 2, 1); break;
         default: compute_pv(pb, 3, 1); break;
     }
-    wait_dma_all();  // no load may still be writing LDS when the workgroup ends
+    wait_dma_all();  // no load may still be writing LDS when the item ends
+    barrier_lds();   // and no wave still reads it when the next item's loads start
 
     // ---- epilogue: O / l, bf16, optional row statistics ----
     const float l_tot = pair32_sum(l_part);
@@ -491,14 +487,58 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
     }
 }
 
+// Persistent grid: one workgroup per CU (the LDS allows no second one), a multiple of the 8
+// XCDs. Workgroup w runs on XCD w mod 8 and walks the x-th contiguous eighth of the work
+// list (so one KV group's tiles are re-read from one XCD's L2), taking its items in snake
+// order over the XCD's workgroups: round r gives the workgroup of local index j the item
+// r * W + j (r even) or r * W + W - 1 - j (r odd). The list runs heaviest query block first,
+// so the snake pairs heavy with light items and the workgroups finish together; and a
+// workgroup moves to its next item without a new launch.
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, float* __restrict__ m_out, float* __restrict__ l_out, int B, int Hq,
+    int Hkv, int N, float scale_log2, int causal, int nqb) {
+    __shared__ __attribute__((aligned(16)))
+    unsigned char smem[kStages * (Tile<D>::kKStage + Tile<D>::kVStage)];
+    const int total = B * Hq * nqb;
+    const int per_xcd = (total + kXcds - 1) / kXcds;
+    const int xcd = (int)(blockIdx.x % kXcds), j = (int)(blockIdx.x / kXcds);
+    const int W = (int)(gridDim.x / kXcds);
+    const int seg0 = xcd * per_xcd;
+    const int seg_n = min_(per_xcd, total - seg0);
+    for (int r = 0; r * W < seg_n; ++r) {
+        const int local = r * W + ((r & 1) ? W - 1 - j : j);
+        if (local >= seg_n) continue;
+        fwd_item<D>(q, k, v, o, m_out, l_out, B, Hq, Hkv, N, scale_log2, causal, nqb,
+                    seg0 + local, smem);
+    }
+}
+
 }  // namespace
+
+// Compute units of the current device (cached per device; 256 on MI355X).
+int persistent_cus() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kPlanCUs;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < kXcds)
+            n = kPlanCUs;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 hipError_t launch_fwd_bf16_sp(const void* q, const void* k, const void* v, void* o, float* m_out,
                               float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
                               int causal, hipStream_t stream) {
     const int nqb = (N + kBr - 1) / kBr;
     const long long items = (long long)nqb * B * Hq;
-    const long long grid = (items + kXcds - 1) / kXcds * kXcds;
+    const long long slots = (long long)(persistent_cus() / kXcds) * kXcds;
+    long long grid = (items + kXcds - 1) / kXcds * kXcds;
+    if (grid > slots) grid = slots;
     const float sl2 = scale * kLog2e;
     auto qp = static_cast<const uint16_t*>(q);
     auto kp = static_cast<const uint16_t*>(k);
