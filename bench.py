@@ -115,7 +115,7 @@ def summarize(paths, kernel=None):
 # Kernels whose HBM traffic is reported, with the source file each is compiled from.
 TRAFFIC_KERNELS = {
     "fwd": ("fwd_bf16_sp_kernel", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
-    "decode": ("decode_bf16_kernel", "exact_tiled_attention_24_amd/csrc/decode.hip"),
+    "decode": ("decode_mx_kernel", "exact_tiled_attention_24_amd/csrc/decode_mx.hip"),
 }
 COPY_KERNEL = "copyBuffer"
 

@@ -158,10 +158,19 @@ fa_status fa_decode_splitk(fa_dtype dt, const void* q, const void* k_cache, cons
     float* ws_o = static_cast<float*>(workspace);
     float* ws_m = ws_o + (size_t)p.splits * B * Hq * d;
     float* ws_l = ws_m + (size_t)p.splits * B * Hq;
-    const hipError_t e = fa::launch_decode_bf16(
-        q, k_cache, v_cache, block_table, seq_lens, o, B, Hq, Hkv, d, num_pages,
-        max_pages_per_seq, p.len_cap, scale, p.splits, p.chunk_pages, ws_o, ws_m, ws_l,
-        static_cast<hipStream_t>(stream));
+    // Decode kernel: the matrix-core one by default; FA_DECODE_KERNEL=valu selects the vector
+    // ALU one (a tuning and testing switch, read at every call).
+    const char* dk = getenv("FA_DECODE_KERNEL");
+    const bool valu = dk && strcmp(dk, "valu") == 0;
+    const hipError_t e =
+        valu ? fa::launch_decode_bf16(q, k_cache, v_cache, block_table, seq_lens, o, B, Hq, Hkv,
+                                      d, num_pages, max_pages_per_seq, p.len_cap, scale,
+                                      p.splits, p.chunk_pages, ws_o, ws_m, ws_l,
+                                      static_cast<hipStream_t>(stream))
+             : fa::launch_decode_bf16_mx(q, k_cache, v_cache, block_table, seq_lens, o, B, Hq,
+                                         Hkv, d, num_pages, max_pages_per_seq, p.len_cap, scale,
+                                         p.splits, p.chunk_pages, ws_o, ws_m, ws_l,
+                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

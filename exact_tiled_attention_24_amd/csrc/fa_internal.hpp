@@ -34,6 +34,14 @@ hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_
                               int len_cap, float scale, int splits, int chunk_pages,
                               float* ws_o, float* ws_m, float* ws_l, hipStream_t stream);
 
+// The same with both products on the matrix cores (query heads per KV head <= 16).
+hipError_t launch_decode_bf16_mx(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens, void* o,
+                                 int B, int Hq, int Hkv, int d, int num_pages,
+                                 int max_pages_per_seq, int len_cap, float scale, int splits,
+                                 int chunk_pages, float* ws_o, float* ws_m, float* ws_l,
+                                 hipStream_t stream);
+
 // Row-wise merge of S partials. log2_units != 0: m is in log2 units (internal workspace);
 // otherwise natural-log units (public fa_merge). out_bf16 selects the output type.
 hipError_t launch_merge(const float* o_parts, const float* m_parts, const float* l_parts, void* o,

@@ -61,6 +61,22 @@ def test_decode_small(case, splits, dev):
     assert_close(to_np(o), o_ref, "bf16", "decode O")
 
 
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"B{c[0]}-Hq{c[1]}-Hkv{c[2]}")
+@pytest.mark.parametrize("kernel", ["valu", "mx"])
+def test_decode_each_kernel(case, kernel, dev, monkeypatch):
+    """Both decode kernels (vector-ALU and matrix-core) against the oracle."""
+    monkeypatch.setenv("FA_DECODE_KERNEL", kernel)
+    B, Hq, Hkv, lens = case
+    seed = 300 + SMALL.index(case)
+    log_case(f"fa_decode_splitk {kernel} {case} seed={seed}")
+    x = gen.decode_inputs(B, Hq, Hkv, 128, 16, seed=seed, lens=lens,
+                          max_pages_per_seq=-(-max(lens) // 16) + 3)
+    t = upload(x, dev)
+    o = run_decode(t, x.max_seq_len, x.scale, 2)
+    o_ref, _, _ = oracle.decode(x.q, x.k_seqs, x.v_seqs, x.scale)
+    assert_close(to_np(o), o_ref, "bf16", "decode O")
+
+
 def test_decode_config5_full(dev):
     import torch
 

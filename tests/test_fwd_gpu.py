@@ -40,6 +40,9 @@ SMALL = [
     ("bf16", 2, 3, 3, 1000, 128, True),
     ("bf16", 1, 8, 2, 513, 128, False),
     ("bf16", 1, 2, 1, 2048, 128, True),
+    # more work items than CUs: several items per persistent workgroup, ragged tiles
+    ("bf16", 4, 32, 8, 1000, 128, True),
+    ("bf16", 2, 64, 64, 777, 64, False),
     ("f32", 1, 1, 1, 256, 64, False),
     ("f32", 2, 4, 2, 100, 128, True),
     ("f32", 1, 2, 1, 1, 64, True),
