@@ -63,18 +63,73 @@ def test_decode_small(case, splits, dev):
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"B{c[0]}-Hq{c[1]}-Hkv{c[2]}")
 @pytest.mark.parametrize("kernel", ["valu", "mx"])
-def test_decode_each_kernel(case, kernel, dev, monkeypatch):
-    """Both decode kernels (vector-ALU and matrix-core) against the oracle."""
+@pytest.mark.parametrize("splits", [0, 2])
+def test_decode_each_kernel(case, kernel, splits, dev, monkeypatch):
+    """The fixed-chunk plan on both decode kernels (vector-ALU and matrix-core), with its
+    automatic split count and with an explicit one, against the oracle."""
     monkeypatch.setenv("FA_DECODE_KERNEL", kernel)
     B, Hq, Hkv, lens = case
     seed = 300 + SMALL.index(case)
-    log_case(f"fa_decode_splitk {kernel} {case} seed={seed}")
+    log_case(f"fa_decode_splitk {kernel} {case} splits={splits} seed={seed}")
     x = gen.decode_inputs(B, Hq, Hkv, 128, 16, seed=seed, lens=lens,
                           max_pages_per_seq=-(-max(lens) // 16) + 3)
     t = upload(x, dev)
-    o = run_decode(t, x.max_seq_len, x.scale, 2)
+    o = run_decode(t, x.max_seq_len, x.scale, splits)
     o_ref, _, _ = oracle.decode(x.q, x.k_seqs, x.v_seqs, x.scale)
     assert_close(to_np(o), o_ref, "bf16", "decode O")
+
+
+EDGE = [
+    # B, Hq, Hkv, lens: the automatic plan on awkward length mixes
+    (1, 8, 1, [40000]),                      # one (sequence, KV head) pair: many chunks
+    (1, 4, 4, [20]),                         # two pages in all
+    (6, 8, 2, [0, 300, 0, 0, 1, 5000]),      # empty sequences between and before others
+    (70, 8, 2, None),                        # many sequences, a fifth of them empty
+    (9, 16, 2, [17, 33, 4097, 16, 15, 2, 900, 1, 64]),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: f"B{c[0]}-Hq{c[1]}-Hkv{c[2]}")
+def test_decode_edge_lengths(case, dev):
+    B, Hq, Hkv, lens = case
+    seed = 400 + EDGE.index(case)
+    if lens is None:
+        rng = np.random.default_rng(seed)
+        lens = [int(v) if rng.random() > 0.2 else 0 for v in rng.integers(1, 3000, size=B)]
+    log_case(f"fa_decode_splitk edge {B, Hq, Hkv} lens={lens[:10]} seed={seed}")
+    x = gen.decode_inputs(B, Hq, Hkv, 128, 16, seed=seed, lens=lens,
+                          max_pages_per_seq=-(-max(max(lens), 1) // 16) + 2)
+    t = upload(x, dev)
+    o = to_np(run_decode(t, x.max_seq_len, x.scale))
+    o_ref, _, _ = oracle.decode(x.q, x.k_seqs, x.v_seqs, x.scale)
+    assert_close(o, o_ref, "bf16", "decode O")
+    for b in range(B):
+        if lens[b] == 0:
+            assert np.all(o[b] == 0)
+
+
+def test_decode_all_empty(dev):
+    log_case("fa_decode_splitk, every length 0")
+    x = gen.decode_inputs(3, 8, 2, 128, 16, seed=410, lens=[0, 0, 0], max_pages_per_seq=2)
+    o = to_np(run_decode(upload(x, dev), 0, x.scale))
+    assert np.all(o == 0)
+
+
+def test_decode_length_clamped_to_table(dev):
+    """Lengths beyond max_pages_per_seq * 16 are clamped (automatic and explicit splits): the
+    result is that of the clamped sequence."""
+    import torch
+
+    log_case("fa_decode_splitk clamp")
+    x = gen.decode_inputs(2, 8, 2, 128, 16, seed=411, lens=[64, 50])
+    t = upload(x, dev)
+    t["seq_lens"] = torch.tensor([100, 50], dtype=torch.int32, device=dev)  # beyond 4 pages
+    o_ref, _, _ = oracle.decode(x.q, x.k_seqs, x.v_seqs, x.scale)
+    for splits in (0, 2):
+        o = fa.fa_decode_splitk(t["q"], t["k_cache"], t["v_cache"], t["block_table"],
+                                t["seq_lens"], 64, scale=x.scale, num_splits=splits)
+        torch.cuda.synchronize()
+        assert_close(to_np(o), o_ref, "bf16", f"clamped, splits={splits}")
 
 
 def test_decode_config5_full(dev):
