@@ -37,7 +37,9 @@
 //  * Every wave runs every half tile of its workgroup (those past its own diagonal are
 //    fully masked and contribute nothing), so all waves follow one schedule; masking is a
 //    uniform branch taken only on the diagonal and ragged tiles.
-//  * Grid: one workgroup per (256-row query block, head), XCD-contiguous work order.
+//  * Grid: one persistent workgroup per CU; a work item is one (256-row query block, head),
+//    and each workgroup walks items of its XCD's contiguous share of the list in snake
+//    order (see the kernel).
 #include <type_traits>
 
 #include "fa_internal.hpp"
