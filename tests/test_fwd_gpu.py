@@ -43,6 +43,9 @@ SMALL = [
     # more work items than CUs: several items per persistent workgroup, ragged tiles
     ("bf16", 4, 32, 8, 1000, 128, True),
     ("bf16", 2, 64, 64, 777, 64, False),
+    # wide query groups: 8 and 16 query heads per KV head
+    ("bf16", 1, 16, 2, 600, 128, True),
+    ("bf16", 2, 16, 1, 300, 64, False),
     ("f32", 1, 1, 1, 256, 64, False),
     ("f32", 2, 4, 2, 100, 128, True),
     ("f32", 1, 2, 1, 1, 64, True),
