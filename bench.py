@@ -41,6 +41,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--fwd-config", type=int, default=3, choices=[2, 3, 4])
     ap.add_argument("--decode-splits", type=int, default=0, help="0 = the library's plan")
+    ap.add_argument("--kv-pools", type=int, default=1,
+                    help="copies of the decode KV cache used in turn, so that no call finds the "
+                         "previous call's pages in the caches (1 = one cache)")
+    ap.add_argument("--decode-mx", default=None, metavar="W,S",
+                    help="matrix-core decode variant: waves per workgroup, page slots per wave "
+                         "(default 4,2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64,
                     help="heads of the forward workload the oracle is timed on")
@@ -221,11 +227,14 @@ def main():
         o = torch.empty_like(q)
 
     dec_bytes, splits, lens_sum = None, None, None
+    if args.decode_mx:
+        os.environ["FA_DECODE_MX"] = args.decode_mx
     if do_dec:
         dx = gen.config_decode_inputs(dcfg)
         dq = gen.to_torch(dx.q, "bf16", dev)
         kc = gen.to_torch(dx.k_cache, "bf16", dev)
         vc = gen.to_torch(dx.v_cache, "bf16", dev)
+        pools = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(max(1, args.kv_pools) - 1)]
         table = torch.from_numpy(dx.block_table).to(dev)
         lens = torch.from_numpy(dx.lens.astype(np.int32)).to(dev)
         do = torch.empty_like(dq)
@@ -243,8 +252,12 @@ def main():
     def run_fwd():
         fa.fa_fwd(q, k, v, scale=fx.scale, causal=fcfg.causal, out=o)
 
+    calls = [0]
+
     def run_decode():
-        fa.fa_decode_splitk(dq, kc, vc, table, lens, dcfg.len_max, scale=dec_scale,
+        kp, vp = pools[calls[0] % len(pools)]
+        calls[0] += 1
+        fa.fa_decode_splitk(dq, kp, vp, table, lens, dcfg.len_max, scale=dec_scale,
                             num_splits=args.decode_splits, out=do, workspace=ws)
 
     copy_src = copy_dst = None

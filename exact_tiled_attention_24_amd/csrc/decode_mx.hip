@@ -31,6 +31,9 @@
 //  * At the end the waves' states are merged through LDS and one normalised float32 partial
 //    (m in log2 units, l, O) per (chunk, query head) is written to the workspace; the merge
 //    kernel (merge.hip) combines the chunks.
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "fa_internal.hpp"
 #include "gfx950.hpp"
 
@@ -39,12 +42,9 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kPage = 16;
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kQ = 16;                          // query columns of the products
 constexpr int kPiece = kPage * kD * 2;          // bytes of K (or V) of one page and KV head
 constexpr int kSlot = 2 * kPiece;               // K then V
-constexpr int kSlots = 2;                       // page slots per wave
 constexpr int kLoadsPerPage = 2 * kPiece / 1024;  // 1 KiB per load instruction
 constexpr float kTau = 8.f;                     // lazy-rescale threshold, log2 units
 constexpr int kBufferDword3 = 0x00020000;
@@ -63,12 +63,16 @@ __device__ __forceinline__ float xlane_sum(float x) {
     return x + __shfl_xor(x, 32);
 }
 
-__global__ __launch_bounds__(kThreads, 2) void decode_mx_kernel(
+// W waves per workgroup, S page slots per wave (S - 1 pages in flight while one is consumed).
+template <int W, int S>
+__global__ __launch_bounds__(64 * W) void decode_mx_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ table,
     const int32_t* __restrict__ lens, float* __restrict__ ws_o, float* __restrict__ ws_m,
     float* __restrict__ ws_l, int Hq, int Hkv, int G, int num_pages, int max_pages,
     int len_cap, float scale_log2, int chunk_pages) {
+    constexpr int kWaves = W, kSlots = S, kThreads = 64 * W;
+    static_assert(S >= 2 && (S - 1) * kLoadsPerPage <= 63, "vmcnt holds at most 63 loads");
     __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * kSlots * kSlot];
     lds_cptr const lds = (lds_cptr)smem;
     const unsigned lds_addr = (unsigned)(size_t)lds;
@@ -246,21 +250,27 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mx_kernel(
         };
 
         // LDS loads are not tracked by the compiler's waits: wait for all but the newest
-        // page's loads (vmcnt counts this wave's vector loads in issue order).
+        // S - 1 pages' loads (vmcnt counts this wave's vector loads in issue order).
         auto wait_older = [&]() {
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerPage) : "memory");
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kSlots - 1) * kLoadsPerPage) : "memory");
         };
-        int ph0 = issue(0, 0), ph1 = -1;
+        // Page i sits in slot i % S; page i + S - 1 is requested just before page i is
+        // consumed. The loop is unrolled over the slots so every slot index is a constant.
+        int ph[kSlots];
+#pragma unroll
+        for (int s = 0; s + 1 < kSlots; ++s) ph[s] = issue(s, s);
         int i = 0;
-        for (;;) {
-            ph1 = issue(i + 1, 1);
-            wait_older();
-            process(i, 0, ph0);
-            if (++i >= n_mine) break;
-            ph0 = issue(i + 1, 0);
-            wait_older();
-            process(i, 1, ph1);
-            if (++i >= n_mine) break;
+        for (bool more = true; more;) {
+#pragma unroll
+            for (int s = 0; s < kSlots; ++s) {
+                if (more) {
+                    const int sn = (s + kSlots - 1) % kSlots;
+                    ph[sn] = issue(i + kSlots - 1, sn);
+                    wait_older();
+                    process(i, s, ph[s]);
+                    more = ++i < n_mine;
+                }
+            }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the extra page's loads
     }
@@ -323,11 +333,20 @@ hipError_t launch_decode_bf16_mx(const void* q, const void* k_cache, const void*
                                  hipStream_t stream) {
     (void)d;
     const dim3 grid((unsigned)(B * Hkv), (unsigned)splits);
-    hipLaunchKernelGGL(decode_mx_kernel, grid, dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
-                       static_cast<const uint16_t*>(v_cache), block_table, seq_lens, ws_o, ws_m,
-                       ws_l, Hq, Hkv, Hq / Hkv, num_pages, max_pages_per_seq, len_cap,
-                       scale * kLog2e, chunk_pages);
+    int W = 4, S = 2;
+    if (const char* e = getenv("FA_DECODE_MX")) sscanf(e, "%d,%d", &W, &S);
+#define FA_MX_CASE(w, s)                                                                         \
+    if (W == w && S == s) {                                                                      \
+        hipLaunchKernelGGL((decode_mx_kernel<w, s>), grid, dim3(64 * w), 0, stream,              \
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache), \
+                           static_cast<const uint16_t*>(v_cache), block_table, seq_lens, ws_o,   \
+                           ws_m, ws_l, Hq, Hkv, Hq / Hkv, num_pages, max_pages_per_seq, len_cap, \
+                           scale * kLog2e, chunk_pages);                                         \
+    } else
+    FA_MX_CASE(2, 3) FA_MX_CASE(2, 4) FA_MX_CASE(3, 3) FA_MX_CASE(3, 4) FA_MX_CASE(4, 3)
+    FA_MX_CASE(4, 4) FA_MX_CASE(5, 4) FA_MX_CASE(6, 3) FA_MX_CASE(8, 2) FA_MX_CASE(4, 2)
+    return hipErrorInvalidValue;
+#undef FA_MX_CASE
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_merge(ws_o, ws_m, ws_l, o, 1, nullptr, nullptr, splits, B * Hq, kD, 1, stream);
