@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64,
                     help="heads of the forward workload the oracle is timed on")
-    ap.add_argument("--only", choices=["fwd", "decode"], default=None,
+    ap.add_argument("--only", choices=["fwd", "decode", "paged"], default=None,
                     help="time one kernel only (profiling runs)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling)")
@@ -212,6 +212,7 @@ def main():
 
     do_fwd = args.only in (None, "fwd")
     do_dec = args.only in (None, "decode")
+    do_paged = args.only in (None, "paged")
 
     # ---- inputs, resident in HBM ----
     fcfg = gen.CONFIGS[args.fwd_config]
@@ -248,6 +249,25 @@ def main():
                      + 4 * int(sum(-(-int(L) // 16) for L in dx.lens)) + 4 * dcfg.B)
         dec_scale = dx.scale
         del dx
+
+    paged_flops = None
+    if do_paged:
+        pcfg = gen.PREFILL_PAGED
+        px = gen.config_prefill_paged_inputs(pcfg)
+        p_q = gen.to_torch(px.q, "bf16", dev)
+        p_kc = gen.to_torch(px.k_cache, "bf16", dev)
+        p_vc = gen.to_torch(px.v_cache, "bf16", dev)
+        p_tab = torch.from_numpy(px.block_table).to(dev)
+        p_lens = torch.from_numpy(px.lens.astype(np.int32)).to(dev)
+        p_o = torch.empty_like(p_q)
+        paged_flops = px.flops()
+        paged_scale = px.scale
+        paged_lens = [int(L) for L in px.lens]
+        del px
+
+    def run_paged():
+        fa.fa_fwd_paged(p_q, p_kc, p_vc, p_tab, p_lens, scale=paged_scale, causal=pcfg.causal,
+                        out=p_o)
 
     def run_fwd():
         fa.fa_fwd(q, k, v, scale=fx.scale, causal=fcfg.causal, out=o)
@@ -291,6 +311,20 @@ def main():
         for _ in range(3):
             copy_dst.copy_(copy_src)
         torch.cuda.synchronize()
+
+    # chunked prefill over the paged cache: timed on its own, after the steps
+    paged_ms = None
+    if do_paged:
+        for _ in range(args.warmup):
+            run_paged()
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in pev:
+            a.record(stream)
+            run_paged()
+            b.record(stream)
+        torch.cuda.synchronize()
+        paged_ms = np.array([a.elapsed_time(b) for a, b in pev])
 
     fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     dec_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
@@ -348,6 +382,16 @@ def main():
         },
         "fwd_tokens_per_s": round(fcfg.B * fcfg.N / (fwd_ms.mean() * 1e-3), 1) if do_fwd else None,
     }
+    if do_paged:
+        p_tflops = paged_flops / (paged_ms.mean() * 1e-3) / 1e12
+        result["paged_prefill"] = {
+            "workload": pcfg.name, "seq_lens": paged_lens, "algorithmic_flops": paged_flops,
+            "value": round(p_tflops, 2), "unit": "TFLOP/s",
+            "avg_call_ms": round(float(paged_ms.mean()), 5),
+            "tokens_per_s": round(pcfg.B * pcfg.Nq / (paged_ms.mean() * 1e-3), 1),
+            "roofline": {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4)},
+        }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(fx, fcfg, args.cpu_heads)
     print(json.dumps(result), flush=True)

@@ -9,6 +9,7 @@ raises.
 Entry points (same names as the C ABI):
     fa_fwd(q, k, v, scale=None, causal=False, out=None, return_stats=False)
     fa_decode_splitk(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, ...)
+    fa_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=True, ...)
     fa_merge(o_parts, m_parts, l_parts, out_dtype=torch.float32, return_stats=False)
     fa_decode_workspace_bytes(...), fa_decode_plan_splits(...), fa_status_string(code)
 """
@@ -59,6 +60,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_decode_plan_splits.argtypes = [i32, i32, i32, i32]
     lib.fa_decode_plan_splits.restype = i32
+    lib.fa_fwd_paged.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                 i32, i32, i32, f32, i32, vp]
+    lib.fa_fwd_paged.restype = i32
     lib.fa_merge.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
     lib.fa_merge.restype = i32
     lib.fa_status_string.argtypes = [i32]
@@ -188,6 +192,45 @@ def fa_decode_splitk(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, sc
             workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(code, "fa_decode_splitk")
     return o
+
+
+def fa_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=True, out=None,
+                 return_stats=False):
+    """Chunked prefill over a paged KV cache: each sequence's newest Nq tokens attend to its
+    whole cache (query i at position seq_lens[b] - Nq + i).
+
+    q: [B, Hq, Nq, d] bf16; k_cache, v_cache: [num_pages, Hkv, 16, d] bf16; block_table:
+    int32 [B, max_pages_per_seq]; seq_lens: int32 [B] (all on the GPU). Returns O [B, Hq, Nq,
+    d] bf16, or (O, m, l) with float32 [B, Hq, Nq] statistics when ``return_stats``.
+    """
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B, Hq, Nq, d]; caches [num_pages, Hkv, page_size, d]")
+    B, Hq, Nq, d = q.shape
+    num_pages, Hkv, page_size, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("head dimension mismatch between q and the cache")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages_per_seq] and seq_lens [B]")
+    o = torch.empty_like(q) if out is None else out
+    m = l = None
+    if return_stats:
+        m = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+        l = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _require_gpu(q, k_cache, v_cache, block_table, seq_lens, o, m, l)
+    if o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        code = lib.fa_fwd_paged(
+            _dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(seq_lens), _ptr(o), _ptr(m), _ptr(l), B, Hq, Hkv, Nq, d, page_size, num_pages,
+            block_table.shape[1], scale, 1 if causal else 0, _stream(q.device))
+    _check(code, "fa_fwd_paged")
+    return (o, m, l) if return_stats else o
 
 
 def fa_merge(o_parts, m_parts, l_parts, out_dtype=None, return_stats=False, out=None):

@@ -174,6 +174,32 @@ fa_status fa_decode_splitk(fa_dtype dt, const void* q, const void* k_cache, cons
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_fwd_paged(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, const int32_t* seq_lens, void* o,
+                       float* m_out, float* l_out, int B, int Hq, int Hkv, int Nq, int d,
+                       int page_size, int num_pages, int max_pages_per_seq, float scale,
+                       int causal, void* stream) {
+    if (dt != FA_F32 && dt != FA_BF16) return FA_ERR_INVALID_ARGUMENT;
+    if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || num_pages < 0 || max_pages_per_seq < 0 ||
+        page_size < 1)
+        return FA_ERR_INVALID_ARGUMENT;
+    if (!scale_ok(scale)) return FA_ERR_INVALID_ARGUMENT;
+    if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0)) return FA_ERR_INVALID_ARGUMENT;
+    if (dt != FA_BF16 || (d != 64 && d != 128) || page_size != kDecodePage) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || Hq == 0 || Nq == 0) return FA_OK;
+    if (!q || !o || !block_table || !seq_lens) return FA_ERR_INVALID_ARGUMENT;
+    if (num_pages > 0 && (!k_cache || !v_cache)) return FA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+        return FA_ERR_INVALID_ARGUMENT;
+    if ((long long)Nq * d >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    if (((long long)Nq + 255) / 256 * B * Hq >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    if ((long long)max_pages_per_seq * page_size >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    const hipError_t e = fa::launch_fwd_bf16_sp_paged(
+        q, k_cache, v_cache, block_table, seq_lens, o, m_out, l_out, B, Hq, Hkv, Nq, d, num_pages,
+        max_pages_per_seq, scale, causal ? 1 : 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_merge(fa_dtype out_dt, const float* o_parts, const float* m_parts,
                    const float* l_parts, void* o, float* m_out, float* l_out, int S, int R, int d,
                    void* stream) {

@@ -40,6 +40,15 @@
 //  * Grid: one persistent workgroup per CU; a work item is one (256-row query block, head),
 //    and each workgroup walks items of its XCD's contiguous share of the list in snake
 //    order (see the kernel).
+//
+// Paged variant (kPaged): chunked prefill over a paged KV cache, the paged rows of the
+// family table on the same page. The queries are the newest Nq tokens of each sequence, so
+// query i sits at position L - Nq + i of its L cached tokens and the causal diagonal is
+// aligned to the bottom right. K/V of token t come from physical page
+// block_table[b][t / 16], slot t % 16. Each 16-row page of a K stage starts at a 1 KiB
+// boundary in LDS (V pages are whole KiB already), so every 1 KiB load lies in one page
+// and takes a scalar descriptor for that page, whose range ends at the sequence end (rows
+// past it fill with zeros). Block-table entries are scalar loads issued one tile ahead.
 #include <type_traits>
 
 #include "fa_internal.hpp"
@@ -76,29 +85,60 @@ __device__ __forceinline__ void barrier_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int D>
+constexpr int kPageTok = 16;      // tokens per page of the paged cache
+
+template <int D, bool kPaged>
 struct Tile {
     static constexpr int kKRow = D * 2 + 16;                          // padded K row, bytes
     // padded V row, bytes: the 64 B pad puts the four rows a transposing read touches per
     // cycle in four different 64 B bank windows
     static constexpr int kVRow = D * 2 + 64;
-    static constexpr int kKStage = kBc * kKRow;
+    // paged: a K page (16 padded rows) occupies whole KiB, so no 1 KiB load spans two pages
+    static constexpr int kKPage = kPaged ? (kPageTok * kKRow + 1023) / 1024 * 1024 : kPageTok * kKRow;
+    static constexpr int kKStage = kPaged ? (kBc / kPageTok) * kKPage : kBc * kKRow;
     static constexpr int kVStage = kBc * kVRow;
+    static constexpr int kKChunksPerPage = kKPage / 1024;             // paged only
+    static constexpr int kVChunksPerPage = kPageTok * kVRow / 1024;
     static constexpr int kVBase = kStages * kKStage;                  // V stages follow K's
     static constexpr int kKChunks = kKStage / 1024;                   // 1 KiB DMA chunks
     static constexpr int kVChunks = kVStage / 1024;
     static constexpr int kDmaPerWave = (kKChunks + kVChunks + kWaves - 1) / kWaves;
     static_assert(kKStage % 1024 == 0 && kVStage % 1024 == 0, "stages are whole DMA chunks");
+    static_assert(!kPaged || (kPageTok * kVRow) % 1024 == 0, "V pages are whole DMA chunks");
+    static_assert(kStages * (kKStage + kVStage) <= 160 * 1024, "fits the LDS of one CU");
+};
+
+// Kernel arguments. Dense: k, v are [B, Hkv, N, d]. Paged: k, v are the caches
+// [num_pages, Hkv, 16, d], N is the query count Nq, and table / lens name the pages and the
+// cached length of each sequence.
+struct FwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* o;
+    float* m_out;
+    float* l_out;
+    const int32_t* table;
+    const int32_t* lens;
+    int B, Hq, Hkv, N;
+    float scale_log2;
+    int causal, nqb;
+    int max_pages, num_pages;
 };
 
 // One work item: the 256-row query block and head that `item` names in the work list
 // (KV group, query block heaviest first, head in group). `smem` is the workgroup's LDS.
-template <int D>
-__device__ __forceinline__ void fwd_item(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ m_out, float* __restrict__ l_out, int B, int Hq,
-    int Hkv, int N, float scale_log2, int causal, int nqb, int item, unsigned char* smem) {
-    using T = Tile<D>;
+template <int D, bool kPaged>
+__device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned char* smem) {
+    using T = Tile<D, kPaged>;
+    const uint16_t* __restrict__ q = a.q;
+    const uint16_t* __restrict__ k = a.k;
+    const uint16_t* __restrict__ v = a.v;
+    uint16_t* __restrict__ o = a.o;
+    float* __restrict__ m_out = a.m_out;
+    float* __restrict__ l_out = a.l_out;
+    const int Hq = a.Hq, Hkv = a.Hkv, N = a.N, nqb = a.nqb, causal = a.causal;
+    const float scale_log2 = a.scale_log2;
     lds_cptr const lds = (lds_cptr)smem;  // generic -> LDS address space
     const unsigned lds_addr = (unsigned)(size_t)lds;  // LDS byte address of smem
 
@@ -113,10 +153,19 @@ __device__ __forceinline__ void fwd_item(
     const int h = kvh * G + gi;
 
     const size_t qoff = ((size_t)(b * Hq + h) * N) * D;
-    const size_t koff = ((size_t)(b * Hkv + kvh) * N) * D;
+    const size_t koff = kPaged ? 0 : ((size_t)(b * Hkv + kvh) * N) * D;
     const uint16_t* qh = q + qoff;
     const uint16_t* kh = k + koff;
     const uint16_t* vh = v + koff;
+    // Keys of this item's sequence and the position offset of its queries: query row i sits
+    // at position i + off (dense: the N keys, off = 0; paged: the cached length L, clamped to
+    // the table, and off = L - Nq, the bottom-right alignment).
+    int Nk = N, off = 0;
+    if constexpr (kPaged) {
+        const int L = a.lens[b];
+        Nk = __builtin_amdgcn_readfirstlane(L < 0 ? 0 : min_(L, a.max_pages * kPageTok));
+        off = Nk - N;
+    }
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -141,8 +190,8 @@ __device__ __forceinline__ void fwd_item(
     for (int i = 0; i < D / 32; ++i) acc_o[i] = f32x16{};
     float m_run = -INFINITY, m_ref = -INFINITY, l_part = 0.f;
 
-    const int kv_end = causal ? min_(N, qb * kBr + kBr) : N;
-    const int n_tiles = (kv_end + kBc - 1) / kBc;
+    const int kv_end = causal ? min_(Nk, qb * kBr + kBr + off) : Nk;
+    const int n_tiles = kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0;
 
     // ---- staging: buffer loads straight into LDS (no registers). A tile's K stage (64
     // padded rows) and V stage (64 padded rows, row-major) are cut into 1 KiB chunks; one
@@ -158,19 +207,62 @@ __device__ __forceinline__ void fwd_item(
     // V) and its LDS offset (relative to the stage) are fixed here. The descriptors span the
     // head's rows up to the end of this work item's last tile, so loads issued past the end
     // fetch nothing and fill zeros (as do the negative tile offsets of the prologue).
+    // Paged: chunk c of a stage belongs to page c / (chunks per page) of the tile (the same
+    // for all lanes: wave-uniform); the lane offset is relative to that page's 16 x d block.
     int dma_src[T::kDmaPerWave];
     unsigned dma_dst[T::kDmaPerWave];
+    int dma_pg[T::kDmaPerWave];
 #pragma unroll
     for (int i = 0; i < T::kDmaPerWave; ++i) {
         const int c = min_(wave + kWaves * i, T::kKChunks + T::kVChunks - 1);
         const bool is_k = c < T::kKChunks;
         const int row_b = is_k ? T::kKRow : T::kVRow;
-        const int slot = 1024 * (is_k ? c : c - T::kKChunks) + 16 * lane;
-        const int row = slot / row_b, col = slot - row * row_b;
-        dma_src[i] = (col < D * 2 ? row * D * 2 + col : kPadOffset) + (is_k ? 3 : 2) * kBc * D * 2;
-        dma_dst[i] = lds_addr + (is_k ? 0u : unsigned(T::kVBase)) + 1024u * (is_k ? c : c - T::kKChunks);
+        const int cc = is_k ? c : c - T::kKChunks;
+        dma_dst[i] = lds_addr + (is_k ? 0u : unsigned(T::kVBase)) + 1024u * cc;
+        if constexpr (kPaged) {
+            const int cpp = is_k ? T::kKChunksPerPage : T::kVChunksPerPage;
+            dma_pg[i] = cc / cpp;
+            const int slot = 1024 * (cc - dma_pg[i] * cpp) + 16 * lane;
+            const int row = slot / row_b, col = slot - row * row_b;
+            dma_src[i] = row < kPageTok && col < D * 2 ? row * D * 2 + col : kPadOffset;
+        } else {
+            const int slot = 1024 * cc + 16 * lane;
+            const int row = slot / row_b, col = slot - row * row_b;
+            dma_src[i] = (col < D * 2 ? row * D * 2 + col : kPadOffset) + (is_k ? 3 : 2) * kBc * D * 2;
+            dma_pg[i] = 0;
+        }
     }
-    const int row_end = min_(N, n_tiles * kBc);
+    // Paged: block-table entries of the K tile being loaded (ek, pages 4t .. 4t + 3) and of
+    // the V tile (ev, one tile behind: the K entries of the previous tile). They come from
+    // a window of 64 entries held one per lane (pages w0 .. w0 + 63) and read back with
+    // v_readlane; the next window is loaded one tile before it is needed. Entries of pages
+    // past the sequence are never used (their loads get an empty range).
+    int ek0 = -1, ek1 = -1, ek2 = -1, ek3 = -1, ev0 = -1, ev1 = -1, ev2 = -1, ev3 = -1;
+    int w0 = 0, win = -1, win_next = -1;
+    const int32_t* trow = nullptr;
+    if constexpr (kPaged) trow = a.table + (size_t)b * a.max_pages;
+    auto table_window = [&](int first) {  // entries first + lane (clamped into the row)
+        return trow[min_(first + lane, a.max_pages - 1)];
+    };
+    // Before the loads of K tile t (and V tile t - 1).
+    auto advance = [&](int t) {
+        if constexpr (kPaged) {
+            if (4 * t >= w0 + 64) {
+                w0 += 64;
+                win = win_next;
+            }
+            ev0 = ek0, ev1 = ek1, ev2 = ek2, ev3 = ek3;
+            const int wi = 4 * t - w0;
+            ek0 = __builtin_amdgcn_readlane(win, wi);
+            ek1 = __builtin_amdgcn_readlane(win, wi + 1);
+            ek2 = __builtin_amdgcn_readlane(win, wi + 2);
+            ek3 = __builtin_amdgcn_readlane(win, wi + 3);
+            if (4 * t + 4 == w0 + 64) win_next = table_window(w0 + 64);
+        }
+    };
+    const size_t page_stride = (size_t)Hkv * kPageTok * D;  // elements per physical page
+    const size_t kv_page = (size_t)kvh * kPageTok * D;       // this KV head within a page
+    const int row_end = min_(Nk, n_tiles * kBc);
     // (readfirstlane: the clamp selects to a vector instruction, and a descriptor word in a
     // VGPR would force a per-lane loop around every buffer load)
     const int head_bytes = __builtin_amdgcn_readfirstlane(row_end * D * 2);
@@ -189,11 +281,32 @@ __device__ __forceinline__ void fwd_item(
         const bool is_k = all_k || (!all_v && wave + kWaves * i < kK);
         const unsigned stage = is_k ? unsigned(((P + 3) & (kStages - 1)) * T::kKStage)
                                     : unsigned(((P + 2) & (kStages - 1)) * T::kVStage);
-        const __amdgpu_buffer_rsrc_t r = is_k ? rsrc_k : rsrc_v;
-        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
-                     :
-                     : "v"(dma_src[i] + j * (kBc * D * 2)), "s"(r), "{m0}"(dma_dst[i] + stage)
-                     : "memory");
+        if constexpr (kPaged) {
+            // page 4 t + pg of the sequence, t = j + 3 (K) or j + 2 (V): a descriptor over
+            // its rows that exist (none past the sequence end or for an invalid entry)
+            const int pg = dma_pg[i];
+            const int t = j + (is_k ? 3 : 2);
+            const int e0 = is_k ? ek0 : ev0, e1 = is_k ? ek1 : ev1;
+            const int e2 = is_k ? ek2 : ev2, e3 = is_k ? ek3 : ev3;
+            const int phys = pg == 0 ? e0 : (pg == 1 ? e1 : (pg == 2 ? e2 : e3));
+            const int rows = Nk - kPageTok * (4 * t + pg);
+            const bool ok = t >= 0 && rows > 0 && phys >= 0 && phys < a.num_pages;
+            const int bytes = __builtin_amdgcn_readfirstlane(ok ? min_(rows, kPageTok) * D * 2 : 0);
+            const int ph = __builtin_amdgcn_readfirstlane(ok ? phys : 0);
+            const uint16_t* src = (is_k ? k : v) + (size_t)ph * page_stride + kv_page;
+            const __amdgpu_buffer_rsrc_t r =
+                __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, bytes, kBufferDword3);
+            asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :
+                         : "v"(dma_src[i]), "s"(r), "{m0}"(dma_dst[i] + stage)
+                         : "memory");
+        } else {
+            const __amdgpu_buffer_rsrc_t r = is_k ? rsrc_k : rsrc_v;
+            asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :
+                         : "v"(dma_src[i] + j * (kBc * D * 2)), "s"(r), "{m0}"(dma_dst[i] + stage)
+                         : "memory");
+        }
     };
     auto dma_tile = [&](int j, int P) {
 #pragma unroll
@@ -217,16 +330,25 @@ __device__ __forceinline__ void fwd_item(
     // field holds 16 bits: the V stages need a second base for stages 2 and 3). The bases
     // go through an empty asm so that the compiler keeps them opaque rather than
     // re-associating the offsets into per-read additions.
-    lds_cptr base_k = lds + kappa(l32) * T::kKRow + hh * 16;
+    // (paged: row r of a K stage sits in page block r / 16 at row r % 16; kappa keeps bit 4,
+    // and the stages need a second base as the V stages do)
+    lds_cptr base_k = kPaged ? lds + (l32 >> 4) * T::kKPage + (kappa(l32) & 15) * T::kKRow + hh * 16
+                             : lds + kappa(l32) * T::kKRow + hh * 16;
+    lds_cptr base_k2 = base_k + 2 * T::kKStage;
     lds_cptr base_v = lds + T::kVBase + (8 * (lane >> 5) + ((lane & 15) >> 2)) * T::kVRow +
                       (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
     lds_cptr base_v2 = base_v + 2 * T::kVStage;
+    if constexpr (kPaged) asm volatile("" : "+v"(base_k2));
     asm volatile("" : "+v"(base_k), "+v"(base_v), "+v"(base_v2));
-    static_assert(3 * T::kKStage + 32 * T::kKRow + 2 * D < 65536, "K offsets fit the immediate");
+    static_assert(kPaged || 3 * T::kKStage + 32 * T::kKRow + 2 * D < 65536, "K offsets fit the immediate");
+    static_assert(!kPaged || T::kKStage + 2 * T::kKPage + 2 * D < 65536, "K offsets fit the immediate");
     static_assert(T::kVStage + 32 * T::kVRow + 20 * T::kVRow + 2 * D < 65536,
                   "V offsets fit the immediate");
     // K rows of half kb of stage st; V rows of half kb of stage st.
-    auto k_at = [&](int st, int kb) { return base_k + st * T::kKStage + 32 * kb * T::kKRow; };
+    auto k_at = [&](int st, int kb) {
+        if constexpr (kPaged) return (st < 2 ? base_k : base_k2) + (st & 1) * T::kKStage + 2 * kb * T::kKPage;
+        else return base_k + st * T::kKStage + 32 * kb * T::kKRow;
+    };
     auto v_at = [&](int st, int kb) {
         return (st < 2 ? base_v : base_v2) + (st & 1) * T::kVStage + 32 * kb * T::kVRow;
     };
@@ -319,7 +441,7 @@ __device__ __forceinline__ void fwd_item(
             const int kv0 = 32 * hi;
             // key of register r is kv0 + 16 (r >> 3) + 8 hh + (r & 7); masked: key > qrow
             // (causal) or key >= N, i.e. c > lim
-            const int lim = (causal ? min_(qrow, N - 1) : N - 1) - kv0 - 8 * hh;
+            const int lim = (causal ? min_(qrow + off, Nk - 1) : Nk - 1) - kv0 - 8 * hh;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int c = 16 * (r >> 3) + (r & 7);
@@ -404,7 +526,7 @@ __device__ __forceinline__ void fwd_item(
     // Tiles before n_plain need no mask in any wave of the workgroup: all their keys precede
     // the workgroup's first query row (causal) and the end of the sequence. The others mask
     // in every wave (a no-op where nothing is masked), behind a uniform branch.
-    const int n_plain = min_(n_tiles, causal ? (qb * kBr) / kBc : N / kBc);
+    const int n_plain = min_(n_tiles, causal ? max_(0, qb * kBr + off + 1) / kBc : Nk / kBc);
 
     f32x16 sa, sb;
     u32x4 pa[2], pb[2];
@@ -413,9 +535,16 @@ __device__ __forceinline__ void fwd_item(
     using Yes = std::true_type;
     using No = std::false_type;
 
+    // (paged: an item none of whose rows sees a key skips to the epilogue)
+    if (!kPaged || n_tiles > 0) {
+    if constexpr (kPaged) win = table_window(0);
+
     // ---- prologue: K0..K2 and V0, V1 staged; scores of half tile 0 ----
+    advance(0);
     dma_tile(-3, 1);  // K0 (and zeros for V of tile -1, in the stage V3 takes later)
+    advance(1);
     dma_tile(-2, 2);  // K1, V0
+    advance(2);
     dma_tile(-1, 3);  // K2, V1
     wait_dma_all();
     barrier_lds();
@@ -427,6 +556,7 @@ __device__ __forceinline__ void fwd_item(
 #pragma unroll
         for (int sl = 0; sl < kAhead; ++sl) fr[sl] = (sl & 1) ? bf16x8{} : frag(b0, sl);
     }
+    advance(3);
     step(0, std::integral_constant<int, 0>{}, sa, sb, pb, pa, n_plain == 0, fr, No{}, Yes{});
     step(1, std::integral_constant<int, 1>{}, sb, sa, pa, pb, n_plain == 0, fr, Yes{}, No{});
     wait_dma_tile();
@@ -441,6 +571,7 @@ __device__ __forceinline__ void fwd_item(
     auto tile = [&](int j, auto phase_c) {
         constexpr int P = decltype(phase_c)::value;
         const bool masked = j >= n_plain;
+        advance(j + 3);
         step(2 * j, std::integral_constant<int, 2 * P>{}, sa, sb, pb, pa, masked, fr, Yes{}, Yes{});
         step(2 * j + 1, std::integral_constant<int, 2 * P + 1>{}, sb, sa, pa, pb, masked, fr, Yes{}, No{});
         wait_dma_tile();
@@ -466,9 +597,19 @@ __device__ __forceinline__ void fwd_item(
     }
     wait_dma_all();  // no load may still be writing LDS when the item ends
     barrier_lds();   // and no wave still reads it when the next item's loads start
+    }
 
     // ---- epilogue: O / l, bf16, optional row statistics ----
-    const float l_tot = pair32_sum(l_part);
+    float l_tot = pair32_sum(l_part);
+    if constexpr (kPaged) {
+        // a query before the sequence's first key (causal, L < Nq) or an empty sequence:
+        // O = 0, m = -inf, l = 0 (its lanes ran on scores that were all masked)
+        if (Nk <= 0 || (causal && qrow + off < 0)) {
+            l_tot = 0.f;
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) acc_o[i] = f32x16{};
+        }
+    }
     if (qrow < N) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         uint16_t* dst = o + qoff + (size_t)qrow * D;
@@ -496,24 +637,37 @@ __device__ __forceinline__ void fwd_item(
 // r * W + j (r even) or r * W + W - 1 - j (r odd). The list runs heaviest query block first,
 // so the snake pairs heavy with light items and the workgroups finish together; and a
 // workgroup moves to its next item without a new launch.
-template <int D>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ m_out, float* __restrict__ l_out, int B, int Hq,
-    int Hkv, int N, float scale_log2, int causal, int nqb) {
+template <int D, bool kPaged>
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16)))
-    unsigned char smem[kStages * (Tile<D>::kKStage + Tile<D>::kVStage)];
-    const int total = B * Hq * nqb;
-    const int per_xcd = (total + kXcds - 1) / kXcds;
+    unsigned char smem[kStages * (Tile<D, kPaged>::kKStage + Tile<D, kPaged>::kVStage)];
+    const int per_unit = a.nqb * (a.Hq / a.Hkv);  // items of one KV group
+    const int n_kvg = a.B * a.Hkv;
+    const int total = n_kvg * per_unit;
     const int xcd = (int)(blockIdx.x % kXcds), j = (int)(blockIdx.x / kXcds);
     const int W = (int)(gridDim.x / kXcds);
-    const int seg0 = xcd * per_xcd;
-    const int seg_n = min_(per_xcd, total - seg0);
+    // Dense: XCD x takes the x-th contiguous eighth of the list. Paged: XCD x takes the KV
+    // groups g = x, x + 8, ..., so every XCD gets a share of every sequence whatever the
+    // sequences' lengths (a KV group's items still stay on one XCD).
+    int seg0 = 0, seg_n;
+    if constexpr (kPaged) {
+        seg_n = (n_kvg > xcd ? (n_kvg - xcd + kXcds - 1) / kXcds : 0) * per_unit;
+    } else {
+        const int per_xcd = (total + kXcds - 1) / kXcds;
+        seg0 = xcd * per_xcd;
+        seg_n = min_(per_xcd, total - seg0);
+    }
     for (int r = 0; r * W < seg_n; ++r) {
         const int local = r * W + ((r & 1) ? W - 1 - j : j);
         if (local >= seg_n) continue;
-        fwd_item<D>(q, k, v, o, m_out, l_out, B, Hq, Hkv, N, scale_log2, causal, nqb,
-                    seg0 + local, smem);
+        int item;
+        if constexpr (kPaged) {
+            const int g = local / per_unit;
+            item = (xcd + kXcds * g) * per_unit + (local - g * per_unit);
+        } else {
+            item = seg0 + local;
+        }
+        fwd_item<D, kPaged>(a, item, smem);
     }
 }
 
@@ -533,26 +687,61 @@ int persistent_cus() {
     return cached[dev];
 }
 
-hipError_t launch_fwd_bf16_sp(const void* q, const void* k, const void* v, void* o, float* m_out,
-                              float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
-                              int causal, hipStream_t stream) {
-    const int nqb = (N + kBr - 1) / kBr;
-    const long long items = (long long)nqb * B * Hq;
+namespace {
+template <bool kPaged>
+hipError_t launch_sp(const FwdArgs& a, int d, hipStream_t stream) {
+    const long long items = (long long)a.nqb * a.B * a.Hq;
     const long long slots = (long long)(persistent_cus() / kXcds) * kXcds;
     long long grid = (items + kXcds - 1) / kXcds * kXcds;
     if (grid > slots) grid = slots;
-    const float sl2 = scale * kLog2e;
-    auto qp = static_cast<const uint16_t*>(q);
-    auto kp = static_cast<const uint16_t*>(k);
-    auto vp = static_cast<const uint16_t*>(v);
-    auto op = static_cast<uint16_t*>(o);
     if (d == 128)
-        hipLaunchKernelGGL(fwd_bf16_sp_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                           qp, kp, vp, op, m_out, l_out, B, Hq, Hkv, N, sl2, causal, nqb);
+        hipLaunchKernelGGL((fwd_bf16_sp_kernel<128, kPaged>), dim3((unsigned)grid), dim3(kThreads), 0,
+                           stream, a);
     else
-        hipLaunchKernelGGL(fwd_bf16_sp_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                           qp, kp, vp, op, m_out, l_out, B, Hq, Hkv, N, sl2, causal, nqb);
+        hipLaunchKernelGGL((fwd_bf16_sp_kernel<64, kPaged>), dim3((unsigned)grid), dim3(kThreads), 0,
+                           stream, a);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_fwd_bf16_sp(const void* q, const void* k, const void* v, void* o, float* m_out,
+                              float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
+                              int causal, hipStream_t stream) {
+    FwdArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.o = static_cast<uint16_t*>(o);
+    a.m_out = m_out;
+    a.l_out = l_out;
+    a.B = B, a.Hq = Hq, a.Hkv = Hkv, a.N = N;
+    a.scale_log2 = scale * kLog2e;
+    a.causal = causal;
+    a.nqb = (N + kBr - 1) / kBr;
+    return launch_sp<false>(a, d, stream);
+}
+
+hipError_t launch_fwd_bf16_sp_paged(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens, void* o,
+                                    float* m_out, float* l_out, int B, int Hq, int Hkv, int Nq,
+                                    int d, int num_pages, int max_pages_per_seq, float scale,
+                                    int causal, hipStream_t stream) {
+    FwdArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k_cache);
+    a.v = static_cast<const uint16_t*>(v_cache);
+    a.o = static_cast<uint16_t*>(o);
+    a.m_out = m_out;
+    a.l_out = l_out;
+    a.table = block_table;
+    a.lens = seq_lens;
+    a.B = B, a.Hq = Hq, a.Hkv = Hkv, a.N = Nq;
+    a.scale_log2 = scale * kLog2e;
+    a.causal = causal;
+    a.nqb = (Nq + kBr - 1) / kBr;
+    a.max_pages = max_pages_per_seq;
+    a.num_pages = num_pages;
+    return launch_sp<true>(a, d, stream);
 }
 
 }  // namespace fa

@@ -158,13 +158,11 @@ class DecodeInputs:
         return int(2 * int(self.lens.sum()) * hkv * d * elem_bytes)
 
 
-def decode_inputs(B, Hq, Hkv, d, page_size, seed, lens=None, len_min=None, len_max=None,
-                  max_pages_per_seq=None, scale=None, unused_fill=np.nan):
-    rng = np.random.default_rng(seed)
-    if lens is None:
-        lens = rng.integers(len_min, len_max + 1, size=B)
-    lens = np.asarray(lens, dtype=np.int32)
-    q = round_to_bf16(rng.standard_normal((B, Hq, d), dtype=np.float32))
+def _paged_cache(rng, lens, Hkv, d, page_size, max_pages_per_seq, unused_fill):
+    """Draw each sequence's logical K_b and V_b, then scatter their 16-token pages to the
+    physical slots of one seeded permutation. Returns (k_seqs, v_seqs, k_cache, v_cache,
+    block_table)."""
+    B = len(lens)
     k_seqs, v_seqs = [], []
     for b in range(B):
         k_seqs.append(round_to_bf16(rng.standard_normal((Hkv, int(lens[b]), d), dtype=np.float32)))
@@ -188,6 +186,18 @@ def decode_inputs(B, Hq, Hkv, d, page_size, seed, lens=None, len_min=None, len_m
             padded[:, :L] = seq
             cache[phys] = padded.reshape(Hkv, npg, page_size, d).transpose(1, 0, 2, 3)
         offset += npg
+    return k_seqs, v_seqs, k_cache, v_cache, block_table
+
+
+def decode_inputs(B, Hq, Hkv, d, page_size, seed, lens=None, len_min=None, len_max=None,
+                  max_pages_per_seq=None, scale=None, unused_fill=np.nan):
+    rng = np.random.default_rng(seed)
+    if lens is None:
+        lens = rng.integers(len_min, len_max + 1, size=B)
+    lens = np.asarray(lens, dtype=np.int32)
+    q = round_to_bf16(rng.standard_normal((B, Hq, d), dtype=np.float32))
+    k_seqs, v_seqs, k_cache, v_cache, block_table = _paged_cache(
+        rng, lens, Hkv, d, page_size, max_pages_per_seq, unused_fill)
     return DecodeInputs(lens, q, k_seqs, v_seqs, k_cache, v_cache, block_table, page_size,
                         1.0 / math.sqrt(d) if scale is None else scale)
 
@@ -197,6 +207,87 @@ def config_decode_inputs(cfg: DecodeConfig) -> DecodeInputs:
     width = -(-cfg.len_max // cfg.page_size)
     return decode_inputs(cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.page_size, cfg.seed, lens=lens,
                          len_min=cfg.len_min, len_max=cfg.len_max, max_pages_per_seq=width)
+
+
+@dataclass(frozen=True)
+class PrefillPagedConfig:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    d: int
+    page_size: int
+    len_min: int
+    len_max: int
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+@dataclass
+class PrefillPagedInputs:
+    lens: np.ndarray  # [B] int32: cached tokens of each sequence, the Nq new ones included
+    q: np.ndarray  # [B, Hq, Nq, d] float32, bf16-exact: the newest Nq tokens of each sequence
+    k_seqs: list  # per sequence [Hkv, L_b, d] (logical cache)
+    v_seqs: list
+    k_cache: np.ndarray  # [num_pages, Hkv, page_size, d]; unused slots hold NaN
+    v_cache: np.ndarray
+    block_table: np.ndarray  # [B, max_pages_per_seq] int32; unused entries are -1
+    page_size: int
+    scale: float
+    causal: bool
+
+    @property
+    def num_pages(self) -> int:
+        return self.k_cache.shape[0]
+
+    def pairs(self) -> int:
+        """Admissible (query, key) pairs per query head."""
+        nq = self.q.shape[2]
+        total = 0
+        for L in self.lens.tolist():
+            pos = np.arange(L - nq, L)
+            total += int(np.clip(pos + 1, 0, L).sum()) if self.causal else nq * L
+        return total
+
+    def flops(self) -> float:
+        return 4.0 * self.q.shape[3] * self.pairs() * self.q.shape[1]
+
+
+def prefill_paged_inputs(B, Hq, Hkv, Nq, d, page_size, seed, lens=None, len_min=None,
+                         len_max=None, max_pages_per_seq=None, scale=None, causal=True,
+                         unused_fill=np.nan):
+    """Chunked prefill over a paged cache: each sequence's newest Nq tokens (q) against its
+    L_b cached tokens. Draw order: lengths, q, then K_b and V_b per sequence, then the page
+    permutation (as for decode)."""
+    rng = np.random.default_rng(seed)
+    if lens is None:
+        lens = rng.integers(len_min, len_max + 1, size=B)
+    lens = np.asarray(lens, dtype=np.int32)
+    q = round_to_bf16(rng.standard_normal((B, Hq, Nq, d), dtype=np.float32))
+    k_seqs, v_seqs, k_cache, v_cache, block_table = _paged_cache(
+        rng, lens, Hkv, d, page_size, max_pages_per_seq, unused_fill)
+    return PrefillPagedInputs(lens, q, k_seqs, v_seqs, k_cache, v_cache, block_table, page_size,
+                              1.0 / math.sqrt(d) if scale is None else scale, causal)
+
+
+# Chunked prefill over the paged cache (not one of the five workloads above): 4 sequences of
+# 4096 to 16384 cached tokens (inclusive) whose newest 2048 are the queries, 32 query heads
+# over 8 KV heads, d = 128, causal with the diagonal at the bottom right, seed 6.
+PREFILL_PAGED = PrefillPagedConfig(
+    "paged chunked prefill bf16 B=4 Hq=32 Hkv=8 Nq=2048 d=128 L~U[4096,16384] page=16",
+    4, 32, 8, 2048, 128, 16, 4096, 16384, True, 6)
+
+
+def config_prefill_paged_inputs(cfg: PrefillPagedConfig) -> PrefillPagedInputs:
+    width = -(-cfg.len_max // cfg.page_size)
+    return prefill_paged_inputs(cfg.B, cfg.Hq, cfg.Hkv, cfg.Nq, cfg.d, cfg.page_size, cfg.seed,
+                                len_min=cfg.len_min, len_max=cfg.len_max,
+                                max_pages_per_seq=width, causal=cfg.causal)
 
 
 def to_torch(x: np.ndarray, dtype: str, device="cuda"):

@@ -14,6 +14,11 @@
  *                     the FlashAttention-family table (Flash-Decoding, paged variants).
  *   fa_merge          merge of partial (m, l, O) results over disjoint key sets with the
  *                     online-softmax rescale; "FlashAttention", "Decode is a different problem".
+ *   fa_fwd_paged      tiled forward for the newest tokens of each sequence against its whole
+ *                     paged KV cache (chunked prefill); the paged variants of the
+ *                     FlashAttention-family table ("FlashAttention") with the update rule of
+ *                     "The trick: tiles and an online softmax". A shared prefix is handled by
+ *                     two calls (prefix unmasked, the rest causal) and fa_merge.
  *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library allocates
@@ -106,6 +111,37 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int d, int page_size, int max_se
 
 /* The number of KV chunks the automatic plan gives the longest sequence (0 if invalid). */
 int fa_decode_plan_splits(int B, int Hkv, int page_size, int max_seq_len);
+
+/*
+ * fa_fwd_paged - tiled forward of each sequence's newest Nq tokens against its paged cache.
+ *
+ *   q, o        : [B, Hq, Nq, d] bf16; query i of sequence b is the token at position
+ *                 seq_lens[b] - Nq + i (the chunk's own K/V are already in the cache)
+ *   k_cache,
+ *   v_cache     : [num_pages, Hkv, 16, d] bf16; token t of sequence b lives in physical page
+ *                 block_table[b][t / 16], slot t % 16; query head h reads KV head h / (Hq / Hkv)
+ *   block_table : int32 [B, max_pages_per_seq], device memory
+ *   seq_lens    : int32 [B], device memory: cached tokens of each sequence, chunk included
+ *   m_out, l_out: optional float32 [B, Hq, Nq] row statistics (NULL = not written)
+ *
+ * causal != 0 admits key j for query i iff j <= seq_lens[b] - Nq + i (the diagonal aligned to
+ * the bottom right); causal == 0 admits every j < seq_lens[b]. A query that admits no key
+ * (seq_lens[b] < Nq, causal, or seq_lens[b] == 0) yields O = 0, m = -inf, l = 0. `scale`
+ * must be finite and > 0. bf16 inputs, float32 accumulation and softmax, bf16 output.
+ *
+ * Caller preconditions that are not checked on the device: block_table[b][p] in
+ * [0, num_pages) for p < ceil(seq_lens[b] / 16). Each length is clamped to
+ * [0, max_pages_per_seq * 16]; a table entry outside [0, num_pages) is never dereferenced
+ * (its page reads as zeros), so a violated precondition gives a wrong result, never an
+ * out-of-bounds access. Entries past a sequence's last page are not used.
+ * Supported: dt = FA_BF16; d in {64, 128}; page_size = 16; Hq % Hkv == 0 (else
+ * FA_ERR_INVALID_ARGUMENT); Nq * d < 2^31. B, Hq or Nq equal to 0 is a valid empty call.
+ */
+fa_status fa_fwd_paged(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, const int32_t* seq_lens, void* o,
+                       float* m_out, float* l_out, int B, int Hq, int Hkv, int Nq, int d,
+                       int page_size, int num_pages, int max_pages_per_seq, float scale,
+                       int causal, void* stream);
 
 /*
  * fa_merge - merge S partial results over disjoint key sets, row by row.

@@ -1,4 +1,4 @@
-"""Plain float64 CPU oracle for exact attention, paged decode and partial merge.
+"""Plain float64 CPU oracle for exact attention, paged prefill and decode, and partial merge.
 
 This package is TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and
 the ``cpu_baseline`` leg of ``bench.py`` may import it. The product (the HIP library in
@@ -19,4 +19,5 @@ from .attention import (  # noqa: F401
     decode,
     merge,
     online_softmax,
+    prefill_paged,
 )

@@ -8,6 +8,8 @@ Sources, cited by page title and section:
   new tile of scores s with values v, and the final division O / l.
 * same page, "Decode is a different problem": one query row per sequence against its whole
   K/V cache; partial (m, l, O) results of KV chunks are merged with the same rule.
+* same page, "The FlashAttention family" table (the paged variants, which read K/V through
+  a block table): the newest tokens of a sequence attend to its whole cached history.
 * "FlashAttention, explained." (vibeengines.com), the worked example of the rescaling
   trick, and the forward-pass statement (Q, K, V are N x d per head, 1/sqrt(d) scale and
   masking fused, the statistics m and l are kept alongside O).
@@ -144,6 +146,46 @@ def decode(q, k_seqs, v_seqs, scale):
                 q[b, h][None, :], kb[h // group], vb[h // group], scale, causal=False)
             out[b, h], m[b, h], l[b, h] = o_bh[0], m_bh[0], l_bh[0]
     return out, m, l
+
+
+def prefill_paged(q, k_seqs, v_seqs, scale, causal, row_block=256):
+    """Attention of each sequence's newest Nq query rows against its whole (logical) K/V.
+
+    q: [B, Hq, Nq, d]; k_seqs[b], v_seqs[b]: [Hkv, L_b, d]. The Nq queries of sequence b are
+    its last Nq tokens: query i sits at position pos_i = L_b - Nq + i, so the causal mask
+    admits key j iff j <= pos_i (the diagonal aligned to the bottom right of the L_b x Nq
+    score block); without the mask every j < L_b is admissible. A query with no admissible
+    key (pos_i < 0 when Nq > L_b, or L_b = 0) has O = 0, m = -inf, l = 0. S and P are
+    materialised in full-width blocks of ``row_block`` rows over all L_b keys.
+
+    Returns O [B, Hq, Nq, d], m [B, Hq, Nq], l [B, Hq, Nq], float64.
+    """
+    q = _f64(q)
+    b_, hq, nq, d = q.shape
+    out = np.zeros((b_, hq, nq, d))
+    m_out = np.full((b_, hq, nq), -np.inf)
+    l_out = np.zeros((b_, hq, nq))
+    for b in range(b_):
+        kb = _f64(k_seqs[b])
+        vb = _f64(v_seqs[b])
+        n_keys = kb.shape[1]
+        group = hq // kb.shape[0]
+        pos = n_keys - nq + np.arange(nq)
+        for h in range(hq):
+            for r0 in range(0, nq, row_block):
+                rows = slice(r0, min(nq, r0 + row_block))
+                s = scale * (q[b, h, rows] @ kb[h // group].T)
+                if causal:
+                    allowed = np.arange(n_keys)[None, :] <= pos[rows, None]
+                else:
+                    allowed = np.ones(s.shape, dtype=bool)
+                p, m, l = _softmax_stats(s, allowed)
+                safe_l = np.where(l > 0, l, 1.0)
+                num = p @ vb[h // group]
+                out[b, h, rows] = np.where(l[:, None] > 0, num / safe_l[:, None], 0.0)
+                m_out[b, h, rows] = m
+                l_out[b, h, rows] = l
+    return out, m_out, l_out
 
 
 def merge(o_parts, m_parts, l_parts):

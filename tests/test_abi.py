@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_decode_splitk", "fa_merge", "fa_status_string",
-              "fa_decode_workspace_bytes", "fa_decode_plan_splits"):
+              "fa_decode_workspace_bytes", "fa_decode_plan_splits", "fa_fwd_paged"):
         assert n in names
 
 
@@ -132,6 +132,38 @@ def test_decode_workspace_and_plan():
     lib = fa.load_library()
     exact = fa.fa_decode_workspace_bytes(2, 8, 128, 16, 80, 3)
     assert decode(lib, splits=3, ws_bytes=exact - 1) == fa.FA_ERR_WORKSPACE_TOO_SMALL
+
+
+def paged(lib, dt=1, q=DEV, kc=DEV, vc=DEV, table=DEV, lens=DEV, o=DEV, B=2, Hq=8, Hkv=2, Nq=64,
+          d=128, page=16, num_pages=10, max_pages=8, scale=0.1, causal=1):
+    return lib.fa_fwd_paged(dt, q, kc, vc, table, lens, o, None, None, B, Hq, Hkv, Nq, d, page,
+                            num_pages, max_pages, scale, causal, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(dt=7), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(dt=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(page=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(page=0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(Hq=7, Hkv=2), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(Hkv=0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(B=-1), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(Nq=-1), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(num_pages=-1), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(max_pages=-1), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(table=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(lens=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(q=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(kc=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(o=MIS), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(max_pages=1 << 28), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nq=0, q=NULL, o=NULL), fa.FA_OK),
+    (dict(B=0, q=NULL, o=NULL), fa.FA_OK),
+])
+def test_fwd_paged_validation(kwargs, code):
+    assert paged(fa.load_library(), **kwargs) == code
 
 
 def merge(lib, dt=0, op=DEV, mp=DEV, lp=DEV, o=DEV, S=4, R=8, d=128):
