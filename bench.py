@@ -120,7 +120,8 @@ def summarize(paths, kernel=None):
 
 # Kernels whose HBM traffic is reported, with the source file each is compiled from.
 TRAFFIC_KERNELS = {
-    "fwd": ("fwd_bf16_sp_kernel", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
+    "fwd": ("fwd_bf16_sp_kernel<128, false>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
+    "paged": ("fwd_bf16_sp_kernel<128, true>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
     "decode": ("decode_mx_kernel", "exact_tiled_attention_24_amd/csrc/decode_mx.hip"),
 }
 COPY_KERNEL = "copyBuffer"
@@ -362,7 +363,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4) if fwd_tflops else None,
             "traffic": traffic.get("fwd"),
-            "kernel": "fwd_bf16_sp_kernel<128>",
+            "kernel": "fwd_bf16_sp_kernel<128, false>",
             "avg_launch_ms": round(float(fwd_ms.mean()), 5) if do_fwd else None,
         },
         "decode": {
@@ -390,7 +391,8 @@ def main():
             "avg_call_ms": round(float(paged_ms.mean()), 5),
             "tokens_per_s": round(pcfg.B * pcfg.Nq / (paged_ms.mean() * 1e-3), 1),
             "roofline": {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4)},
+                         "unit": "TFLOP/s", "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic.get("paged"), "kernel": "fwd_bf16_sp_kernel<128, true>"},
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(fx, fcfg, args.cpu_heads)

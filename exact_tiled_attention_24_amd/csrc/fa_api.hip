@@ -194,6 +194,8 @@ fa_status fa_fwd_paged(fa_dtype dt, const void* q, const void* k_cache, const vo
     if ((long long)Nq * d >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
     if (((long long)Nq + 255) / 256 * B * Hq >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
     if ((long long)max_pages_per_seq * page_size >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    // the kernel addresses each cache with 32-bit byte offsets below 2^31
+    if ((long long)num_pages * Hkv * page_size * d * 2 >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
     const hipError_t e = fa::launch_fwd_bf16_sp_paged(
         q, k_cache, v_cache, block_table, seq_lens, o, m_out, l_out, B, Hq, Hkv, Nq, d, num_pages,
         max_pages_per_seq, scale, causal ? 1 : 0, static_cast<hipStream_t>(stream));

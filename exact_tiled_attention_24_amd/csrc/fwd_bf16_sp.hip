@@ -46,9 +46,11 @@
 // query i sits at position L - Nq + i of its L cached tokens and the causal diagonal is
 // aligned to the bottom right. K/V of token t come from physical page
 // block_table[b][t / 16], slot t % 16. Each 16-row page of a K stage starts at a 1 KiB
-// boundary in LDS (V pages are whole KiB already), so every 1 KiB load lies in one page
-// and takes a scalar descriptor for that page, whose range ends at the sequence end (rows
-// past it fill with zeros). Block-table entries are scalar loads issued one tile ahead.
+// boundary in LDS (V pages are whole KiB already), so every 1 KiB load lies in one page and
+// its lanes add one wave-uniform page offset to fixed per-lane offsets. Pages past the
+// sequence end, rows past it in the last page and invalid table entries read as zeros
+// through the descriptor's range. Block-table entries come from a per-lane window of 64
+// read back with v_readlane.
 #include <type_traits>
 
 #include "fa_internal.hpp"
@@ -232,44 +234,56 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
             dma_pg[i] = 0;
         }
     }
-    // Paged: block-table entries of the K tile being loaded (ek, pages 4t .. 4t + 3) and of
-    // the V tile (ev, one tile behind: the K entries of the previous tile). They come from
-    // a window of 64 entries held one per lane (pages w0 .. w0 + 63) and read back with
-    // v_readlane; the next window is loaded one tile before it is needed. Entries of pages
-    // past the sequence are never used (their loads get an empty range).
-    int ek0 = -1, ek1 = -1, ek2 = -1, ek3 = -1, ev0 = -1, ev1 = -1, ev2 = -1, ev3 = -1;
-    int w0 = 0, win = -1, win_next = -1;
+    // Paged: byte offset (from this KV head's block in physical page 0) of every page of a
+    // window of 64 pages, one per lane: lane l holds page wb + l, or kPagePad where the page
+    // holds no row of the sequence or its table entry lies outside [0, num_pages), which puts
+    // every lane of its loads past the descriptor's range (zeros). A load picks its page's
+    // offset with one v_readlane. The window moves by 60 pages, so the V tile (one behind the
+    // K tile) always lies in it too; the next window's table entries are loaded one tile
+    // before they are needed. Rows of the last page past the sequence end are cut per lane
+    // in the V loads (K rows there only meet masked scores).
+    constexpr unsigned kPagePad = 0x80000000u;
+    const int p_last = (Nk - 1) / kPageTok;                          // last page holding a row
+    const int last_bytes = (Nk - kPageTok * p_last) * D * 2;         // its rows, in bytes
+    const unsigned stride_bytes = (unsigned)Hkv * kPageTok * D * 2;  // one physical page
     const int32_t* trow = nullptr;
     if constexpr (kPaged) trow = a.table + (size_t)b * a.max_pages;
-    auto table_window = [&](int first) {  // entries first + lane (clamped into the row)
-        return trow[min_(first + lane, a.max_pages - 1)];
+    int wb = -4, kidx = 0, vidx = 0;
+    int raw_next = -1;
+    unsigned win = kPagePad;
+    auto table_entries = [&](int first) {  // entry of page first + lane (clamped into the row)
+        return trow[min_(max_(first + lane, 0), a.max_pages - 1)];
     };
-    // Before the loads of K tile t (and V tile t - 1).
+    auto page_offsets = [&](int e, int first) {
+        const int p = first + lane;
+        return p >= 0 && p <= p_last && e >= 0 && e < a.num_pages ? (unsigned)e * stride_bytes
+                                                                 : kPagePad;
+    };
+    // Before the loads of K tile t and V tile t - 1.
     auto advance = [&](int t) {
         if constexpr (kPaged) {
-            if (4 * t >= w0 + 64) {
-                w0 += 64;
-                win = win_next;
+            if (4 * t + 3 >= wb + 64) {
+                wb = 4 * t - 4;
+                win = page_offsets(raw_next, wb);
             }
-            ev0 = ek0, ev1 = ek1, ev2 = ek2, ev3 = ek3;
-            const int wi = 4 * t - w0;
-            ek0 = __builtin_amdgcn_readlane(win, wi);
-            ek1 = __builtin_amdgcn_readlane(win, wi + 1);
-            ek2 = __builtin_amdgcn_readlane(win, wi + 2);
-            ek3 = __builtin_amdgcn_readlane(win, wi + 3);
-            if (4 * t + 4 == w0 + 64) win_next = table_window(w0 + 64);
+            if (4 * t + 7 >= wb + 64) raw_next = table_entries(4 * t);
+            kidx = 4 * t - wb;
+            vidx = kidx - 4;
         }
     };
-    const size_t page_stride = (size_t)Hkv * kPageTok * D;  // elements per physical page
-    const size_t kv_page = (size_t)kvh * kPageTok * D;       // this KV head within a page
     const int row_end = min_(Nk, n_tiles * kBc);
     // (readfirstlane: the clamp selects to a vector instruction, and a descriptor word in a
     // VGPR would force a per-lane loop around every buffer load)
-    const int head_bytes = __builtin_amdgcn_readfirstlane(row_end * D * 2);
+    // Dense: the head's rows up to the end of this item's last tile. Paged: the cache from
+    // this KV head's block of page 0 to the end of its block in the last page (under 2 GiB).
+    const int head_bytes = __builtin_amdgcn_readfirstlane(
+        kPaged ? (a.num_pages > 0 ? (a.num_pages - 1) * (int)stride_bytes + kPageTok * D * 2 : 0)
+               : row_end * D * 2);
+    const size_t kv_page = kPaged ? (size_t)kvh * kPageTok * D : 0;  // KV head within a page
     const __amdgpu_buffer_rsrc_t rsrc_k =
-        __builtin_amdgcn_make_buffer_rsrc((void*)kh, (short)0, head_bytes, kBufferDword3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kh + kv_page), (short)0, head_bytes, kBufferDword3);
     const __amdgpu_buffer_rsrc_t rsrc_v =
-        __builtin_amdgcn_make_buffer_rsrc((void*)vh, (short)0, head_bytes, kBufferDword3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vh + kv_page), (short)0, head_bytes, kBufferDword3);
     // DMA operation i of tile step j (stage phase P = j mod 4): K of tile j + 3 and V of
     // tile j + 2. Written as assembly: the compiler's own form makes it wait for every
     // outstanding load to LDS before each transposing read (it cannot tell the stages
@@ -282,23 +296,19 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
         const unsigned stage = is_k ? unsigned(((P + 3) & (kStages - 1)) * T::kKStage)
                                     : unsigned(((P + 2) & (kStages - 1)) * T::kVStage);
         if constexpr (kPaged) {
-            // page 4 t + pg of the sequence, t = j + 3 (K) or j + 2 (V): a descriptor over
-            // its rows that exist (none past the sequence end or for an invalid entry)
+            // page 4 t + pg of the sequence, t = j + 3 (K) or j + 2 (V)
             const int pg = dma_pg[i];
-            const int t = j + (is_k ? 3 : 2);
-            const int e0 = is_k ? ek0 : ev0, e1 = is_k ? ek1 : ev1;
-            const int e2 = is_k ? ek2 : ev2, e3 = is_k ? ek3 : ev3;
-            const int phys = pg == 0 ? e0 : (pg == 1 ? e1 : (pg == 2 ? e2 : e3));
-            const int rows = Nk - kPageTok * (4 * t + pg);
-            const bool ok = t >= 0 && rows > 0 && phys >= 0 && phys < a.num_pages;
-            const int bytes = __builtin_amdgcn_readfirstlane(ok ? min_(rows, kPageTok) * D * 2 : 0);
-            const int ph = __builtin_amdgcn_readfirstlane(ok ? phys : 0);
-            const uint16_t* src = (is_k ? k : v) + (size_t)ph * page_stride + kv_page;
-            const __amdgpu_buffer_rsrc_t r =
-                __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, bytes, kBufferDword3);
+            const unsigned po = __builtin_amdgcn_readlane(win, (is_k ? kidx : vidx) + pg);
+            unsigned src = (unsigned)dma_src[i] + po;
+            if (!all_k) {
+                const int page = 4 * (j + (is_k ? 3 : 2)) + pg;
+                const unsigned lim = !is_k && page == p_last ? (unsigned)last_bytes : 0xffffffffu;
+                src = (unsigned)dma_src[i] < lim ? src : kPagePad;
+            }
+            const __amdgpu_buffer_rsrc_t r = is_k ? rsrc_k : rsrc_v;
             asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                          :
-                         : "v"(dma_src[i]), "s"(r), "{m0}"(dma_dst[i] + stage)
+                         : "v"(src), "s"(r), "{m0}"(dma_dst[i] + stage)
                          : "memory");
         } else {
             const __amdgpu_buffer_rsrc_t r = is_k ? rsrc_k : rsrc_v;
@@ -537,7 +547,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
 
     // (paged: an item none of whose rows sees a key skips to the epilogue)
     if (!kPaged || n_tiles > 0) {
-    if constexpr (kPaged) win = table_window(0);
+    if constexpr (kPaged) win = page_offsets(table_entries(wb), wb);
 
     // ---- prologue: K0..K2 and V0, V1 staged; scores of half tile 0 ----
     advance(0);

@@ -135,7 +135,9 @@ int fa_decode_plan_splits(int B, int Hkv, int page_size, int max_seq_len);
  * (its page reads as zeros), so a violated precondition gives a wrong result, never an
  * out-of-bounds access. Entries past a sequence's last page are not used.
  * Supported: dt = FA_BF16; d in {64, 128}; page_size = 16; Hq % Hkv == 0 (else
- * FA_ERR_INVALID_ARGUMENT); Nq * d < 2^31. B, Hq or Nq equal to 0 is a valid empty call.
+ * FA_ERR_INVALID_ARGUMENT); Nq * d < 2^31; each cache under 2 GiB (num_pages * Hkv * 16 *
+ * d * 2 bytes < 2^31, about 1M tokens at Hkv = 8, d = 128), else FA_ERR_UNSUPPORTED.
+ * B, Hq or Nq equal to 0 is a valid empty call.
  */
 fa_status fa_fwd_paged(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_table, const int32_t* seq_lens, void* o,

@@ -159,6 +159,7 @@ def paged(lib, dt=1, q=DEV, kc=DEV, vc=DEV, table=DEV, lens=DEV, o=DEV, B=2, Hq=
     (dict(kc=NULL), fa.FA_ERR_INVALID_ARGUMENT),
     (dict(o=MIS), fa.FA_ERR_INVALID_ARGUMENT),
     (dict(max_pages=1 << 28), fa.FA_ERR_UNSUPPORTED),
+    (dict(num_pages=1 << 16, Hkv=8, Hq=8), fa.FA_ERR_UNSUPPORTED),   # a 2 GiB cache
     (dict(Nq=0, q=NULL, o=NULL), fa.FA_OK),
     (dict(B=0, q=NULL, o=NULL), fa.FA_OK),
 ])
