@@ -18,8 +18,13 @@ discuss; every value is drawn from N(0, 1) with numpy's PCG64 ``default_rng(seed
    16-token pages at randomly permuted physical slots named by an int32 block table,
    seed 5.
 
+Beyond these five: chunked prefill over the paged cache (``PREFILL_PAGED``): 4 sequences of
+4096 to 16384 cached tokens whose newest 2048 are the queries, 32 query heads over 8 KV
+heads, d=128, causal with the diagonal at the bottom right, pages laid out as for decode,
+seed 6.
+
 Draw order: Q, then K, then V (forward); lengths, q, then K_b and V_b per sequence, then
-the page permutation (decode). Values are rounded to bfloat16 with round-to-nearest-even
+the page permutation (decode and paged prefill). Values are rounded to bfloat16 with round-to-nearest-even
 before anyone sees them, so both sides receive identical, exactly representable inputs.
 """
 
