@@ -12,7 +12,8 @@ Sources, cited by page title and section:
   a block table): the newest tokens of a sequence attend to its whole cached history.
 * "FlashAttention, explained." (vibeengines.com), the worked example of the rescaling
   trick, and the forward-pass statement (Q, K, V are N x d per head, 1/sqrt(d) scale and
-  masking fused, the statistics m and l are kept alongside O).
+  masking fused, the statistics m and l are kept alongside O); its block-sparse section: a
+  block mask over (query block, key block) pairs removes whole blocks of scores.
 
 Conventions (readings of points the pages leave open):
 
@@ -182,6 +183,59 @@ def prefill_paged(q, k_seqs, v_seqs, scale, causal, row_block=256):
                 p, m, l = _softmax_stats(s, allowed)
                 safe_l = np.where(l > 0, l, 1.0)
                 num = p @ vb[h // group]
+                out[b, h, rows] = np.where(l[:, None] > 0, num / safe_l[:, None], 0.0)
+                m_out[b, h, rows] = m
+                l_out[b, h, rows] = l
+    return out, m_out, l_out
+
+
+def attention_block_sparse(q, k, v, scale, causal, block_offsets, block_indices, block_q,
+                           block_k, row_block=256):
+    """Exact attention restricted by a block mask.
+
+    q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]. Query i and key j of head (b, h) may attend iff
+    key block j // block_k is listed for query block i // block_q of that head and, when
+    ``causal``, j <= i. The lists are compressed rows: the key blocks of query block qb of
+    head (b, h) are block_indices[block_offsets[r] : block_offsets[r + 1]] with
+    r = (b * Hq + h) * ceil(N / block_q) + qb. Indices outside [0, ceil(N / block_k)) name no
+    key. Everything else is the definition: O = softmax(scale * q k^T + M) v with M = -inf
+    outside the admitted set; a row with no admissible key has O = 0, m = -inf, l = 0.
+    S and P are materialised in full-width blocks of ``row_block`` rows.
+
+    Returns O [B, Hq, N, d], m [B, Hq, N], l [B, Hq, N], float64.
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    b_, hq, n, d = q.shape
+    group = hq // k.shape[1]
+    nqb = -(-n // block_q)
+    nkb = -(-n // block_k)
+    offsets = np.asarray(block_offsets, dtype=np.int64)
+    indices = np.asarray(block_indices, dtype=np.int64)
+    out = np.zeros((b_, hq, n, d))
+    m_out = np.full((b_, hq, n), -np.inf)
+    l_out = np.zeros((b_, hq, n))
+    key_block = np.arange(n) // block_k
+    for b in range(b_):
+        for h in range(hq):
+            # admitted (query block, key block) pairs of this head
+            blocks = np.zeros((nqb, nkb), dtype=bool)
+            for qb in range(nqb):
+                r = (b * hq + h) * nqb + qb
+                sel = indices[offsets[r]:offsets[r + 1]]
+                sel = sel[(sel >= 0) & (sel < nkb)]
+                blocks[qb, sel] = True
+            kh = h // group
+            for r0 in range(0, n, row_block):
+                rows = np.arange(r0, min(n, r0 + row_block))
+                s = scale * (q[b, h, rows] @ k[b, kh].T)
+                allowed = blocks[rows // block_q][:, key_block]
+                if causal:
+                    allowed &= np.arange(n)[None, :] <= rows[:, None]
+                p, m, l = _softmax_stats(s, allowed)
+                safe_l = np.where(l > 0, l, 1.0)
+                num = p @ v[b, kh]
                 out[b, h, rows] = np.where(l[:, None] > 0, num / safe_l[:, None], 0.0)
                 m_out[b, h, rows] = m
                 l_out[b, h, rows] = l
