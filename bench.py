@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64,
                     help="heads of the forward workload the oracle is timed on")
-    ap.add_argument("--only", choices=["fwd", "decode", "paged"], default=None,
+    ap.add_argument("--only", choices=["fwd", "decode", "paged", "sparse"], default=None,
                     help="time one kernel only (profiling runs)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling)")
@@ -120,8 +120,8 @@ def summarize(paths, kernel=None):
 
 # Kernels whose HBM traffic is reported, with the source file each is compiled from.
 TRAFFIC_KERNELS = {
-    "fwd": ("fwd_bf16_sp_kernel<128, false>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
-    "paged": ("fwd_bf16_sp_kernel<128, true>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
+    "fwd": ("fwd_bf16_sp_kernel<128, 0>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
+    "paged": ("fwd_bf16_sp_kernel<128, 1>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
     "decode": ("decode_mx_kernel", "exact_tiled_attention_24_amd/csrc/decode_mx.hip"),
 }
 COPY_KERNEL = "copyBuffer"
@@ -214,6 +214,7 @@ def main():
     do_fwd = args.only in (None, "fwd")
     do_dec = args.only in (None, "decode")
     do_paged = args.only in (None, "paged")
+    do_sparse = args.only in (None, "sparse")
 
     # ---- inputs, resident in HBM ----
     fcfg = gen.CONFIGS[args.fwd_config]
@@ -265,6 +266,25 @@ def main():
         paged_scale = px.scale
         paged_lens = [int(L) for L in px.lens]
         del px
+
+    sparse_flops = None
+    if do_sparse:
+        scfg = gen.BLOCK_SPARSE
+        sx = gen.fwd_inputs(scfg.B, scfg.Hq, scfg.Hkv, scfg.N, scfg.d, scfg.seed, causal=scfg.causal)
+        s_rows = gen.local_global_blocks(scfg.B, scfg.Hq, scfg.N, scfg.window, scfg.n_global,
+                                         scfg.causal)
+        s_offs, s_idx = gen.block_csr(s_rows)
+        s_q, s_k, s_v = (gen.to_torch(t, "bf16", dev) for t in (sx.q, sx.k, sx.v))
+        s_o = torch.empty_like(s_q)
+        s_offs_t = torch.from_numpy(s_offs).to(dev)
+        s_idx_t = torch.from_numpy(s_idx).to(dev)
+        sparse_flops = 4.0 * scfg.d * gen.block_pairs(s_rows, scfg.B, scfg.Hq, scfg.N, scfg.causal)
+        sparse_blocks = int(s_idx.size)
+        del sx
+
+    def run_sparse():
+        fa.fa_fwd_block_sparse(s_q, s_k, s_v, s_offs_t, s_idx_t, scale=scfg.scale,
+                               causal=scfg.causal, out=s_o)
 
     def run_paged():
         fa.fa_fwd_paged(p_q, p_kc, p_vc, p_tab, p_lens, scale=paged_scale, causal=pcfg.causal,
@@ -327,6 +347,19 @@ def main():
         torch.cuda.synchronize()
         paged_ms = np.array([a.elapsed_time(b) for a, b in pev])
 
+    sparse_ms = None
+    if do_sparse:
+        for _ in range(args.warmup):
+            run_sparse()
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in sev:
+            a.record(stream)
+            run_sparse()
+            b.record(stream)
+        torch.cuda.synchronize()
+        sparse_ms = np.array([a.elapsed_time(b) for a, b in sev])
+
     fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     dec_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
 
@@ -363,7 +396,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4) if fwd_tflops else None,
             "traffic": traffic.get("fwd"),
-            "kernel": "fwd_bf16_sp_kernel<128, false>",
+            "kernel": "fwd_bf16_sp_kernel<128, 0>",
             "avg_launch_ms": round(float(fwd_ms.mean()), 5) if do_fwd else None,
         },
         "decode": {
@@ -392,7 +425,18 @@ def main():
             "tokens_per_s": round(pcfg.B * pcfg.Nq / (paged_ms.mean() * 1e-3), 1),
             "roofline": {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
-                         "traffic": traffic.get("paged"), "kernel": "fwd_bf16_sp_kernel<128, true>"},
+                         "traffic": traffic.get("paged"), "kernel": "fwd_bf16_sp_kernel<128, 1>"},
+        }
+    if do_sparse:
+        s_tflops = sparse_flops / (sparse_ms.mean() * 1e-3) / 1e12
+        result["block_sparse"] = {
+            "workload": scfg.name, "listed_blocks": sparse_blocks, "algorithmic_flops": sparse_flops,
+            "value": round(s_tflops, 2), "unit": "TFLOP/s",
+            "avg_call_ms": round(float(sparse_ms.mean()), 5),
+            "tokens_per_s": round(scfg.B * scfg.N / (sparse_ms.mean() * 1e-3), 1),
+            "roofline": {"bound": "mfma", "achieved": round(s_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(s_tflops / PEAK_BF16_TFLOPS, 4),
+                         "kernel": "fwd_bf16_sp_kernel<128, 2>"},
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(fx, fcfg, args.cpu_heads)

@@ -10,6 +10,7 @@ Entry points (same names as the C ABI):
     fa_fwd(q, k, v, scale=None, causal=False, out=None, return_stats=False)
     fa_decode_splitk(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, ...)
     fa_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=True, ...)
+    fa_fwd_block_sparse(q, k, v, block_offsets, block_indices, scale=None, causal=False, ...)
     fa_merge(o_parts, m_parts, l_parts, out_dtype=torch.float32, return_stats=False)
     fa_decode_workspace_bytes(...), fa_decode_plan_splits(...), fa_status_string(code)
 """
@@ -63,6 +64,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_paged.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                  i32, i32, i32, f32, i32, vp]
     lib.fa_fwd_paged.restype = i32
+    lib.fa_fwd_block_sparse.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                        i32, i32, f32, i32, vp]
+    lib.fa_fwd_block_sparse.restype = i32
     lib.fa_merge.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
     lib.fa_merge.restype = i32
     lib.fa_status_string.argtypes = [i32]
@@ -230,6 +234,49 @@ def fa_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=
             _ptr(seq_lens), _ptr(o), _ptr(m), _ptr(l), B, Hq, Hkv, Nq, d, page_size, num_pages,
             block_table.shape[1], scale, 1 if causal else 0, _stream(q.device))
     _check(code, "fa_fwd_paged")
+    return (o, m, l) if return_stats else o
+
+
+SPARSE_BLOCK_Q = 256
+SPARSE_BLOCK_K = 64
+
+
+def fa_fwd_block_sparse(q, k, v, block_offsets, block_indices, scale=None, causal=False,
+                        out=None, return_stats=False):
+    """Block-sparse forward: query block qb (256 rows) of head (b, h) attends only to the
+    64-key blocks block_indices[block_offsets[r]:block_offsets[r + 1]],
+    r = (b * Hq + h) * ceil(N / 256) + qb. q: [B, Hq, N, d]; k, v: [B, Hkv, N, d] (bf16);
+    block_offsets, block_indices: int32 on the GPU. Returns O, or (O, m, l) with
+    ``return_stats``.
+    """
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if block_offsets.dtype != torch.int32 or block_indices.dtype != torch.int32:
+        raise TypeError("block_offsets and block_indices must be int32")
+    nqb = -(-N // SPARSE_BLOCK_Q)
+    if block_offsets.dim() != 1 or block_offsets.numel() != B * Hq * nqb + 1:
+        raise ValueError("block_offsets must hold B * Hq * ceil(N / 256) + 1 entries")
+    Hkv = k.shape[1]
+    o = torch.empty_like(q) if out is None else out
+    m = l = None
+    if return_stats:
+        m = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+        l = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _require_gpu(q, k, v, o, block_offsets, block_indices, m, l)
+    if o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        code = lib.fa_fwd_block_sparse(
+            _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(m), _ptr(l),
+            _ptr(block_offsets), _ptr(block_indices), block_indices.numel(), B, Hq, Hkv, N, d,
+            scale, 1 if causal else 0, _stream(q.device))
+    _check(code, "fa_fwd_block_sparse")
     return (o, m, l) if return_stats else o
 
 

@@ -174,6 +174,28 @@ fa_status fa_decode_splitk(fa_dtype dt, const void* q, const void* k_cache, cons
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_fwd_block_sparse(fa_dtype dt, const void* q, const void* k, const void* v, void* o,
+                              float* m_out, float* l_out, const int32_t* block_offsets,
+                              const int32_t* block_indices, int nnz, int B, int Hq, int Hkv,
+                              int N, int d, float scale, int causal, void* stream) {
+    if (dt != FA_F32 && dt != FA_BF16) return FA_ERR_INVALID_ARGUMENT;
+    if (B < 0 || Hq < 0 || Hkv < 0 || N < 0 || nnz < 0) return FA_ERR_INVALID_ARGUMENT;
+    if (!scale_ok(scale)) return FA_ERR_INVALID_ARGUMENT;
+    if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0)) return FA_ERR_INVALID_ARGUMENT;
+    if (dt != FA_BF16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || Hq == 0 || N == 0) return FA_OK;
+    if (!q || !k || !v || !o || !block_offsets || (nnz > 0 && !block_indices))
+        return FA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return FA_ERR_INVALID_ARGUMENT;
+    if ((long long)N * d >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    if (((long long)N + 255) / 256 * B * Hq >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    const hipError_t e = fa::launch_fwd_bf16_sp_block_sparse(
+        q, k, v, o, m_out, l_out, block_offsets, block_indices, nnz, B, Hq, Hkv, N, d, scale,
+        causal ? 1 : 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_fwd_paged(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_table, const int32_t* seq_lens, void* o,
                        float* m_out, float* l_out, int B, int Hq, int Hkv, int Nq, int d,

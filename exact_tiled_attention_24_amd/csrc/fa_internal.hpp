@@ -30,6 +30,14 @@ hipError_t launch_fwd_bf16_sp_paged(const void* q, const void* k_cache, const vo
                                     int d, int num_pages, int max_pages_per_seq, float scale,
                                     int causal, hipStream_t stream);
 
+// Block-sparse forward with the same kernel: query block qb (256 rows) of head (b, h) visits
+// only the 64-key tiles blk_idx[blk_off[r] .. blk_off[r + 1]), r = (b * Hq + h) * nqb + qb.
+hipError_t launch_fwd_bf16_sp_block_sparse(const void* q, const void* k, const void* v, void* o,
+                                           float* m_out, float* l_out, const int32_t* block_offsets,
+                                           const int32_t* block_indices, int nnz, int B, int Hq,
+                                           int Hkv, int N, int d, float scale, int causal,
+                                           hipStream_t stream);
+
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* m_out,
                           float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
                           int causal, hipStream_t stream);

@@ -41,6 +41,12 @@
 //    and each workgroup walks items of its XCD's contiguous share of the list in snake
 //    order (see the kernel).
 //
+// Block-sparse variant (kSparse): the block-sparse forward of "FlashAttention, explained."
+// (vibeengines.com): each work item processes only the key tiles its block list names (64
+// keys per tile, 256 query rows per block), in list order; a per-lane window of the list's
+// tile offsets feeds the loads as in the paged variant, and a short delay line of the tiles'
+// first key positions drives the masking of diagonal, ragged and invalid tiles.
+//
 // Paged variant (kPaged): chunked prefill over a paged KV cache, the paged rows of the
 // family table on the same page. The queries are the newest Nq tokens of each sequence, so
 // query i sits at position L - Nq + i of its L cached tokens and the causal diagonal is
@@ -88,6 +94,7 @@ __device__ __forceinline__ void barrier_lds() {
 }
 
 constexpr int kPageTok = 16;      // tokens per page of the paged cache
+constexpr int kModeDense = 0, kModePaged = 1, kModeSparse = 2;
 
 template <int D, bool kPaged>
 struct Tile {
@@ -122,6 +129,9 @@ struct FwdArgs {
     float* l_out;
     const int32_t* table;
     const int32_t* lens;
+    const int32_t* blk_off;  // block-sparse: compressed rows of key-tile lists
+    const int32_t* blk_idx;
+    int nnz;                 // entries of blk_idx
     int B, Hq, Hkv, N;
     float scale_log2;
     int causal, nqb;
@@ -130,8 +140,9 @@ struct FwdArgs {
 
 // One work item: the 256-row query block and head that `item` names in the work list
 // (KV group, query block heaviest first, head in group). `smem` is the workgroup's LDS.
-template <int D, bool kPaged>
+template <int D, int kMode>
 __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned char* smem) {
+    constexpr bool kPaged = kMode == kModePaged, kSparse = kMode == kModeSparse;
     using T = Tile<D, kPaged>;
     const uint16_t* __restrict__ q = a.q;
     const uint16_t* __restrict__ k = a.k;
@@ -168,6 +179,16 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
         Nk = __builtin_amdgcn_readfirstlane(L < 0 ? 0 : min_(L, a.max_pages * kPageTok));
         off = Nk - N;
     }
+    // Block-sparse: this item's key tiles are blk_idx[list0 .. list0 + n_list) (clamped into
+    // the array, so no read leaves it whatever the offsets hold).
+    int list0 = 0, n_list = 0;
+    if constexpr (kSparse) {
+        const int r = (b * Hq + h) * nqb + qb;
+        const int e0 = min_(max_(a.blk_off[r], 0), a.nnz);
+        const int e1 = min_(max_(a.blk_off[r + 1], e0), a.nnz);
+        list0 = __builtin_amdgcn_readfirstlane(e0);
+        n_list = __builtin_amdgcn_readfirstlane(e1 - e0);
+    }
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -190,10 +211,12 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     f32x16 acc_o[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) acc_o[i] = f32x16{};
-    float m_run = -INFINITY, m_ref = -INFINITY, l_part = 0.f;
+    // (the exponent reference starts finite: a row whose first tiles are all masked then gets
+    // exp2(-inf) = 0 rather than exp2(-inf + inf), and moves to its first finite maximum)
+    float m_run = -INFINITY, m_ref = -1e30f, l_part = 0.f;
 
     const int kv_end = causal ? min_(Nk, qb * kBr + kBr + off) : Nk;
-    const int n_tiles = kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0;
+    const int n_tiles = kSparse ? n_list : (kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0);
 
     // ---- staging: buffer loads straight into LDS (no registers). A tile's K stage (64
     // padded rows) and V stage (64 padded rows, row-major) are cut into 1 KiB chunks; one
@@ -230,7 +253,8 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
         } else {
             const int slot = 1024 * cc + 16 * lane;
             const int row = slot / row_b, col = slot - row * row_b;
-            dma_src[i] = (col < D * 2 ? row * D * 2 + col : kPadOffset) + (is_k ? 3 : 2) * kBc * D * 2;
+            dma_src[i] = (col < D * 2 ? row * D * 2 + col : kPadOffset) +
+                         (kSparse ? 0 : (is_k ? 3 : 2) * kBc * D * 2);
             dma_pg[i] = 0;
         }
     }
@@ -248,9 +272,22 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     const unsigned stride_bytes = (unsigned)Hkv * kPageTok * D * 2;  // one physical page
     const int32_t* trow = nullptr;
     if constexpr (kPaged) trow = a.table + (size_t)b * a.max_pages;
-    int wb = -4, kidx = 0, vidx = 0;
+    // Block-sparse: the window holds the byte offsets of list positions wb .. wb + 63 (one
+    // tile each; kPagePad past the list or for an index outside the key tiles), and kvq0..3
+    // the first key position of tiles j .. j + 3 (1 << 30 for an invalid index: fully masked).
+    constexpr int kTileBytes = kBc * D * 2;
+    const int n_ktiles = (N + kBc - 1) / kBc;
+    int kvq0 = 0, kvq1 = 0, kvq2 = 0, kvq3 = 0;
+    int wb = kSparse ? -1 : -4, kidx = 0, vidx = 0;
     int raw_next = -1;
     unsigned win = kPagePad;
+    auto list_entries = [&](int first) {  // list entry of position first + lane (clamped)
+        return a.blk_idx[list0 + min_(max_(first + lane, 0), n_list - 1)];
+    };
+    auto tile_offsets = [&](int e, int first) {
+        const int pos = first + lane;
+        return pos >= 0 && pos < n_list && e >= 0 && e < n_ktiles ? (unsigned)e * kTileBytes : kPagePad;
+    };
     auto table_entries = [&](int first) {  // entry of page first + lane (clamped into the row)
         return trow[min_(max_(first + lane, 0), a.max_pages - 1)];
     };
@@ -261,6 +298,18 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     };
     // Before the loads of K tile t and V tile t - 1.
     auto advance = [&](int t) {
+        if constexpr (kSparse) {
+            if (t >= wb + 64) {
+                wb = t - 1;
+                win = tile_offsets(raw_next, wb);
+            }
+            if (t + 1 >= wb + 64) raw_next = list_entries(t);
+            kidx = t - wb;
+            vidx = kidx - 1;
+            const unsigned ot = __builtin_amdgcn_readlane(win, kidx);
+            kvq0 = kvq1, kvq1 = kvq2, kvq2 = kvq3;
+            kvq3 = ot >= kPagePad ? (1 << 30) : (int)(ot / kTileBytes) * kBc;
+        }
         if constexpr (kPaged) {
             if (4 * t + 3 >= wb + 64) {
                 wb = 4 * t - 4;
@@ -271,7 +320,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
             vidx = kidx - 4;
         }
     };
-    const int row_end = min_(Nk, n_tiles * kBc);
+    const int row_end = kSparse ? N : min_(Nk, n_tiles * kBc);
     // (readfirstlane: the clamp selects to a vector instruction, and a descriptor word in a
     // VGPR would force a per-lane loop around every buffer load)
     // Dense: the head's rows up to the end of this item's last tile. Paged: the cache from
@@ -309,6 +358,14 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
             asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                          :
                          : "v"(src), "s"(r), "{m0}"(dma_dst[i] + stage)
+                         : "memory");
+        } else if constexpr (kSparse) {
+            // list position j + 3 (K) or j + 2 (V)
+            const unsigned po = __builtin_amdgcn_readlane(win, is_k ? kidx : vidx);
+            const __amdgpu_buffer_rsrc_t r = is_k ? rsrc_k : rsrc_v;
+            asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :
+                         : "v"((unsigned)dma_src[i] + po), "s"(r), "{m0}"(dma_dst[i] + stage)
                          : "memory");
         } else {
             const __amdgpu_buffer_rsrc_t r = is_k ? rsrc_k : rsrc_v;
@@ -427,7 +484,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     // (with_pv false: half tile 0, whose step has no O update; its odd slots stay empty.)
     // with_dma: this step (the first of tile j = hi / 2) also issues the loads of K of tile
     // j + 3 and V of tile j + 2 (one DMA per odd slot).
-    auto step = [&](int hi, auto h8_c, f32x16& s_cur, f32x16& s_next, const u32x4 (&pk_prev)[2],
+    auto step = [&](int hi, int kv_tile, auto h8_c, f32x16& s_cur, f32x16& s_next, const u32x4 (&pk_prev)[2],
                     u32x4 (&pk_cur)[2], bool masked, bf16x8 (&fr)[kAhead], auto with_pv,
                     auto with_dma) {
         constexpr int H8 = decltype(h8_c)::value;
@@ -448,7 +505,8 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
         float e0[8], e1[8];  // exp2 of score pair k (held until packed)
         uint32_t wk[8];      // packed pair k (held until summed)
         auto mask_scores = [&]() {
-            const int kv0 = 32 * hi;
+            // first key of this half tile (block-sparse: of the listed tile)
+            const int kv0 = kSparse ? kv_tile + 32 * (hi & 1) : 32 * hi;
             // key of register r is kv0 + 16 (r >> 3) + 8 hh + (r & 7); masked: key > qrow
             // (causal) or key >= N, i.e. c > lim
             const int lim = (causal ? min_(qrow + off, Nk - 1) : Nk - 1) - kv0 - 8 * hh;
@@ -536,7 +594,10 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     // Tiles before n_plain need no mask in any wave of the workgroup: all their keys precede
     // the workgroup's first query row (causal) and the end of the sequence. The others mask
     // in every wave (a no-op where nothing is masked), behind a uniform branch.
-    const int n_plain = min_(n_tiles, causal ? max_(0, qb * kBr + off + 1) / kBc : Nk / kBc);
+    // (block-sparse: a key-tile index below n_plain needs no mask; the other modes compare the
+    // tile's position, which is its index)
+    const int n_plain = kSparse ? (causal ? (qb * kBr + 1) / kBc : N / kBc)
+                                : min_(n_tiles, causal ? max_(0, qb * kBr + off + 1) / kBc : Nk / kBc);
 
     f32x16 sa, sb;
     u32x4 pa[2], pb[2];
@@ -546,8 +607,9 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     using No = std::false_type;
 
     // (paged: an item none of whose rows sees a key skips to the epilogue)
-    if (!kPaged || n_tiles > 0) {
+    if (!(kPaged || kSparse) || n_tiles > 0) {
     if constexpr (kPaged) win = page_offsets(table_entries(wb), wb);
+    if constexpr (kSparse) win = tile_offsets(list_entries(wb), wb);
 
     // ---- prologue: K0..K2 and V0, V1 staged; scores of half tile 0 ----
     advance(0);
@@ -567,8 +629,11 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
         for (int sl = 0; sl < kAhead; ++sl) fr[sl] = (sl & 1) ? bf16x8{} : frag(b0, sl);
     }
     advance(3);
-    step(0, std::integral_constant<int, 0>{}, sa, sb, pb, pa, n_plain == 0, fr, No{}, Yes{});
-    step(1, std::integral_constant<int, 1>{}, sb, sa, pa, pb, n_plain == 0, fr, Yes{}, No{});
+    {
+        const bool masked0 = kSparse ? kvq0 >= n_plain * kBc : n_plain == 0;
+        step(0, kvq0, std::integral_constant<int, 0>{}, sa, sb, pb, pa, masked0, fr, No{}, Yes{});
+        step(1, kvq0, std::integral_constant<int, 1>{}, sb, sa, pa, pb, masked0, fr, Yes{}, No{});
+    }
     wait_dma_tile();
     barrier_lds();
 
@@ -580,10 +645,10 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     // unrolled over the four stage phases (it starts at j = 1). ----
     auto tile = [&](int j, auto phase_c) {
         constexpr int P = decltype(phase_c)::value;
-        const bool masked = j >= n_plain;
         advance(j + 3);
-        step(2 * j, std::integral_constant<int, 2 * P>{}, sa, sb, pb, pa, masked, fr, Yes{}, Yes{});
-        step(2 * j + 1, std::integral_constant<int, 2 * P + 1>{}, sb, sa, pa, pb, masked, fr, Yes{}, No{});
+        const bool masked = kSparse ? kvq0 >= n_plain * kBc : j >= n_plain;
+        step(2 * j, kvq0, std::integral_constant<int, 2 * P>{}, sa, sb, pb, pa, masked, fr, Yes{}, Yes{});
+        step(2 * j + 1, kvq0, std::integral_constant<int, 2 * P + 1>{}, sb, sa, pa, pb, masked, fr, Yes{}, No{});
         wait_dma_tile();
         barrier_lds();
     };
@@ -647,20 +712,20 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
 // r * W + j (r even) or r * W + W - 1 - j (r odd). The list runs heaviest query block first,
 // so the snake pairs heavy with light items and the workgroups finish together; and a
 // workgroup moves to its next item without a new launch.
-template <int D, bool kPaged>
+template <int D, int kMode>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(FwdArgs a) {
-    __shared__ __attribute__((aligned(16)))
-    unsigned char smem[kStages * (Tile<D, kPaged>::kKStage + Tile<D, kPaged>::kVStage)];
+    using T = Tile<D, kMode == kModePaged>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * (T::kKStage + T::kVStage)];
     const int per_unit = a.nqb * (a.Hq / a.Hkv);  // items of one KV group
     const int n_kvg = a.B * a.Hkv;
     const int total = n_kvg * per_unit;
     const int xcd = (int)(blockIdx.x % kXcds), j = (int)(blockIdx.x / kXcds);
     const int W = (int)(gridDim.x / kXcds);
-    // Dense: XCD x takes the x-th contiguous eighth of the list. Paged: XCD x takes the KV
-    // groups g = x, x + 8, ..., so every XCD gets a share of every sequence whatever the
-    // sequences' lengths (a KV group's items still stay on one XCD).
+    // Dense: XCD x takes the x-th contiguous eighth of the list. Paged and block-sparse: XCD x
+    // takes the KV groups g = x, x + 8, ..., so every XCD gets a share of every sequence (or
+    // head) whatever their lengths or block lists (a KV group's items stay on one XCD).
     int seg0 = 0, seg_n;
-    if constexpr (kPaged) {
+    if constexpr (kMode != kModeDense) {
         seg_n = (n_kvg > xcd ? (n_kvg - xcd + kXcds - 1) / kXcds : 0) * per_unit;
     } else {
         const int per_xcd = (total + kXcds - 1) / kXcds;
@@ -671,13 +736,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(FwdArgs a) {
         const int local = r * W + ((r & 1) ? W - 1 - j : j);
         if (local >= seg_n) continue;
         int item;
-        if constexpr (kPaged) {
+        if constexpr (kMode != kModeDense) {
             const int g = local / per_unit;
             item = (xcd + kXcds * g) * per_unit + (local - g * per_unit);
         } else {
             item = seg0 + local;
         }
-        fwd_item<D, kPaged>(a, item, smem);
+        fwd_item<D, kMode>(a, item, smem);
     }
 }
 
@@ -698,17 +763,17 @@ int persistent_cus() {
 }
 
 namespace {
-template <bool kPaged>
+template <int kMode>
 hipError_t launch_sp(const FwdArgs& a, int d, hipStream_t stream) {
     const long long items = (long long)a.nqb * a.B * a.Hq;
     const long long slots = (long long)(persistent_cus() / kXcds) * kXcds;
     long long grid = (items + kXcds - 1) / kXcds * kXcds;
     if (grid > slots) grid = slots;
     if (d == 128)
-        hipLaunchKernelGGL((fwd_bf16_sp_kernel<128, kPaged>), dim3((unsigned)grid), dim3(kThreads), 0,
+        hipLaunchKernelGGL((fwd_bf16_sp_kernel<128, kMode>), dim3((unsigned)grid), dim3(kThreads), 0,
                            stream, a);
     else
-        hipLaunchKernelGGL((fwd_bf16_sp_kernel<64, kPaged>), dim3((unsigned)grid), dim3(kThreads), 0,
+        hipLaunchKernelGGL((fwd_bf16_sp_kernel<64, kMode>), dim3((unsigned)grid), dim3(kThreads), 0,
                            stream, a);
     return hipGetLastError();
 }
@@ -728,7 +793,7 @@ hipError_t launch_fwd_bf16_sp(const void* q, const void* k, const void* v, void*
     a.scale_log2 = scale * kLog2e;
     a.causal = causal;
     a.nqb = (N + kBr - 1) / kBr;
-    return launch_sp<false>(a, d, stream);
+    return launch_sp<kModeDense>(a, d, stream);
 }
 
 hipError_t launch_fwd_bf16_sp_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -751,7 +816,29 @@ hipError_t launch_fwd_bf16_sp_paged(const void* q, const void* k_cache, const vo
     a.nqb = (Nq + kBr - 1) / kBr;
     a.max_pages = max_pages_per_seq;
     a.num_pages = num_pages;
-    return launch_sp<true>(a, d, stream);
+    return launch_sp<kModePaged>(a, d, stream);
+}
+
+hipError_t launch_fwd_bf16_sp_block_sparse(const void* q, const void* k, const void* v, void* o,
+                                           float* m_out, float* l_out, const int32_t* block_offsets,
+                                           const int32_t* block_indices, int nnz, int B, int Hq,
+                                           int Hkv, int N, int d, float scale, int causal,
+                                           hipStream_t stream) {
+    FwdArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.o = static_cast<uint16_t*>(o);
+    a.m_out = m_out;
+    a.l_out = l_out;
+    a.blk_off = block_offsets;
+    a.blk_idx = block_indices;
+    a.nnz = nnz;
+    a.B = B, a.Hq = Hq, a.Hkv = Hkv, a.N = N;
+    a.scale_log2 = scale * kLog2e;
+    a.causal = causal;
+    a.nqb = (N + kBr - 1) / kBr;
+    return launch_sp<kModeSparse>(a, d, stream);
 }
 
 }  // namespace fa

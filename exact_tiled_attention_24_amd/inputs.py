@@ -295,6 +295,83 @@ def config_prefill_paged_inputs(cfg: PrefillPagedConfig) -> PrefillPagedInputs:
                                 max_pages_per_seq=width, causal=cfg.causal)
 
 
+# ---- block masks for the block-sparse forward (256 query rows x 64 keys per block) ----
+
+SPARSE_BQ, SPARSE_BK = 256, 64
+
+
+def block_csr(rows):
+    """Compressed rows (int32 offsets, int32 indices) from one key-block list per row."""
+    offsets = np.zeros(len(rows) + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum([len(r) for r in rows])
+    indices = np.asarray([j for r in rows for j in r], dtype=np.int32)
+    return offsets, indices
+
+
+def local_global_blocks(B, Hq, N, window, n_global, causal=True, bq=SPARSE_BQ, bk=SPARSE_BK):
+    """Every head: query block qb lists the key blocks within `window` keys before its first
+    row up to its last row (or to the end without the causal mask), and the first
+    `n_global` key blocks."""
+    nqb, nkb = -(-N // bq), -(-N // bk)
+    rows = []
+    for _ in range(B * Hq):
+        for qb in range(nqb):
+            lo = max(0, (qb * bq - window) // bk)
+            hi = min(nkb, -(-min(N, (qb + 1) * bq) // bk)) if causal else min(nkb, -(-min(N, (qb + 1) * bq + window) // bk))
+            rows.append(sorted(set(range(min(n_global, nkb))) | set(range(lo, hi))))
+    return rows
+
+
+def random_blocks(B, Hq, N, density, seed, bq=SPARSE_BQ, bk=SPARSE_BK):
+    """Each (head, query block) lists each key block with probability `density`."""
+    rng = np.random.default_rng(seed)
+    nqb, nkb = -(-N // bq), -(-N // bk)
+    return [sorted(np.flatnonzero(rng.random(nkb) < density).tolist()) for _ in range(B * Hq * nqb)]
+
+
+def block_pairs(rows, B, Hq, N, causal, bq=SPARSE_BQ, bk=SPARSE_BK):
+    """Admissible (query, key) pairs over all heads: the FLOP count's 4 d multiplier aside,
+    the algorithmic work of the block-sparse forward."""
+    nqb, nkb = -(-N // bq), -(-N // bk)
+    total = 0
+    for r, blocks in enumerate(rows):
+        qb = r % nqb
+        i = np.arange(qb * bq, min(N, (qb + 1) * bq))
+        for kb in set(j for j in blocks if 0 <= j < nkb):
+            j0, j1 = kb * bk, min(N, (kb + 1) * bk)
+            if causal:
+                total += int(np.clip(i + 1 - j0, 0, j1 - j0).sum())
+            else:
+                total += len(i) * (j1 - j0)
+    return total
+
+
+@dataclass(frozen=True)
+class BlockSparseConfig:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    window: int
+    n_global: int
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+# Block-sparse forward (not one of the five workloads above): 2 x 32 query heads over 8 KV
+# heads, N = 16384, d = 128, causal, each 256-row query block sees the 2048 keys before it,
+# its own block and the first 256 keys (local window + global tokens), seed 7.
+BLOCK_SPARSE = BlockSparseConfig(
+    "block-sparse causal prefill bf16 B=2 Hq=32 Hkv=8 N=16384 d=128 window 2048 + 256 global",
+    2, 32, 8, 16384, 128, 2048, 4, True, 7)
+
+
 def to_torch(x: np.ndarray, dtype: str, device="cuda"):
     """Upload a float32 array as a torch tensor of ``dtype`` ("f32" or "bf16"), exactly."""
     import torch

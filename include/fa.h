@@ -14,6 +14,8 @@
  *                     the FlashAttention-family table (Flash-Decoding, paged variants).
  *   fa_merge          merge of partial (m, l, O) results over disjoint key sets with the
  *                     online-softmax rescale; "FlashAttention", "Decode is a different problem".
+ *   fa_fwd_block_sparse  tiled forward that visits only the key blocks a block mask lists;
+ *                     "FlashAttention, explained." (vibeengines.com), block-sparse section.
  *   fa_fwd_paged      tiled forward for the newest tokens of each sequence against its whole
  *                     paged KV cache (chunked prefill); the paged variants of the
  *                     FlashAttention-family table ("FlashAttention") with the update rule of
@@ -111,6 +113,34 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int d, int page_size, int max_se
 
 /* The number of KV chunks the automatic plan gives the longest sequence (0 if invalid). */
 int fa_decode_plan_splits(int B, int Hkv, int page_size, int max_seq_len);
+
+/* Block sizes of fa_fwd_block_sparse's mask: query rows per block, keys per block. */
+#define FA_SPARSE_BLOCK_Q 256
+#define FA_SPARSE_BLOCK_K 64
+
+/*
+ * fa_fwd_block_sparse - tiled forward restricted to listed (query block, key block) pairs.
+ *
+ *   q, o    : [B, Hq, N, d] bf16;  k, v : [B, Hkv, N, d] bf16 (GQA as in fa_fwd)
+ *   m_out, l_out : optional float32 [B, Hq, N] row statistics (NULL = not written)
+ *   block_offsets : int32 [B * Hq * ceil(N / 256) + 1], device memory
+ *   block_indices : int32 [nnz], device memory
+ *
+ * Query block qb (rows 256 qb .. 256 qb + 255) of head (b, h) attends to the key blocks
+ * (keys 64 kb .. 64 kb + 63) block_indices[block_offsets[r] .. block_offsets[r + 1]) with
+ * r = (b * Hq + h) * ceil(N / 256) + qb, in that order; with causal != 0 key j is further
+ * limited to j <= i. An index outside [0, ceil(N / 64)) names no key; a block listed twice
+ * counts twice (the caller lists each at most once). A query that admits no key yields O = 0,
+ * m = -inf, l = 0. Each list is clamped into [0, nnz], so no offset makes the kernel read
+ * outside block_indices. Every listed block is computed: blocks that lie wholly above the
+ * causal diagonal cost time and contribute nothing.
+ * Supported: dt = FA_BF16; d in {64, 128}; Hq % Hkv == 0 (else FA_ERR_INVALID_ARGUMENT);
+ * N * d < 2^31; nnz >= 0. B, Hq or N equal to 0 is a valid empty call.
+ */
+fa_status fa_fwd_block_sparse(fa_dtype dt, const void* q, const void* k, const void* v, void* o,
+                              float* m_out, float* l_out, const int32_t* block_offsets,
+                              const int32_t* block_indices, int nnz, int B, int Hq, int Hkv,
+                              int N, int d, float scale, int causal, void* stream);
 
 /*
  * fa_fwd_paged - tiled forward of each sequence's newest Nq tokens against its paged cache.

@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_decode_splitk", "fa_merge", "fa_status_string",
-              "fa_decode_workspace_bytes", "fa_decode_plan_splits", "fa_fwd_paged"):
+              "fa_decode_workspace_bytes", "fa_decode_plan_splits", "fa_fwd_paged",
+              "fa_fwd_block_sparse"):
         assert n in names
 
 
@@ -165,6 +166,31 @@ def paged(lib, dt=1, q=DEV, kc=DEV, vc=DEV, table=DEV, lens=DEV, o=DEV, B=2, Hq=
 ])
 def test_fwd_paged_validation(kwargs, code):
     assert paged(fa.load_library(), **kwargs) == code
+
+
+def sparse(lib, dt=1, q=DEV, k=DEV, v=DEV, o=DEV, offs=DEV, idx=DEV, nnz=4, B=1, Hq=4, Hkv=2,
+           N=512, d=128, scale=0.1, causal=0):
+    return lib.fa_fwd_block_sparse(dt, q, k, v, o, None, None, offs, idx, nnz, B, Hq, Hkv, N, d,
+                                   scale, causal, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(dt=3), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(dt=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(Hq=3, Hkv=2), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(nnz=-1), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(N=-5), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(offs=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(idx=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(v=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(k=MIS), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(N=1 << 25), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=0, q=NULL), fa.FA_OK),
+])
+def test_fwd_block_sparse_validation(kwargs, code):
+    assert sparse(fa.load_library(), **kwargs) == code
 
 
 def merge(lib, dt=0, op=DEV, mp=DEV, lp=DEV, o=DEV, S=4, R=8, d=128):
