@@ -122,6 +122,7 @@ def summarize(paths, kernel=None):
 TRAFFIC_KERNELS = {
     "fwd": ("fwd_bf16_sp_kernel<128, 0>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
     "paged": ("fwd_bf16_sp_kernel<128, 1>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
+    "sparse": ("fwd_bf16_sp_kernel<128, 2>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
     "decode": ("decode_mx_kernel", "exact_tiled_attention_24_amd/csrc/decode_mx.hip"),
 }
 COPY_KERNEL = "copyBuffer"
@@ -436,7 +437,7 @@ def main():
             "tokens_per_s": round(scfg.B * scfg.N / (sparse_ms.mean() * 1e-3), 1),
             "roofline": {"bound": "mfma", "achieved": round(s_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(s_tflops / PEAK_BF16_TFLOPS, 4),
-                         "kernel": "fwd_bf16_sp_kernel<128, 2>"},
+                         "traffic": traffic.get("sparse"), "kernel": "fwd_bf16_sp_kernel<128, 2>"},
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(fx, fcfg, args.cpu_heads)
