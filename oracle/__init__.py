@@ -14,6 +14,7 @@ here are pinned; none is "parity unpinned".
 
 from .attention import (  # noqa: F401
     attention,
+    attention_backward,
     attention_block_sparse,
     attention_head,
     attention_probs,

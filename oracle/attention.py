@@ -13,7 +13,9 @@ Sources, cited by page title and section:
 * "FlashAttention, explained." (vibeengines.com), the worked example of the rescaling
   trick, and the forward-pass statement (Q, K, V are N x d per head, 1/sqrt(d) scale and
   masking fused, the statistics m and l are kept alongside O); its block-sparse section: a
-  block mask over (query block, key block) pairs removes whole blocks of scores.
+  block mask over (query block, key block) pairs removes whole blocks of scores; its
+  backward-pass section: the gradients are recomputed from Q, K, V with the saved m, l and
+  D_i = rowsum(dO_i * O_i).
 
 Conventions (readings of points the pages leave open):
 
@@ -240,6 +242,43 @@ def attention_block_sparse(q, k, v, scale, causal, block_offsets, block_indices,
                 m_out[b, h, rows] = m
                 l_out[b, h, rows] = l
     return out, m_out, l_out
+
+
+def attention_backward(q, k, v, dout, scale, causal):
+    """Gradients of O = softmax(scale * q k^T + M) v with respect to q, k and v.
+
+    q, dout: [B, Hq, N, d]; k, v: [B, Hkv, N, d]. Per head, with P the normalised
+    probabilities and D_i = sum_c dO_ic O_ic:
+        dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   dQ = scale dS K,   dK = scale dS^T Q
+    (the chain rule through the row-wise softmax: dS_ij = P_ij (dP_ij - sum_t P_it dP_it), and
+    sum_t P_it dP_it = D_i). A key/value head shared by several query heads receives the sum
+    of their gradients. P is materialised in full for each head (small inputs only).
+
+    Returns dQ [B, Hq, N, d], dK [B, Hkv, N, d], dV [B, Hkv, N, d], float64.
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    dout = _f64(dout)
+    b_, hq, n, d = q.shape
+    hkv = k.shape[1]
+    group = hq // hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros((b_, hkv, n, d))
+    dv = np.zeros((b_, hkv, n, v.shape[-1]))
+    for b in range(b_):
+        for h in range(hq):
+            kh = h // group
+            p = attention_probs(q[b, h], k[b, kh], scale, causal)
+            o = p @ v[b, kh]
+            dvv = p.T @ dout[b, h]
+            dp = dout[b, h] @ v[b, kh].T
+            dd = (dout[b, h] * o).sum(axis=1)
+            ds = p * (dp - dd[:, None])
+            dq[b, h] = scale * (ds @ k[b, kh])
+            dk[b, kh] += scale * (ds.T @ q[b, h])
+            dv[b, kh] += dvv
+    return dq, dk, dv
 
 
 def merge(o_parts, m_parts, l_parts):
