@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
     fa_decode_splitk(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, ...)
     fa_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=True, ...)
     fa_fwd_block_sparse(q, k, v, block_offsets, block_indices, scale=None, causal=False, ...)
+    fa_bwd(q, k, v, o, dout, m, l, scale=None, causal=False, workspace=None)
     fa_merge(o_parts, m_parts, l_parts, out_dtype=torch.float32, return_stats=False)
     fa_decode_workspace_bytes(...), fa_decode_plan_splits(...), fa_status_string(code)
 """
@@ -67,6 +68,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_block_sparse.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                         i32, i32, f32, i32, vp]
     lib.fa_fwd_block_sparse.restype = i32
+    lib.fa_bwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                           f32, i32, vp, sz, vp]
+    lib.fa_bwd.restype = i32
+    lib.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_merge.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
     lib.fa_merge.restype = i32
     lib.fa_status_string.argtypes = [i32]
@@ -235,6 +241,39 @@ def fa_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=
             block_table.shape[1], scale, 1 if causal else 0, _stream(q.device))
     _check(code, "fa_fwd_paged")
     return (o, m, l) if return_stats else o
+
+
+def fa_bwd_workspace_bytes(B, Hq, N) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(B, Hq, N))
+
+
+def fa_bwd(q, k, v, o, dout, m, l, scale=None, causal=False, workspace=None):
+    """Backward of fa_fwd: returns (dq, dk, dv) in q's dtype (bf16). q, o, dout: [B, Hq, N, d];
+    k, v: [B, Hkv, N, d]; m, l: the float32 [B, Hq, N] statistics fa_fwd returned."""
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B, Hq, N, d] and k, v [B, Hkv, N, d]")
+    B, Hq, N, d = q.shape
+    if o.shape != q.shape or dout.shape != q.shape or k.shape[0] != B or k.shape[2:] != q.shape[2:]:
+        raise ValueError("shape mismatch")
+    if m.shape != (B, Hq, N) or l.shape != (B, Hq, N) or m.dtype != torch.float32 or l.dtype != torch.float32:
+        raise ValueError("m and l must be float32 [B, Hq, N]")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    if workspace is None:
+        workspace = torch.empty(max(fa_bwd_workspace_bytes(B, Hq, N), 16), dtype=torch.uint8,
+                                device=q.device)
+    _require_gpu(q, k, v, o, dout, m, l, dq, dk, dv, workspace)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        code = lib.fa_bwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(m),
+                          _ptr(l), _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, k.shape[1], N, d, scale,
+                          1 if causal else 0, _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(code, "fa_bwd")
+    return dq, dk, dv
 
 
 SPARSE_BLOCK_Q = 256

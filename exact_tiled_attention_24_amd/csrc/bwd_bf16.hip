@@ -1,0 +1,363 @@
+// bwd_bf16.hip - attention backward by recomputation, bf16 in / bf16 out, fp32 accumulation.
+//
+// Method: "FlashAttention, explained." (vibeengines.com), the backward-pass section: nothing of
+// size N x N is stored by the forward; the backward recomputes the probabilities tile by tile
+// from Q, K and the saved row statistics, P = exp(s - m) / l, and uses D_i = rowsum(dO_i * O_i)
+// so that dS = P * (dP - D) needs no second pass over the keys. With dP = dO V^T:
+//     dV = P^T dO,   dK = scale dS^T Q,   dQ = scale dS K.
+//
+// Three kernels:
+//  * bwd_prep: D_i and the log2-domain normaliser L_i = (m_i + ln l_i) log2 e of every query
+//    row, so that P = exp2(scale log2e q.k - L) (L = +inf for a row with no key: P = 0).
+//  * bwd_dkdv: one workgroup per (128-key block, KV head); each wave keeps its 32 keys' K and V
+//    in registers and walks the query chunks (32 rows of Q and dO staged in LDS) of every
+//    query head of the KV group, accumulating dV^T and dK^T.
+//  * bwd_dq: one workgroup per (128-query block, query head); each wave keeps its 32 queries'
+//    Q and dO in registers and walks the key chunks (32 rows of K and V in LDS).
+// All products use v_mfma_f32_32x32x16_bf16. As in the forward kernel, the score tile is
+// computed with the rows of its A operand read in an order that swaps bits 2 and 3 of the row
+// index, so that the accumulator, rounded to bf16, is directly the B operand of the next
+// product (no LDS round trip for P or dS); the transposed operands (Q^T, dO^T, K^T) come out
+// of row-major LDS tiles through ds_read_b64_tr_b16.
+#include "fa_internal.hpp"
+#include "gfx950.hpp"
+
+namespace fa {
+namespace {
+
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kChunk = 32;     // rows of a staged chunk
+constexpr int kBlock = 128;    // keys (dK/dV) or queries (dQ) per workgroup: 32 per wave
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef const __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef const __attribute__((address_space(3))) unsigned char* lds_cptr;
+
+__device__ __forceinline__ int kappa(int m) {
+    return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// Natural row index of accumulator register r in lane half h when the A operand's rows were
+// read in kappa order: registers 0-7 hold rows 8h .. 8h + 7, registers 8-15 rows 16 + 8h ..
+__device__ __forceinline__ int acc_row(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
+
+template <int D>
+struct Stage {
+    static constexpr int kRow = D * 2 + 16;  // padded row, bytes
+    static constexpr int kTile = kChunk * kRow;
+};
+
+// A chunk of 32 rows x D bf16 from global memory (rows past n read as zero) into LDS at dst,
+// padded rows; all 256 threads take part.
+template <int D>
+__device__ __forceinline__ void stage_rows(unsigned char* dst, const uint16_t* src, int row0, int n) {
+    constexpr int kPer = D * 2 / 16;  // 16-byte pieces per row
+    for (int i = threadIdx.x; i < kChunk * kPer; i += kThreads) {
+        const int r = i / kPer, c = i - r * kPer;
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (row0 + r < n) v = *reinterpret_cast<const u32x4*>(src + (size_t)(row0 + r) * D + 8 * c);
+        *reinterpret_cast<u32x4*>(dst + r * Stage<D>::kRow + 16 * c) = v;
+    }
+}
+
+// A operand of a 32 x 16 slice (K-dim chunk kk) of a staged tile, rows in kappa order.
+template <int D>
+__device__ __forceinline__ bf16x8 rows_frag(lds_cptr tile, int lane, int kk) {
+    return *reinterpret_cast<const lds_bf16x8*>(tile + kappa(lane & 31) * Stage<D>::kRow + 32 * kk +
+                                                 16 * (lane >> 5));
+}
+
+// A operand of the transposed tile X^T (rows = head dimensions 32 db .., K-dim = the tile's
+// rows 16 t ..): ds_read_b64_tr_b16 transposes within each 16-lane group, so two reads give
+// a lane its 8 consecutive rows of one head dimension.
+template <int D>
+__device__ __forceinline__ bf16x8 trans_frag(lds_cptr tile, int lane, int t, int db) {
+    constexpr int R = Stage<D>::kRow;
+    const lds_cptr p = tile + (8 * (lane >> 5) + ((lane & 15) >> 2)) * R +
+                       (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2 + 16 * t * R + 64 * db;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * R));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Accumulator registers 8 t .. 8 t + 7, rounded to bf16: the B operand (K-dim rows 16 t ..).
+__device__ __forceinline__ bf16x8 acc_operand(const float (&x)[16], int t) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(x[8 * t + 2 * i], x[8 * t + 2 * i + 1]);
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+// ---- D_i = rowsum(dO * O) and L_i = (m_i + ln l_i) log2 e, 4 threads per row ----
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const uint16_t* __restrict__ o,
+                                                            const uint16_t* __restrict__ dout,
+                                                            const float* __restrict__ m,
+                                                            const float* __restrict__ l,
+                                                            float* __restrict__ lse2,
+                                                            float* __restrict__ dsum, long long rows) {
+    const long long row = (long long)blockIdx.x * (kThreads / 4) + threadIdx.x / 4;
+    const int part = threadIdx.x & 3;
+    float acc = 0.f;
+    if (row < rows) {
+        const uint16_t* po = o + row * D + part * (D / 4);
+        const uint16_t* pd = dout + row * D + part * (D / 4);
+#pragma unroll
+        for (int c = 0; c < D / 4; c += 8) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(po + c);
+            const u32x4 b = *reinterpret_cast<const u32x4*>(pd + c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc = __builtin_fmaf(bf16_lo(a[i]), bf16_lo(b[i]), acc);
+                acc = __builtin_fmaf(bf16_hi(a[i]), bf16_hi(b[i]), acc);
+            }
+        }
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    if (row < rows && part == 0) {
+        dsum[row] = acc;
+        const float lr = l[row];
+        lse2[row] = lr > 0.f ? (m[row] + logf(lr)) * kLog2e : INFINITY;
+    }
+}
+
+struct BwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* dout;
+    const float* lse2;  // [B, Hq, N]
+    const float* dsum;  // [B, Hq, N]
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    int Hq, Hkv, N;
+    float scale, scale_log2;
+    int causal;
+};
+
+// ---- dK, dV: workgroup = 128 keys of one KV head; wave = 32 keys ----
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
+    using S = Stage<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * S::kTile + 2 * kChunk * 4];
+    unsigned char* const t_q = smem;
+    unsigned char* const t_do = smem + S::kTile;
+    float* const s_l = reinterpret_cast<float*>(smem + 2 * S::kTile);
+    float* const s_d = s_l + kChunk;
+    lds_cptr const lq = (lds_cptr)t_q;
+    lds_cptr const ldo = (lds_cptr)t_do;
+
+    const int N = a.N, G = a.Hq / a.Hkv;
+    const int bk = blockIdx.y;  // b * Hkv + kvh
+    const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
+    const int kb0 = blockIdx.x * kBlock;
+    const int lane = threadIdx.x & 63, h = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int key = kb0 + 32 * wave + (lane & 31);  // this lane's key (accumulator column)
+
+    // K and V of the lane's key as B operands (K-dim = head dimension 16 kk + 8 h ..)
+    const size_t kvoff = (size_t)bk * N * D;
+    bf16x8 kf[D / 16], vf[D / 16];
+    {
+        const int kr = min_(key, N - 1);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            kf[kk] = *reinterpret_cast<const bf16x8*>(a.k + kvoff + (size_t)kr * D + 16 * kk + 8 * h);
+            vf[kk] = *reinterpret_cast<const bf16x8*>(a.v + kvoff + (size_t)kr * D + 16 * kk + 8 * h);
+        }
+    }
+    f32x16 acc_dk[D / 32], acc_dv[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) acc_dk[i] = acc_dv[i] = f32x16{};
+
+    // causal: queries before the block's first key see none of its keys
+    const int q_first = a.causal ? (kb0 / kChunk) * kChunk : 0;
+    for (int g = 0; g < G; ++g) {
+        const int hq = kvh * G + g;
+        const size_t qoff = ((size_t)b * a.Hq + hq) * N;
+        for (int qc0 = q_first; qc0 < N; qc0 += kChunk) {
+            __syncthreads();  // the previous chunk's tiles are no longer read
+            stage_rows<D>(t_q, a.q + qoff * D, qc0, N);
+            stage_rows<D>(t_do, a.dout + qoff * D, qc0, N);
+            if (threadIdx.x < kChunk) {
+                const int qi = qc0 + threadIdx.x;
+                s_l[threadIdx.x] = qi < N ? a.lse2[qoff + qi] : INFINITY;
+                s_d[threadIdx.x] = qi < N ? a.dsum[qoff + qi] : 0.f;
+            }
+            __syncthreads();
+
+            // S = Q K^T and dP = dO V^T for the chunk's 32 queries x the wave's 32 keys
+            f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                sc = mfma_32x32x16(rows_frag<D>(lq, lane, kk), kf[kk], sc);
+                dp = mfma_32x32x16(rows_frag<D>(ldo, lane, kk), vf[kk], dp);
+            }
+            float p[16], ds[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qr = acc_row(r, h);
+                const int qi = qc0 + qr;
+                const bool ok = key < N && qi < N && (!a.causal || key <= qi);
+                p[r] = ok ? exp2_hw(__builtin_fmaf(sc[r], a.scale_log2, -s_l[qr])) : 0.f;
+                ds[r] = p[r] * (dp[r] - s_d[qr]);
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS (K-dim = the chunk's queries)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const bf16x8 pb = acc_operand(p, t), sb = acc_operand(ds, t);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    acc_dv[db] = mfma_32x32x16(trans_frag<D>(ldo, lane, t, db), pb, acc_dv[db]);
+                    acc_dk[db] = mfma_32x32x16(trans_frag<D>(lq, lane, t, db), sb, acc_dk[db]);
+                }
+            }
+        }
+    }
+    // accumulator register r of block db: head dimension 32 db + 8 (r / 4) + 4 h + r % 4
+    if (key < N) {
+        uint16_t* pk = a.dk + kvoff + (size_t)key * D;
+        uint16_t* pv = a.dv + kvoff + (size_t)key * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int d0 = 32 * db + 8 * gq + 4 * h;
+                u32x2 wk = {pack_bf16x2(a.scale * acc_dk[db][4 * gq], a.scale * acc_dk[db][4 * gq + 1]),
+                            pack_bf16x2(a.scale * acc_dk[db][4 * gq + 2], a.scale * acc_dk[db][4 * gq + 3])};
+                u32x2 wv = {pack_bf16x2(acc_dv[db][4 * gq], acc_dv[db][4 * gq + 1]),
+                            pack_bf16x2(acc_dv[db][4 * gq + 2], acc_dv[db][4 * gq + 3])};
+                *reinterpret_cast<u32x2*>(pk + d0) = wk;
+                *reinterpret_cast<u32x2*>(pv + d0) = wv;
+            }
+    }
+}
+
+// ---- dQ: workgroup = 128 queries of one query head; wave = 32 queries ----
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
+    using S = Stage<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * S::kTile];
+    unsigned char* const t_k = smem;
+    unsigned char* const t_v = smem + S::kTile;
+    lds_cptr const lk = (lds_cptr)t_k;
+    lds_cptr const lv = (lds_cptr)t_v;
+
+    const int N = a.N, G = a.Hq / a.Hkv;
+    const int bh = blockIdx.y;  // b * Hq + hq
+    const int b = bh / a.Hq, hq = bh - b * a.Hq;
+    const int kvh = hq / G;
+    const int qb0 = blockIdx.x * kBlock;
+    const int lane = threadIdx.x & 63, h = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int query = qb0 + 32 * wave + (lane & 31);  // this lane's query (accumulator column)
+
+    const size_t qoff = (size_t)bh * N;
+    const size_t kvoff = ((size_t)b * a.Hkv + kvh) * N * D;
+    bf16x8 qf[D / 16], dof[D / 16];
+    {
+        const int qr = min_(query, N - 1);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            qf[kk] = *reinterpret_cast<const bf16x8*>(a.q + (qoff + qr) * D + 16 * kk + 8 * h);
+            dof[kk] = *reinterpret_cast<const bf16x8*>(a.dout + (qoff + qr) * D + 16 * kk + 8 * h);
+        }
+    }
+    const float lse = query < N ? a.lse2[qoff + query] : INFINITY;
+    const float dsum = query < N ? a.dsum[qoff + query] : 0.f;
+    f32x16 acc_dq[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) acc_dq[i] = f32x16{};
+
+    const int k_end = a.causal ? min_(N, qb0 + kBlock) : N;  // keys past the block's last query
+    for (int kc0 = 0; kc0 < k_end; kc0 += kChunk) {
+        __syncthreads();
+        stage_rows<D>(t_k, a.k + kvoff, kc0, N);
+        stage_rows<D>(t_v, a.v + kvoff, kc0, N);
+        __syncthreads();
+
+        // S^T = K Q^T and dP^T = V dO^T: the chunk's 32 keys x the wave's 32 queries
+        f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            sc = mfma_32x32x16(rows_frag<D>(lk, lane, kk), qf[kk], sc);
+            dp = mfma_32x32x16(rows_frag<D>(lv, lane, kk), dof[kk], dp);
+        }
+        float ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kj = kc0 + acc_row(r, h);
+            const bool ok = kj < N && query < N && (!a.causal || kj <= query);
+            const float p = ok ? exp2_hw(__builtin_fmaf(sc[r], a.scale_log2, -lse)) : 0.f;
+            ds[r] = p * (dp[r] - dsum);
+        }
+        // dQ^T += K^T dS^T (K-dim = the chunk's keys)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const bf16x8 sb = acc_operand(ds, t);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+                acc_dq[db] = mfma_32x32x16(trans_frag<D>(lk, lane, t, db), sb, acc_dq[db]);
+        }
+    }
+    if (query < N) {
+        uint16_t* pq = a.dq + (qoff + query) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int d0 = 32 * db + 8 * gq + 4 * h;
+                u32x2 w = {pack_bf16x2(a.scale * acc_dq[db][4 * gq], a.scale * acc_dq[db][4 * gq + 1]),
+                           pack_bf16x2(a.scale * acc_dq[db][4 * gq + 2], a.scale * acc_dq[db][4 * gq + 3])};
+                *reinterpret_cast<u32x2*>(pq + d0) = w;
+            }
+    }
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a, const uint16_t* o, const float* m, const float* l,
+                        float* lse2, float* dsum, int B, hipStream_t stream) {
+    const long long rows = (long long)B * a.Hq * a.N;
+    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + 63) / 64)), dim3(kThreads), 0,
+                       stream, o, a.dout, m, l, lse2, dsum, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned blocks = (unsigned)((a.N + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(blocks, (unsigned)(B * a.Hkv)), dim3(kThreads), 0,
+                       stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(blocks, (unsigned)(B * a.Hq)), dim3(kThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* m, const float* l, void* dq, void* dk,
+                           void* dv, int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                           float* lse2, float* dsum, hipStream_t stream) {
+    BwdArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.dout = static_cast<const uint16_t*>(dout);
+    a.lse2 = lse2;
+    a.dsum = dsum;
+    a.dq = static_cast<uint16_t*>(dq);
+    a.dk = static_cast<uint16_t*>(dk);
+    a.dv = static_cast<uint16_t*>(dv);
+    a.Hq = Hq, a.Hkv = Hkv, a.N = N;
+    a.scale = scale;
+    a.scale_log2 = scale * kLog2e;
+    a.causal = causal;
+    const uint16_t* op = static_cast<const uint16_t*>(o);
+    return d == 128 ? launch_bwd_d<128>(a, op, m, l, lse2, dsum, B, stream)
+                    : launch_bwd_d<64>(a, op, m, l, lse2, dsum, B, stream);
+}
+
+}  // namespace fa

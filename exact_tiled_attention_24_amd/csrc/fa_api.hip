@@ -174,6 +174,38 @@ fa_status fa_decode_splitk(fa_dtype dt, const void* q, const void* k_cache, cons
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_bwd_workspace_bytes(int B, int Hq, int N) {
+    if (B < 0 || Hq < 0 || N < 0) return 0;
+    return 2 * (size_t)B * (size_t)Hq * (size_t)N * sizeof(float);
+}
+
+fa_status fa_bwd(fa_dtype dt, const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* m, const float* l, void* dq, void* dk, void* dv,
+                 int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    if (dt != FA_F32 && dt != FA_BF16) return FA_ERR_INVALID_ARGUMENT;
+    if (B < 0 || Hq < 0 || Hkv < 0 || N < 0) return FA_ERR_INVALID_ARGUMENT;
+    if (!scale_ok(scale)) return FA_ERR_INVALID_ARGUMENT;
+    if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0)) return FA_ERR_INVALID_ARGUMENT;
+    if (dt != FA_BF16 || (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || Hq == 0 || N == 0) return FA_OK;
+    if (!q || !k || !v || !o || !dout || !m || !l || !dq || !dk || !dv || !workspace)
+        return FA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+        return FA_ERR_INVALID_ARGUMENT;
+    if ((long long)N * d >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * Hq >= 65536 || ((long long)N + 127) / 128 >= (1LL << 31))
+        return FA_ERR_UNSUPPORTED;  // grid y holds (batch, head)
+    if (workspace_bytes < fa_bwd_workspace_bytes(B, Hq, N)) return FA_ERR_WORKSPACE_TOO_SMALL;
+    float* lse2 = static_cast<float*>(workspace);
+    float* dsum = lse2 + (size_t)B * Hq * N;
+    const hipError_t e = fa::launch_bwd_bf16(q, k, v, o, dout, m, l, dq, dk, dv, B, Hq, Hkv, N, d,
+                                             scale, causal ? 1 : 0, lse2, dsum,
+                                             static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_fwd_block_sparse(fa_dtype dt, const void* q, const void* k, const void* v, void* o,
                               float* m_out, float* l_out, const int32_t* block_offsets,
                               const int32_t* block_indices, int nnz, int B, int Hq, int Hkv,

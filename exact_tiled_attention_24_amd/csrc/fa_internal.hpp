@@ -38,6 +38,13 @@ hipError_t launch_fwd_bf16_sp_block_sparse(const void* q, const void* k, const v
                                            int Hkv, int N, int d, float scale, int causal,
                                            hipStream_t stream);
 
+// Backward by recomputation: D and the log2 normaliser into lse2 / dsum ([B, Hq, N] float32
+// each, caller workspace), then dK/dV and dQ (bf16 outputs, float32 accumulation).
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* m, const float* l, void* dq, void* dk,
+                           void* dv, int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                           float* lse2, float* dsum, hipStream_t stream);
+
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* m_out,
                           float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
                           int causal, hipStream_t stream);

@@ -14,6 +14,9 @@
  *                     the FlashAttention-family table (Flash-Decoding, paged variants).
  *   fa_merge          merge of partial (m, l, O) results over disjoint key sets with the
  *                     online-softmax rescale; "FlashAttention", "Decode is a different problem".
+ *   fa_bwd            backward by recomputation (dQ, dK, dV from Q, K, V, O, dO and the saved
+ *                     row statistics); "FlashAttention, explained." (vibeengines.com),
+ *                     backward-pass section.
  *   fa_fwd_block_sparse  tiled forward that visits only the key blocks a block mask lists;
  *                     "FlashAttention, explained." (vibeengines.com), block-sparse section.
  *   fa_fwd_paged      tiled forward for the newest tokens of each sequence against its whole
@@ -113,6 +116,30 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int d, int page_size, int max_se
 
 /* The number of KV chunks the automatic plan gives the longest sequence (0 if invalid). */
 int fa_decode_plan_splits(int B, int Hkv, int page_size, int max_seq_len);
+
+/*
+ * fa_bwd - gradients of fa_fwd's output with respect to q, k and v.
+ *
+ *   q, o, dout, dq : [B, Hq, N, d] bf16;  k, v, dk, dv : [B, Hkv, N, d] bf16
+ *   m, l           : float32 [B, Hq, N], the row statistics fa_fwd returned for (q, k, v)
+ *   workspace      : device scratch of at least fa_bwd_workspace_bytes(B, Hq, N) bytes;
+ *                    contents on entry are ignored
+ *
+ * With P = exp(scale q k^T + M - m) / l, D_i = sum_c dout_ic o_ic and dP = dout v^T:
+ * dv = P^T dout, dS = P * (dP - D), dq = scale dS k, dk = scale dS^T q. A key/value head shared
+ * by several query heads receives the sum of their gradients. `causal` and `scale` must be the
+ * forward's. float32 accumulation; dq, dk, dv rounded to bf16 once. Rows with l = 0 contribute
+ * nothing. Supported: dt = FA_BF16; d in {64, 128}; Hq % Hkv == 0 (else
+ * FA_ERR_INVALID_ARGUMENT); N * d < 2^31; B * Hq < 65536. B, Hq or N equal to 0 is a valid
+ * empty call.
+ */
+fa_status fa_bwd(fa_dtype dt, const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* m, const float* l, void* dq, void* dk, void* dv,
+                 int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_bwd needs (two float32 values per query row; 0 for negative sizes). */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int N);
 
 /* Block sizes of fa_fwd_block_sparse's mask: query rows per block, keys per block. */
 #define FA_SPARSE_BLOCK_Q 256

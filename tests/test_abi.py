@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_decode_splitk", "fa_merge", "fa_status_string",
               "fa_decode_workspace_bytes", "fa_decode_plan_splits", "fa_fwd_paged",
-              "fa_fwd_block_sparse"):
+              "fa_fwd_block_sparse", "fa_bwd", "fa_bwd_workspace_bytes"):
         assert n in names
 
 
@@ -191,6 +191,36 @@ def sparse(lib, dt=1, q=DEV, k=DEV, v=DEV, o=DEV, offs=DEV, idx=DEV, nnz=4, B=1,
 ])
 def test_fwd_block_sparse_validation(kwargs, code):
     assert sparse(fa.load_library(), **kwargs) == code
+
+
+def bwd(lib, dt=1, q=DEV, k=DEV, v=DEV, o=DEV, do=DEV, m=DEV, l=DEV, dq=DEV, dk=DEV, dv=DEV,
+        B=1, Hq=4, Hkv=2, N=300, d=128, scale=0.1, causal=1, ws=DEV, ws_bytes=1 << 20):
+    return lib.fa_bwd(dt, q, k, v, o, do, m, l, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal, ws,
+                      ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(dt=4), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(dt=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(Hq=5, Hkv=2), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(N=-1), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(do=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(l=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(dk=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(ws=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(dq=MIS), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(ws_bytes=2 * 4 * 300 * 4 - 1), fa.FA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(B=0, q=NULL), fa.FA_OK),
+])
+def test_bwd_validation(kwargs, code):
+    assert bwd(fa.load_library(), **kwargs) == code
+
+
+def test_bwd_workspace_bytes():
+    assert fa.fa_bwd_workspace_bytes(2, 8, 1000) == 2 * 2 * 8 * 1000 * 4
+    assert fa.fa_bwd_workspace_bytes(-1, 8, 10) == 0
 
 
 def merge(lib, dt=0, op=DEV, mp=DEV, lp=DEV, o=DEV, S=4, R=8, d=128):
