@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64,
                     help="heads of the forward workload the oracle is timed on")
-    ap.add_argument("--only", choices=["fwd", "decode", "paged", "sparse"], default=None,
+    ap.add_argument("--only", choices=["fwd", "decode", "paged", "sparse", "bwd"], default=None,
                     help="time one kernel only (profiling runs)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling)")
@@ -216,6 +216,7 @@ def main():
     do_dec = args.only in (None, "decode")
     do_paged = args.only in (None, "paged")
     do_sparse = args.only in (None, "sparse")
+    do_bwd = args.only in (None, "bwd")
 
     # ---- inputs, resident in HBM ----
     fcfg = gen.CONFIGS[args.fwd_config]
@@ -282,6 +283,27 @@ def main():
         sparse_flops = 4.0 * scfg.d * gen.block_pairs(s_rows, scfg.B, scfg.Hq, scfg.N, scfg.causal)
         sparse_blocks = int(s_idx.size)
         del sx
+
+    bwd_flops = None
+    if do_bwd:
+        # backward of the forward workload: 10 d FLOP per admissible pair (S, dP, dV, dK, dQ)
+        bcfg = gen.CONFIGS[args.fwd_config]
+        bx = gen.config_fwd_inputs(bcfg)
+        b_q, b_k, b_v = (gen.to_torch(t, "bf16", dev) for t in (bx.q, bx.k, bx.v))
+        b_do = gen.to_torch(gen.round_to_bf16(
+            np.random.default_rng(bcfg.seed + 100).standard_normal(bx.q.shape, dtype=np.float32)),
+            "bf16", dev)
+        b_o, b_m, b_l = fa.fa_fwd(b_q, b_k, b_v, scale=bx.scale, causal=bcfg.causal,
+                                  return_stats=True)
+        b_ws = torch.empty(fa.fa_bwd_workspace_bytes(bcfg.B, bcfg.Hq, bcfg.N), dtype=torch.uint8,
+                           device=dev)
+        bwd_flops = 2.5 * bcfg.flops()
+        bwd_scale = bx.scale
+        del bx
+
+    def run_bwd():
+        fa.fa_bwd(b_q, b_k, b_v, b_o, b_do, b_m, b_l, scale=bwd_scale, causal=bcfg.causal,
+                  workspace=b_ws)
 
     def run_sparse():
         fa.fa_fwd_block_sparse(s_q, s_k, s_v, s_offs_t, s_idx_t, scale=scfg.scale,
@@ -361,6 +383,19 @@ def main():
         torch.cuda.synchronize()
         sparse_ms = np.array([a.elapsed_time(b) for a, b in sev])
 
+    bwd_ms = None
+    if do_bwd:
+        for _ in range(min(args.warmup, 2)):
+            run_bwd()
+        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(max(1, args.steps // 4))]
+        for a, b in bev:
+            a.record(stream)
+            run_bwd()
+            b.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = np.array([a.elapsed_time(b) for a, b in bev])
+
     fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     dec_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
 
@@ -438,6 +473,16 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(s_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(s_tflops / PEAK_BF16_TFLOPS, 4),
                          "traffic": traffic.get("sparse"), "kernel": "fwd_bf16_sp_kernel<128, 2>"},
+        }
+    if do_bwd:
+        b_tflops = bwd_flops / (bwd_ms.mean() * 1e-3) / 1e12
+        result["backward"] = {
+            "workload": f"backward of {bcfg.name}", "algorithmic_flops": bwd_flops,
+            "value": round(b_tflops, 2), "unit": "TFLOP/s",
+            "avg_call_ms": round(float(bwd_ms.mean()), 5), "calls": int(bwd_ms.size),
+            "roofline": {"bound": "mfma", "achieved": round(b_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(b_tflops / PEAK_BF16_TFLOPS, 4),
+                         "kernels": "bwd_prep_kernel, bwd_dkdv_kernel, bwd_dq_kernel"},
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(fx, fcfg, args.cpu_heads)
