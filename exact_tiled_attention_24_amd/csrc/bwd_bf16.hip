@@ -14,6 +14,8 @@
 //    query head of the KV group, accumulating dV^T and dK^T.
 //  * bwd_dq: one workgroup per (128-query block, query head); each wave keeps its 32 queries'
 //    Q and dO in registers and walks the key chunks (32 rows of K and V in LDS).
+// Chunks are double-buffered: the next chunk's global loads go to registers before the current
+// chunk's products and to the other LDS buffer after them, with one barrier per chunk.
 // All products use v_mfma_f32_32x32x16_bf16. As in the forward kernel, the score tile is
 // computed with the rows of its A operand read in an order that swaps bits 2 and 3 of the row
 // index, so that the accumulator, rounded to bf16, is directly the B operand of the next
@@ -48,18 +50,33 @@ struct Stage {
     static constexpr int kTile = kChunk * kRow;
 };
 
-// A chunk of 32 rows x D bf16 from global memory (rows past n read as zero) into LDS at dst,
-// padded rows; all 256 threads take part.
+// A chunk of 32 rows x D bf16 travels global memory -> registers -> LDS (padded rows); the
+// registers let the next chunk's loads fly while the current chunk is computed. Thread i
+// holds the 16-byte pieces i, i + 256, ... of the chunk; rows past n read as zero.
 template <int D>
-__device__ __forceinline__ void stage_rows(unsigned char* dst, const uint16_t* src, int row0, int n) {
-    constexpr int kPer = D * 2 / 16;  // 16-byte pieces per row
-    for (int i = threadIdx.x; i < kChunk * kPer; i += kThreads) {
-        const int r = i / kPer, c = i - r * kPer;
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (row0 + r < n) v = *reinterpret_cast<const u32x4*>(src + (size_t)(row0 + r) * D + 8 * c);
-        *reinterpret_cast<u32x4*>(dst + r * Stage<D>::kRow + 16 * c) = v;
+struct ChunkRegs {
+    static constexpr int kPer = D * 2 / 16;  // 16-byte pieces per row
+    static constexpr int kPieces = kChunk * kPer / kThreads;
+    static_assert(kChunk * kPer % kThreads == 0, "whole pieces per thread");
+    u32x4 v[kPieces];
+    __device__ __forceinline__ void load(const uint16_t* src, int row0, int n) {
+#pragma unroll
+        for (int p = 0; p < kPieces; ++p) {
+            const int i = threadIdx.x + kThreads * p;
+            const int r = i / kPer, c = i - r * kPer;
+            v[p] = u32x4{0u, 0u, 0u, 0u};
+            if (row0 + r < n) v[p] = *reinterpret_cast<const u32x4*>(src + (size_t)(row0 + r) * D + 8 * c);
+        }
     }
-}
+    __device__ __forceinline__ void store(unsigned char* dst) const {
+#pragma unroll
+        for (int p = 0; p < kPieces; ++p) {
+            const int i = threadIdx.x + kThreads * p;
+            const int r = i / kPer, c = i - r * kPer;
+            *reinterpret_cast<u32x4*>(dst + r * Stage<D>::kRow + 16 * c) = v[p];
+        }
+    }
+};
 
 // A operand of a 32 x 16 slice (K-dim chunk kk) of a staged tile, rows in kappa order.
 template <int D>
@@ -142,13 +159,9 @@ struct BwdArgs {
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
     using S = Stage<D>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * S::kTile + 2 * kChunk * 4];
-    unsigned char* const t_q = smem;
-    unsigned char* const t_do = smem + S::kTile;
-    float* const s_l = reinterpret_cast<float*>(smem + 2 * S::kTile);
-    float* const s_d = s_l + kChunk;
-    lds_cptr const lq = (lds_cptr)t_q;
-    lds_cptr const ldo = (lds_cptr)t_do;
+    // two buffers, each: Q chunk, dO chunk, L and D of its 32 queries
+    constexpr int kBuf = 2 * S::kTile + 2 * kChunk * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kBuf];
 
     const int N = a.N, G = a.Hq / a.Hkv;
     const int bk = blockIdx.y;  // b * Hkv + kvh
@@ -173,49 +186,82 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) acc_dk[i] = acc_dv[i] = f32x16{};
 
-    // causal: queries before the block's first key see none of its keys
+    // causal: queries before the block's first key see none of its keys. The chunks of all
+    // query heads of the KV group form one sequence it = 0 .. G * nch - 1.
     const int q_first = a.causal ? (kb0 / kChunk) * kChunk : 0;
-    for (int g = 0; g < G; ++g) {
-        const int hq = kvh * G + g;
-        const size_t qoff = ((size_t)b * a.Hq + hq) * N;
-        for (int qc0 = q_first; qc0 < N; qc0 += kChunk) {
-            __syncthreads();  // the previous chunk's tiles are no longer read
-            stage_rows<D>(t_q, a.q + qoff * D, qc0, N);
-            stage_rows<D>(t_do, a.dout + qoff * D, qc0, N);
-            if (threadIdx.x < kChunk) {
-                const int qi = qc0 + threadIdx.x;
-                s_l[threadIdx.x] = qi < N ? a.lse2[qoff + qi] : INFINITY;
-                s_d[threadIdx.x] = qi < N ? a.dsum[qoff + qi] : 0.f;
-            }
-            __syncthreads();
+    const int nch = (N - q_first + kChunk - 1) / kChunk;
+    const int total = G * nch;
+    ChunkRegs<D> rq, rdo;
+    float rl = INFINITY, rd = 0.f;
+    auto chunk_rows = [&](int it, size_t& qoff) {  // first query row; qoff = head's row base
+        const int g = it / nch;
+        qoff = ((size_t)b * a.Hq + kvh * G + g) * N;
+        return q_first + (it - g * nch) * kChunk;
+    };
+    auto load_chunk = [&](int it) {
+        size_t qoff;
+        const int qc0 = chunk_rows(it, qoff);
+        rq.load(a.q + qoff * D, qc0, N);
+        rdo.load(a.dout + qoff * D, qc0, N);
+        if (threadIdx.x < kChunk) {
+            const int qi = qc0 + threadIdx.x;
+            rl = qi < N ? a.lse2[qoff + qi] : INFINITY;
+            rd = qi < N ? a.dsum[qoff + qi] : 0.f;
+        }
+    };
+    auto store_chunk = [&](int buf) {
+        unsigned char* base = smem + buf * kBuf;
+        rq.store(base);
+        rdo.store(base + S::kTile);
+        if (threadIdx.x < kChunk) {
+            reinterpret_cast<float*>(base + 2 * S::kTile)[threadIdx.x] = rl;
+            reinterpret_cast<float*>(base + 2 * S::kTile)[kChunk + threadIdx.x] = rd;
+        }
+    };
+    if (total > 0) {
+        load_chunk(0);
+        store_chunk(0);
+    }
+    __syncthreads();
+    for (int it = 0; it < total; ++it) {
+        if (it + 1 < total) load_chunk(it + 1);  // in flight during this chunk's products
+        size_t qoff_unused;
+        const int qc0 = chunk_rows(it, qoff_unused);
+        const unsigned char* base = smem + (it & 1) * kBuf;
+        lds_cptr const lq = (lds_cptr)base;
+        lds_cptr const ldo = (lds_cptr)(base + S::kTile);
+        const float* s_l = reinterpret_cast<const float*>(base + 2 * S::kTile);
+        const float* s_d = s_l + kChunk;
 
-            // S = Q K^T and dP = dO V^T for the chunk's 32 queries x the wave's 32 keys
-            f32x16 sc = f32x16{}, dp = f32x16{};
+        // S = Q K^T and dP = dO V^T for the chunk's 32 queries x the wave's 32 keys
+        f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                sc = mfma_32x32x16(rows_frag<D>(lq, lane, kk), kf[kk], sc);
-                dp = mfma_32x32x16(rows_frag<D>(ldo, lane, kk), vf[kk], dp);
-            }
-            float p[16], ds[16];
+        for (int kk = 0; kk < D / 16; ++kk) {
+            sc = mfma_32x32x16(rows_frag<D>(lq, lane, kk), kf[kk], sc);
+            dp = mfma_32x32x16(rows_frag<D>(ldo, lane, kk), vf[kk], dp);
+        }
+        float p[16], ds[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qr = acc_row(r, h);
-                const int qi = qc0 + qr;
-                const bool ok = key < N && qi < N && (!a.causal || key <= qi);
-                p[r] = ok ? exp2_hw(__builtin_fmaf(sc[r], a.scale_log2, -s_l[qr])) : 0.f;
-                ds[r] = p[r] * (dp[r] - s_d[qr]);
-            }
-            // dV^T += dO^T P and dK^T += Q^T dS (K-dim = the chunk's queries)
+        for (int r = 0; r < 16; ++r) {
+            const int qr = acc_row(r, h);
+            const int qi = qc0 + qr;
+            const bool ok = key < N && qi < N && (!a.causal || key <= qi);
+            p[r] = ok ? exp2_hw(__builtin_fmaf(sc[r], a.scale_log2, -s_l[qr])) : 0.f;
+            ds[r] = p[r] * (dp[r] - s_d[qr]);
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS (K-dim = the chunk's queries)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const bf16x8 pb = acc_operand(p, t), sb = acc_operand(ds, t);
+        for (int t = 0; t < 2; ++t) {
+            const bf16x8 pb = acc_operand(p, t), sb = acc_operand(ds, t);
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    acc_dv[db] = mfma_32x32x16(trans_frag<D>(ldo, lane, t, db), pb, acc_dv[db]);
-                    acc_dk[db] = mfma_32x32x16(trans_frag<D>(lq, lane, t, db), sb, acc_dk[db]);
-                }
+            for (int db = 0; db < D / 32; ++db) {
+                acc_dv[db] = mfma_32x32x16(trans_frag<D>(ldo, lane, t, db), pb, acc_dv[db]);
+                acc_dk[db] = mfma_32x32x16(trans_frag<D>(lq, lane, t, db), sb, acc_dk[db]);
             }
         }
+        // the other buffer was last read before the previous barrier
+        if (it + 1 < total) store_chunk((it + 1) & 1);
+        __syncthreads();
     }
     // accumulator register r of block db: head dimension 32 db + 8 (r / 4) + 4 h + r % 4
     if (key < N) {
@@ -240,11 +286,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
     using S = Stage<D>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * S::kTile];
-    unsigned char* const t_k = smem;
-    unsigned char* const t_v = smem + S::kTile;
-    lds_cptr const lk = (lds_cptr)t_k;
-    lds_cptr const lv = (lds_cptr)t_v;
+    // two buffers, each: K chunk, V chunk
+    __shared__ __attribute__((aligned(16))) unsigned char smem[4 * S::kTile];
 
     const int N = a.N, G = a.Hq / a.Hkv;
     const int bh = blockIdx.y;  // b * Hq + hq
@@ -273,11 +316,26 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
     for (int i = 0; i < D / 32; ++i) acc_dq[i] = f32x16{};
 
     const int k_end = a.causal ? min_(N, qb0 + kBlock) : N;  // keys past the block's last query
-    for (int kc0 = 0; kc0 < k_end; kc0 += kChunk) {
-        __syncthreads();
-        stage_rows<D>(t_k, a.k + kvoff, kc0, N);
-        stage_rows<D>(t_v, a.v + kvoff, kc0, N);
-        __syncthreads();
+    const int total = (k_end + kChunk - 1) / kChunk;
+    ChunkRegs<D> rk, rv;
+    auto load_chunk = [&](int it) {
+        rk.load(a.k + kvoff, it * kChunk, N);
+        rv.load(a.v + kvoff, it * kChunk, N);
+    };
+    auto store_chunk = [&](int buf) {
+        rk.store(smem + 2 * buf * S::kTile);
+        rv.store(smem + (2 * buf + 1) * S::kTile);
+    };
+    if (total > 0) {
+        load_chunk(0);
+        store_chunk(0);
+    }
+    __syncthreads();
+    for (int it = 0; it < total; ++it) {
+        if (it + 1 < total) load_chunk(it + 1);  // in flight during this chunk's products
+        const int kc0 = it * kChunk;
+        lds_cptr const lk = (lds_cptr)(smem + 2 * (it & 1) * S::kTile);
+        lds_cptr const lv = (lds_cptr)(smem + (2 * (it & 1) + 1) * S::kTile);
 
         // S^T = K Q^T and dP^T = V dO^T: the chunk's 32 keys x the wave's 32 queries
         f32x16 sc = f32x16{}, dp = f32x16{};
@@ -302,6 +360,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
             for (int db = 0; db < D / 32; ++db)
                 acc_dq[db] = mfma_32x32x16(trans_frag<D>(lk, lane, t, db), sb, acc_dq[db]);
         }
+        if (it + 1 < total) store_chunk((it + 1) & 1);
+        __syncthreads();
     }
     if (query < N) {
         uint16_t* pq = a.dq + (qoff + query) * D;
