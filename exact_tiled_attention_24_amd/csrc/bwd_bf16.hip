@@ -10,8 +10,8 @@
 //  * bwd_prep: D_i and the log2-domain normaliser L_i = (m_i + ln l_i) log2 e of every query
 //    row, so that P = exp2(scale log2e q.k - L) (L = +inf for a row with no key: P = 0).
 //  * bwd_dkdv: one workgroup per (128-key block, KV head); each wave keeps its 32 keys' K and V
-//    in registers and walks the query chunks (32 rows of Q and dO staged in LDS) of every
-//    query head of the KV group, accumulating dV^T and dK^T.
+//    in registers and walks the query chunks (64 rows of Q and dO staged in LDS, computed as
+//    two 32-row sub-chunks) of every query head of the KV group, accumulating dV^T and dK^T.
 //  * bwd_dq: one workgroup per (128-query block, query head); each wave keeps its 32 queries'
 //    Q and dO in registers and walks the key chunks (32 rows of K and V in LDS).
 // Chunks are double-buffered: the next chunk's global loads go to registers before the current
@@ -28,7 +28,9 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;  // 4 waves
-constexpr int kChunk = 32;     // rows of a staged chunk
+// 32-row sub-chunks per staged chunk: two for dK/dV (their products interleave), one for dQ
+// (two would cost it its second wave per SIMD)
+constexpr int kSubKV = 2, kSubQ = 1;
 constexpr int kBlock = 128;    // keys (dK/dV) or queries (dQ) per workgroup: 32 per wave
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -44,8 +46,9 @@ __device__ __forceinline__ int kappa(int m) {
 // read in kappa order: registers 0-7 hold rows 8h .. 8h + 7, registers 8-15 rows 16 + 8h ..
 __device__ __forceinline__ int acc_row(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
 
-template <int D>
+template <int D, int SUB>
 struct Stage {
+    static constexpr int kChunk = 32 * SUB;  // rows of a staged chunk
     static constexpr int kRow = D * 2 + 16;  // padded row, bytes
     static constexpr int kTile = kChunk * kRow;
 };
@@ -53,8 +56,9 @@ struct Stage {
 // A chunk of 32 rows x D bf16 travels global memory -> registers -> LDS (padded rows); the
 // registers let the next chunk's loads fly while the current chunk is computed. Thread i
 // holds the 16-byte pieces i, i + 256, ... of the chunk; rows past n read as zero.
-template <int D>
+template <int D, int SUB>
 struct ChunkRegs {
+    static constexpr int kChunk = Stage<D, SUB>::kChunk;
     static constexpr int kPer = D * 2 / 16;  // 16-byte pieces per row
     static constexpr int kPieces = kChunk * kPer / kThreads;
     static_assert(kChunk * kPer % kThreads == 0, "whole pieces per thread");
@@ -73,7 +77,7 @@ struct ChunkRegs {
         for (int p = 0; p < kPieces; ++p) {
             const int i = threadIdx.x + kThreads * p;
             const int r = i / kPer, c = i - r * kPer;
-            *reinterpret_cast<u32x4*>(dst + r * Stage<D>::kRow + 16 * c) = v[p];
+            *reinterpret_cast<u32x4*>(dst + r * Stage<D, SUB>::kRow + 16 * c) = v[p];
         }
     }
 };
@@ -81,7 +85,7 @@ struct ChunkRegs {
 // A operand of a 32 x 16 slice (K-dim chunk kk) of a staged tile, rows in kappa order.
 template <int D>
 __device__ __forceinline__ bf16x8 rows_frag(lds_cptr tile, int lane, int kk) {
-    return *reinterpret_cast<const lds_bf16x8*>(tile + kappa(lane & 31) * Stage<D>::kRow + 32 * kk +
+    return *reinterpret_cast<const lds_bf16x8*>(tile + kappa(lane & 31) * Stage<D, 1>::kRow + 32 * kk +
                                                  16 * (lane >> 5));
 }
 
@@ -90,7 +94,7 @@ __device__ __forceinline__ bf16x8 rows_frag(lds_cptr tile, int lane, int kk) {
 // a lane its 8 consecutive rows of one head dimension.
 template <int D>
 __device__ __forceinline__ bf16x8 trans_frag(lds_cptr tile, int lane, int t, int db) {
-    constexpr int R = Stage<D>::kRow;
+    constexpr int R = Stage<D, 1>::kRow;
     const lds_cptr p = tile + (8 * (lane >> 5) + ((lane & 15) >> 2)) * R +
                        (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2 + 16 * t * R + 64 * db;
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
@@ -158,7 +162,9 @@ struct BwdArgs {
 // ---- dK, dV: workgroup = 128 keys of one KV head; wave = 32 keys ----
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
-    using S = Stage<D>;
+    constexpr int kSub = kSubKV;
+    using S = Stage<D, kSub>;
+    constexpr int kChunk = S::kChunk;
     // two buffers, each: Q chunk, dO chunk, L and D of its 32 queries
     constexpr int kBuf = 2 * S::kTile + 2 * kChunk * 4;
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kBuf];
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
     const int q_first = a.causal ? (kb0 / kChunk) * kChunk : 0;
     const int nch = (N - q_first + kChunk - 1) / kChunk;
     const int total = G * nch;
-    ChunkRegs<D> rq, rdo;
+    ChunkRegs<D, kSub> rq, rdo;
     float rl = INFINITY, rd = 0.f;
     auto chunk_rows = [&](int it, size_t& qoff) {  // first query row; qoff = head's row base
         const int g = it / nch;
@@ -233,30 +239,42 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
         const float* s_l = reinterpret_cast<const float*>(base + 2 * S::kTile);
         const float* s_d = s_l + kChunk;
 
-        // S = Q K^T and dP = dO V^T for the chunk's 32 queries x the wave's 32 keys
-        f32x16 sc = f32x16{}, dp = f32x16{};
+        // S = Q K^T and dP = dO V^T for each 32-query sub-chunk x the wave's 32 keys; the
+        // sub-chunks are independent until the accumulations, so their matrix and vector work
+        // can interleave
+        f32x16 sc[kSub], dp[kSub];
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            sc = mfma_32x32x16(rows_frag<D>(lq, lane, kk), kf[kk], sc);
-            dp = mfma_32x32x16(rows_frag<D>(ldo, lane, kk), vf[kk], dp);
+        for (int u = 0; u < kSub; ++u) {
+            sc[u] = f32x16{};
+            dp[u] = f32x16{};
+            const lds_cptr tq = lq + 32 * u * S::kRow, tdo = ldo + 32 * u * S::kRow;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                sc[u] = mfma_32x32x16(rows_frag<D>(tq, lane, kk), kf[kk], sc[u]);
+                dp[u] = mfma_32x32x16(rows_frag<D>(tdo, lane, kk), vf[kk], dp[u]);
+            }
         }
-        float p[16], ds[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int qr = acc_row(r, h);
-            const int qi = qc0 + qr;
-            const bool ok = key < N && qi < N && (!a.causal || key <= qi);
-            p[r] = ok ? exp2_hw(__builtin_fmaf(sc[r], a.scale_log2, -s_l[qr])) : 0.f;
-            ds[r] = p[r] * (dp[r] - s_d[qr]);
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS (K-dim = the chunk's queries)
+        for (int u = 0; u < kSub; ++u) {
+            float p[16], ds[16];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const bf16x8 pb = acc_operand(p, t), sb = acc_operand(ds, t);
+            for (int r = 0; r < 16; ++r) {
+                const int qr = 32 * u + acc_row(r, h);
+                const int qi = qc0 + qr;
+                const bool ok = key < N && qi < N && (!a.causal || key <= qi);
+                p[r] = ok ? exp2_hw(__builtin_fmaf(sc[u][r], a.scale_log2, -s_l[qr])) : 0.f;
+                ds[r] = p[r] * (dp[u][r] - s_d[qr]);
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS (K-dim = the sub-chunk's queries)
+            const lds_cptr tq = lq + 32 * u * S::kRow, tdo = ldo + 32 * u * S::kRow;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                acc_dv[db] = mfma_32x32x16(trans_frag<D>(ldo, lane, t, db), pb, acc_dv[db]);
-                acc_dk[db] = mfma_32x32x16(trans_frag<D>(lq, lane, t, db), sb, acc_dk[db]);
+            for (int t = 0; t < 2; ++t) {
+                const bf16x8 pb = acc_operand(p, t), sb = acc_operand(ds, t);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    acc_dv[db] = mfma_32x32x16(trans_frag<D>(tdo, lane, t, db), pb, acc_dv[db]);
+                    acc_dk[db] = mfma_32x32x16(trans_frag<D>(tq, lane, t, db), sb, acc_dk[db]);
+                }
             }
         }
         // the other buffer was last read before the previous barrier
@@ -285,7 +303,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
 // ---- dQ: workgroup = 128 queries of one query head; wave = 32 queries ----
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
-    using S = Stage<D>;
+    constexpr int kSub = kSubQ;
+    using S = Stage<D, kSub>;
+    constexpr int kChunk = S::kChunk;
     // two buffers, each: K chunk, V chunk
     __shared__ __attribute__((aligned(16))) unsigned char smem[4 * S::kTile];
 
@@ -317,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
 
     const int k_end = a.causal ? min_(N, qb0 + kBlock) : N;  // keys past the block's last query
     const int total = (k_end + kChunk - 1) / kChunk;
-    ChunkRegs<D> rk, rv;
+    ChunkRegs<D, kSub> rk, rv;
     auto load_chunk = [&](int it) {
         rk.load(a.k + kvoff, it * kChunk, N);
         rv.load(a.v + kvoff, it * kChunk, N);
@@ -337,28 +357,38 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
         lds_cptr const lk = (lds_cptr)(smem + 2 * (it & 1) * S::kTile);
         lds_cptr const lv = (lds_cptr)(smem + (2 * (it & 1) + 1) * S::kTile);
 
-        // S^T = K Q^T and dP^T = V dO^T: the chunk's 32 keys x the wave's 32 queries
-        f32x16 sc = f32x16{}, dp = f32x16{};
+        // S^T = K Q^T and dP^T = V dO^T: each 32-key sub-chunk x the wave's 32 queries
+        f32x16 sc[kSub], dp[kSub];
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            sc = mfma_32x32x16(rows_frag<D>(lk, lane, kk), qf[kk], sc);
-            dp = mfma_32x32x16(rows_frag<D>(lv, lane, kk), dof[kk], dp);
+        for (int u = 0; u < kSub; ++u) {
+            sc[u] = f32x16{};
+            dp[u] = f32x16{};
+            const lds_cptr tk = lk + 32 * u * S::kRow, tv = lv + 32 * u * S::kRow;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                sc[u] = mfma_32x32x16(rows_frag<D>(tk, lane, kk), qf[kk], sc[u]);
+                dp[u] = mfma_32x32x16(rows_frag<D>(tv, lane, kk), dof[kk], dp[u]);
+            }
         }
-        float ds[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int kj = kc0 + acc_row(r, h);
-            const bool ok = kj < N && query < N && (!a.causal || kj <= query);
-            const float p = ok ? exp2_hw(__builtin_fmaf(sc[r], a.scale_log2, -lse)) : 0.f;
-            ds[r] = p * (dp[r] - dsum);
-        }
-        // dQ^T += K^T dS^T (K-dim = the chunk's keys)
+        for (int u = 0; u < kSub; ++u) {
+            float ds[16];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const bf16x8 sb = acc_operand(ds, t);
+            for (int r = 0; r < 16; ++r) {
+                const int kj = kc0 + 32 * u + acc_row(r, h);
+                const bool ok = kj < N && query < N && (!a.causal || kj <= query);
+                const float p = ok ? exp2_hw(__builtin_fmaf(sc[u][r], a.scale_log2, -lse)) : 0.f;
+                ds[r] = p * (dp[u][r] - dsum);
+            }
+            // dQ^T += K^T dS^T (K-dim = the sub-chunk's keys)
+            const lds_cptr tk = lk + 32 * u * S::kRow;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-                acc_dq[db] = mfma_32x32x16(trans_frag<D>(lk, lane, t, db), sb, acc_dq[db]);
+            for (int t = 0; t < 2; ++t) {
+                const bf16x8 sb = acc_operand(ds, t);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+                    acc_dq[db] = mfma_32x32x16(trans_frag<D>(tk, lane, t, db), sb, acc_dq[db]);
+            }
         }
         if (it + 1 < total) store_chunk((it + 1) & 1);
         __syncthreads();
