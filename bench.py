@@ -484,6 +484,11 @@ def main():
                          "unit": "TFLOP/s", "frac": round(b_tflops / PEAK_BF16_TFLOPS, 4),
                          "kernels": "bwd_prep_kernel, bwd_dkdv_kernel, bwd_dq_kernel"},
         }
+    try:  # the counter evidence behind the tile and split choices (from the sweeps)
+        with open(os.path.join(ROOT, "profiles", "choices.json")) as f:
+            result["choices"] = json.load(f)
+    except (OSError, ValueError):
+        result["choices"] = None
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(fx, fcfg, args.cpu_heads)
     print(json.dumps(result), flush=True)
