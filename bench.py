@@ -30,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attn fwd TFLOP/s & % MFMA peak; decode HBM GB/s & % peak (1×MI355X)"
+PEAK_FP8_TFLOPS = 5000.0  # dense fp8 MFMA, MI355X public figure
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 
@@ -50,7 +51,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=64,
                     help="heads of the forward workload the oracle is timed on")
-    ap.add_argument("--only", choices=["fwd", "decode", "paged", "sparse", "bwd"], default=None,
+    ap.add_argument("--only", choices=["fwd", "decode", "paged", "sparse", "bwd", "fp8"], default=None,
                     help="time one kernel only (profiling runs)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling)")
@@ -217,6 +218,7 @@ def main():
     do_paged = args.only in (None, "paged")
     do_sparse = args.only in (None, "sparse")
     do_bwd = args.only in (None, "bwd")
+    do_fp8 = args.only in (None, "fp8")
 
     # ---- inputs, resident in HBM ----
     fcfg = gen.CONFIGS[args.fwd_config]
@@ -301,6 +303,22 @@ def main():
         bwd_scale = bx.scale
         del bx
 
+    fp8_flops = None
+    if do_fp8:
+        # the forward workload with e4m3 Q and K (the same draws, a different rounding)
+        f8cfg = gen.CONFIGS[args.fwd_config]
+        f8x = gen.fp8_fwd_inputs(f8cfg.B, f8cfg.Hq, f8cfg.Hkv, f8cfg.N, f8cfg.d, f8cfg.seed,
+                                 causal=f8cfg.causal, k_mult=f8cfg.k_mult)
+        f8_q, f8_k = gen.to_torch(f8x.q, "e4m3", dev), gen.to_torch(f8x.k, "e4m3", dev)
+        f8_v = gen.to_torch(f8x.v, "bf16", dev)
+        f8_o = torch.empty(f8x.q.shape, dtype=torch.bfloat16, device=dev)
+        fp8_flops = f8cfg.flops()
+        fp8_scale = f8x.scale
+        del f8x
+
+    def run_fp8():
+        fa.fa_fwd_fp8(f8_q, f8_k, f8_v, scale=fp8_scale, causal=f8cfg.causal, out=f8_o)
+
     def run_bwd():
         fa.fa_bwd(b_q, b_k, b_v, b_o, b_do, b_m, b_l, scale=bwd_scale, causal=bcfg.causal,
                   workspace=b_ws)
@@ -382,6 +400,19 @@ def main():
             b.record(stream)
         torch.cuda.synchronize()
         sparse_ms = np.array([a.elapsed_time(b) for a, b in sev])
+
+    fp8_ms = None
+    if do_fp8:
+        for _ in range(args.warmup):
+            run_fp8()
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in fev:
+            a.record(stream)
+            run_fp8()
+            b.record(stream)
+        torch.cuda.synchronize()
+        fp8_ms = np.array([a.elapsed_time(b) for a, b in fev])
 
     bwd_ms = None
     if do_bwd:
@@ -473,6 +504,20 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(s_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(s_tflops / PEAK_BF16_TFLOPS, 4),
                          "traffic": traffic.get("sparse"), "kernel": "fwd_bf16_sp_kernel<128, 2>"},
+        }
+    if do_fp8:
+        f_tflops = fp8_flops / (fp8_ms.mean() * 1e-3) / 1e12
+        # half the work (S = Q K^T) on the fp8 matrix cores, half (P V) on the bf16 ones
+        mixed_peak = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
+        result["fp8_qk"] = {
+            "workload": f"{f8cfg.name} with e4m3 Q and K", "algorithmic_flops": fp8_flops,
+            "value": round(f_tflops, 2), "unit": "TFLOP/s",
+            "avg_call_ms": round(float(fp8_ms.mean()), 5),
+            "roofline": {"bound": "mfma", "achieved": round(f_tflops, 2),
+                         "peak": round(mixed_peak, 1), "unit": "TFLOP/s",
+                         "frac": round(f_tflops / mixed_peak, 4),
+                         "peak_note": "S on fp8 (5.0 PFLOP/s), P V on bf16 (2.5 PFLOP/s)",
+                         "kernel": "fwd_bf16_sp_kernel<128, 3>"},
         }
     if do_bwd:
         b_tflops = bwd_flops / (bwd_ms.mean() * 1e-3) / 1e12

@@ -174,6 +174,24 @@ fa_status fa_decode_splitk(fa_dtype dt, const void* q, const void* k_cache, cons
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* m_out,
+                     float* l_out, int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                     void* stream) {
+    if (B < 0 || Hq < 0 || Hkv < 0 || N < 0) return FA_ERR_INVALID_ARGUMENT;
+    if (!scale_ok(scale)) return FA_ERR_INVALID_ARGUMENT;
+    if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0)) return FA_ERR_INVALID_ARGUMENT;
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || Hq == 0 || N == 0) return FA_OK;
+    if (!q || !k || !v || !o) return FA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return FA_ERR_INVALID_ARGUMENT;
+    if ((long long)N * d * 2 >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    if (((long long)N + 255) / 256 * B * Hq >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    const hipError_t e = fa::launch_fwd_fp8qk_sp(q, k, v, o, m_out, l_out, B, Hq, Hkv, N, d, scale,
+                                                 causal ? 1 : 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Hq, int N) {
     if (B < 0 || Hq < 0 || N < 0) return 0;
     return 2 * (size_t)B * (size_t)Hq * (size_t)N * sizeof(float);

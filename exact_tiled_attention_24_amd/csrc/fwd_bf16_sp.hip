@@ -94,11 +94,15 @@ __device__ __forceinline__ void barrier_lds() {
 }
 
 constexpr int kPageTok = 16;      // tokens per page of the paged cache
-constexpr int kModeDense = 0, kModePaged = 1, kModeSparse = 2;
+constexpr int kModeDense = 0, kModePaged = 1, kModeSparse = 2, kModeFp8 = 3;
+typedef int v8i32 __attribute__((ext_vector_type(8)));
 
-template <int D, bool kPaged>
+template <int D, bool kPaged, bool kFp8 = false>
 struct Tile {
-    static constexpr int kKRow = D * 2 + 16;                          // padded K row, bytes
+    // K element bytes (fp8 e4m3 K: 1); the 16 B pad keeps a 16 B read of 16 rows in 16
+    // distinct bank groups for both row lengths
+    static constexpr int kKElem = kFp8 ? 1 : 2;
+    static constexpr int kKRow = D * kKElem + 16;                     // padded K row, bytes
     // padded V row, bytes: the 64 B pad puts the four rows a transposing read touches per
     // cycle in four different 64 B bank windows
     static constexpr int kVRow = D * 2 + 64;
@@ -143,7 +147,9 @@ struct FwdArgs {
 template <int D, int kMode>
 __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned char* smem) {
     constexpr bool kPaged = kMode == kModePaged, kSparse = kMode == kModeSparse;
-    using T = Tile<D, kPaged>;
+    constexpr bool kFp8 = kMode == kModeFp8;
+    using T = Tile<D, kPaged, kFp8>;
+    constexpr int kKTile = kBc * D * T::kKElem, kVTile = kBc * D * 2;  // HBM bytes of a tile
     const uint16_t* __restrict__ q = a.q;
     const uint16_t* __restrict__ k = a.k;
     const uint16_t* __restrict__ v = a.v;
@@ -168,7 +174,8 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     const size_t qoff = ((size_t)(b * Hq + h) * N) * D;
     const size_t koff = kPaged ? 0 : ((size_t)(b * Hkv + kvh) * N) * D;
     const uint16_t* qh = q + qoff;
-    const uint16_t* kh = k + koff;
+    // (K addressed in bytes: fp8 K has one byte per element)
+    const unsigned char* kh = reinterpret_cast<const unsigned char*>(k) + koff * T::kKElem;
     const uint16_t* vh = v + koff;
     // Keys of this item's sequence and the position offset of its queries: query row i sits
     // at position i + off (dense: the N keys, off = 0; paged: the cached length L, clamped to
@@ -198,15 +205,30 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     const int row0 = qb * kBr + 32 * wave;
     const int qrow = row0 + l32;
 
-    bf16x8 qf[D / 16];
-    {
+    // Q as the B operand of S^T = K Q^T: bf16, 8 head dimensions per 16-wide chunk and lane
+    // half; fp8, 32 per 64-wide chunk (the same split as the K operand, so every head
+    // dimension meets its partner once)
+    bf16x8 qf[kFp8 ? 1 : D / 16];
+    v8i32 qf8[kFp8 ? D / 64 : 1];
+    if constexpr (kFp8) {
+        const unsigned char* src = reinterpret_cast<const unsigned char*>(q) + qoff +
+                                   (size_t)min_(qrow, N - 1) * D + 32 * hh;
+#pragma unroll
+        for (int c = 0; c < D / 64; ++c) {
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(src + 64 * c);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(src + 64 * c + 16);
+            qf8[c] = v8i32{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+#pragma unroll
+        for (int c = 0; c < D / 64; ++c) asm volatile("" : "+v"(qf8[c]));
+    } else {
         const uint16_t* src = qh + (size_t)min_(qrow, N - 1) * D + 8 * hh;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
             qf[kk] = *reinterpret_cast<const bf16x8*>(src + 16 * kk);
-    }
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(qf[kk]));
+        for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(qf[kk]));
+    }
 
     f32x16 acc_o[D / 32];
 #pragma unroll
@@ -253,8 +275,9 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
         } else {
             const int slot = 1024 * cc + 16 * lane;
             const int row = slot / row_b, col = slot - row * row_b;
-            dma_src[i] = (col < D * 2 ? row * D * 2 + col : kPadOffset) +
-                         (kSparse ? 0 : (is_k ? 3 : 2) * kBc * D * 2);
+            const int rb = is_k ? D * T::kKElem : D * 2;  // HBM row bytes
+            dma_src[i] = (col < rb ? row * rb + col : kPadOffset) +
+                         (kSparse ? 0 : (is_k ? 3 * kKTile : 2 * kVTile));
             dma_pg[i] = 0;
         }
     }
@@ -328,9 +351,10 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     const int head_bytes = __builtin_amdgcn_readfirstlane(
         kPaged ? (a.num_pages > 0 ? (a.num_pages - 1) * (int)stride_bytes + kPageTok * D * 2 : 0)
                : row_end * D * 2);
+    const int head_bytes_k = kFp8 ? __builtin_amdgcn_readfirstlane(row_end * D) : head_bytes;
     const size_t kv_page = kPaged ? (size_t)kvh * kPageTok * D : 0;  // KV head within a page
-    const __amdgpu_buffer_rsrc_t rsrc_k =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kh + kv_page), (short)0, head_bytes, kBufferDword3);
+    const __amdgpu_buffer_rsrc_t rsrc_k = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kh + kv_page * 2), (short)0, head_bytes_k, kBufferDword3);
     const __amdgpu_buffer_rsrc_t rsrc_v =
         __builtin_amdgcn_make_buffer_rsrc((void*)(vh + kv_page), (short)0, head_bytes, kBufferDword3);
     // DMA operation i of tile step j (stage phase P = j mod 4): K of tile j + 3 and V of
@@ -371,7 +395,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
             const __amdgpu_buffer_rsrc_t r = is_k ? rsrc_k : rsrc_v;
             asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                          :
-                         : "v"(dma_src[i] + j * (kBc * D * 2)), "s"(r), "{m0}"(dma_dst[i] + stage)
+                         : "v"(dma_src[i] + j * (is_k ? kKTile : kVTile)), "s"(r), "{m0}"(dma_dst[i] + stage)
                          : "memory");
         }
     };
@@ -399,8 +423,9 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     // re-associating the offsets into per-read additions.
     // (paged: row r of a K stage sits in page block r / 16 at row r % 16; kappa keeps bit 4,
     // and the stages need a second base as the V stages do)
+    // (fp8: a lane reads 32 bytes of its row per 64 head dimensions, lane half hh the second 32)
     lds_cptr base_k = kPaged ? lds + (l32 >> 4) * T::kKPage + (kappa(l32) & 15) * T::kKRow + hh * 16
-                             : lds + kappa(l32) * T::kKRow + hh * 16;
+                             : lds + kappa(l32) * T::kKRow + hh * (kFp8 ? 32 : 16);
     lds_cptr base_k2 = base_k + 2 * T::kKStage;
     lds_cptr base_v = lds + T::kVBase + (8 * (lane >> 5) + ((lane & 15) >> 2)) * T::kVRow +
                       (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
@@ -420,14 +445,30 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
         return (st < 2 ? base_v : base_v2) + (st & 1) * T::kVStage + 32 * kb * T::kVRow;
     };
 
+    // fp8 K operand of the 64 head dimensions c of the rows at ks (two 16 B reads)
+    auto kfrag8 = [&](lds_cptr ks, int c) -> v8i32 {
+        typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
+        const u32x4 lo = *reinterpret_cast<lds_u32x4*>(ks + 64 * c);
+        const u32x4 hi = *reinterpret_cast<lds_u32x4*>(ks + 64 * c + 16);
+        return v8i32{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+    // e4m3 x e4m3 -> f32 on the matrix cores (no block scales)
+    auto mfma_fp8 = [&](v8i32 a8, v8i32 b8, f32x16 c) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 0, 0, 0, 0, 0, 0);
+    };
     // S^T = K Q^T of half tile (K stage st, half kb) into s.
     auto compute_s = [&](f32x16& s, int st, int kb) {
         const lds_cptr ks = k_at(st, kb);
         s = f32x16{};
+        if constexpr (kFp8) {
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            const bf16x8 a = *reinterpret_cast<const lds_bf16x8*>(ks + 32 * kk);
-            s = mfma_32x32x16(a, qf[kk], s);
+            for (int c = 0; c < D / 64; ++c) s = mfma_fp8(kfrag8(ks, c), qf8[c], s);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const bf16x8 a = *reinterpret_cast<const lds_bf16x8*>(ks + 32 * kk);
+                s = mfma_32x32x16(a, qf[kk], s);
+            }
         }
     };
     // V^T operand for key group t (16 keys) and head-dimension block db, from the V rows at
@@ -484,14 +525,20 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     // (with_pv false: half tile 0, whose step has no O update; its odd slots stay empty.)
     // with_dma: this step (the first of tile j = hi / 2) also issues the loads of K of tile
     // j + 3 and V of tile j + 2 (one DMA per odd slot).
+    //
+    // fp8 scores (kFp8): 8 slots, each one O MFMA (key group sl / 4, head-dimension block
+    // sl % 4) and two softmax phases; the two fp8 S^T MFMAs (64 head dimensions each, as long
+    // as two bf16 products) sit in slots 0 and 4 with K operands in kq, and the K operands of
+    // the next step (half tile hi+2) replace them in slots 2 and 6. V^T operands are read two
+    // slots ahead (fr[0..1] carries the next step's first two).
     auto step = [&](int hi, int kv_tile, auto h8_c, f32x16& s_cur, f32x16& s_next, const u32x4 (&pk_prev)[2],
-                    u32x4 (&pk_cur)[2], bool masked, bf16x8 (&fr)[kAhead], auto with_pv,
-                    auto with_dma) {
+                    u32x4 (&pk_cur)[2], bool masked, bf16x8 (&fr)[kAhead], v8i32 (&kq)[2],
+                    auto with_pv, auto with_dma) {
         constexpr int H8 = decltype(h8_c)::value;
         constexpr bool kPV = decltype(with_pv)::value;
         constexpr bool kDma = decltype(with_dma)::value;
         constexpr int kS = D / 16;             // S^T MFMAs (one per 16 head dimensions)
-        constexpr int kSlots = 2 * kS;         // as many O MFMAs: 2 key groups x D/32 blocks
+        constexpr int kSlots = kFp8 ? D / 16 : 2 * kS;  // bf16: as many O MFMAs as S^T ones
         constexpr int kPhasesPerSlot = 16 / kSlots;
         static_assert(kAhead <= kSlots, "read-ahead deeper than a step");
 
@@ -560,9 +607,38 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
 
         const Bases b_cur = bases(h8_c), b_next = bases(std::integral_constant<int, (H8 + 1) & 7>{});
         bf16x8 cur[kSlots];
+        s_next = f32x16{};
+        if constexpr (kFp8) {
+            static_assert(D == 128, "fp8 scores: d = 128");
+            constexpr int kA8 = 2;  // V^T operand read-ahead, slots
+            cur[0] = fr[0];
+            cur[1] = fr[1];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int sl = 0; sl < kSlots; ++sl) {
+                if (sl + kA8 < kSlots) {
+                    if (kPV) cur[sl + kA8] = vfrag(b_cur.v, (sl + kA8) >> 2, (sl + kA8) & 3);
+                } else {
+                    fr[sl + kA8 - kSlots] = vfrag(b_next.v, (sl + kA8 - kSlots) >> 2, (sl + kA8 - kSlots) & 3);
+                }
+                if ((sl & 3) == 0) s_next = mfma_fp8(kq[sl >> 2], qf8[sl >> 2], s_next);
+                if ((sl & 3) == 2) kq[sl >> 2] = kfrag8(b_next.k, sl >> 2);
+                if (kPV)
+                    acc_o[sl & 3] = mfma_32x32x16(cur[sl], __builtin_bit_cast(bf16x8, pk_prev[sl >> 2]),
+                                                  acc_o[sl & 3]);
+#pragma unroll
+                for (int ph = sl * kPhasesPerSlot; ph < (sl + 1) * kPhasesPerSlot; ++ph) phase(ph);
+#pragma unroll
+                for (int i = 0; i < T::kDmaPerWave; ++i)
+                    if (sl == 1 + 2 * i && kDma) dma_op(hi >> 1, i, H8 >> 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            asm volatile("" : "+v"(pk_cur[0]), "+v"(pk_cur[1]), "+v"(l_part));
+            rescale(move, alpha);
+            return;
+        }
 #pragma unroll
         for (int sl = 0; sl < kAhead; ++sl) cur[sl] = fr[sl];
-        s_next = f32x16{};
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int sl = 0; sl < kSlots; ++sl) {
@@ -572,7 +648,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
                 fr[sl + kAhead - kSlots] = frag(b_next, sl + kAhead - kSlots);
             }
             if ((sl & 1) == 0) {
-                s_next = mfma_32x32x16(cur[sl], qf[sl >> 1], s_next);
+                s_next = mfma_32x32x16(cur[sl], qf[kFp8 ? 0 : sl >> 1], s_next);
             } else if (kPV) {
                 const int i = sl >> 1;
                 const int t = i / (D / 32), db = i % (D / 32);
@@ -602,6 +678,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     f32x16 sa, sb;
     u32x4 pa[2], pb[2];
     bf16x8 fr[kAhead];
+    v8i32 kq[2] = {};  // fp8: K operands of the coming S^T (unused otherwise)
 
     using Yes = std::true_type;
     using No = std::false_type;
@@ -625,14 +702,22 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     // ---- tile 0: half 0 has no O update yet; its first step issues K3 / V2 ----
     {
         const Bases b0 = bases(std::integral_constant<int, 0>{});
+        if constexpr (kFp8) {
+            // step 0 has no O update; its S^T (half tile 1) takes K from the first stage
 #pragma unroll
-        for (int sl = 0; sl < kAhead; ++sl) fr[sl] = (sl & 1) ? bf16x8{} : frag(b0, sl);
+            for (int sl = 0; sl < kAhead; ++sl) fr[sl] = bf16x8{};
+#pragma unroll
+            for (int c = 0; c < D / 64; ++c) kq[c] = kfrag8(b0.k, c);
+        } else {
+#pragma unroll
+            for (int sl = 0; sl < kAhead; ++sl) fr[sl] = (sl & 1) ? bf16x8{} : frag(b0, sl);
+        }
     }
     advance(3);
     {
         const bool masked0 = kSparse ? kvq0 >= n_plain * kBc : n_plain == 0;
-        step(0, kvq0, std::integral_constant<int, 0>{}, sa, sb, pb, pa, masked0, fr, No{}, Yes{});
-        step(1, kvq0, std::integral_constant<int, 1>{}, sb, sa, pa, pb, masked0, fr, Yes{}, No{});
+        step(0, kvq0, std::integral_constant<int, 0>{}, sa, sb, pb, pa, masked0, fr, kq, No{}, Yes{});
+        step(1, kvq0, std::integral_constant<int, 1>{}, sb, sa, pa, pb, masked0, fr, kq, Yes{}, No{});
     }
     wait_dma_tile();
     barrier_lds();
@@ -647,8 +732,8 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
         constexpr int P = decltype(phase_c)::value;
         advance(j + 3);
         const bool masked = kSparse ? kvq0 >= n_plain * kBc : j >= n_plain;
-        step(2 * j, kvq0, std::integral_constant<int, 2 * P>{}, sa, sb, pb, pa, masked, fr, Yes{}, Yes{});
-        step(2 * j + 1, kvq0, std::integral_constant<int, 2 * P + 1>{}, sb, sa, pa, pb, masked, fr, Yes{}, No{});
+        step(2 * j, kvq0, std::integral_constant<int, 2 * P>{}, sa, sb, pb, pa, masked, fr, kq, Yes{}, Yes{});
+        step(2 * j + 1, kvq0, std::integral_constant<int, 2 * P + 1>{}, sb, sa, pa, pb, masked, fr, kq, Yes{}, No{});
         wait_dma_tile();
         barrier_lds();
     };
@@ -714,7 +799,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
 // workgroup moves to its next item without a new launch.
 template <int D, int kMode>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(FwdArgs a) {
-    using T = Tile<D, kMode == kModePaged>;
+    using T = Tile<D, kMode == kModePaged, kMode == kModeFp8>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * (T::kKStage + T::kVStage)];
     const int per_unit = a.nqb * (a.Hq / a.Hkv);  // items of one KV group
     const int n_kvg = a.B * a.Hkv;
@@ -772,9 +857,11 @@ hipError_t launch_sp(const FwdArgs& a, int d, hipStream_t stream) {
     if (d == 128)
         hipLaunchKernelGGL((fwd_bf16_sp_kernel<128, kMode>), dim3((unsigned)grid), dim3(kThreads), 0,
                            stream, a);
-    else
+    else if constexpr (kMode != kModeFp8)
         hipLaunchKernelGGL((fwd_bf16_sp_kernel<64, kMode>), dim3((unsigned)grid), dim3(kThreads), 0,
                            stream, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 }  // namespace
@@ -817,6 +904,23 @@ hipError_t launch_fwd_bf16_sp_paged(const void* q, const void* k_cache, const vo
     a.max_pages = max_pages_per_seq;
     a.num_pages = num_pages;
     return launch_sp<kModePaged>(a, d, stream);
+}
+
+hipError_t launch_fwd_fp8qk_sp(const void* q, const void* k, const void* v, void* o, float* m_out,
+                               float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
+                               int causal, hipStream_t stream) {
+    FwdArgs a{};
+    a.q = static_cast<const uint16_t*>(q);  // e4m3 bytes, addressed as such in the kernel
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.o = static_cast<uint16_t*>(o);
+    a.m_out = m_out;
+    a.l_out = l_out;
+    a.B = B, a.Hq = Hq, a.Hkv = Hkv, a.N = N;
+    a.scale_log2 = scale * kLog2e;
+    a.causal = causal;
+    a.nqb = (N + kBr - 1) / kBr;
+    return launch_sp<kModeFp8>(a, d, stream);
 }
 
 hipError_t launch_fwd_bf16_sp_block_sparse(const void* q, const void* k, const void* v, void* o,

@@ -102,6 +102,33 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return rounded.view(np.float32)
 
 
+def round_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest OCP fp8 e4m3 value (ties to even; 3 mantissa bits,
+    exponent bias 7, subnormals below 2^-6 in steps of 2^-9, largest finite 448; larger
+    magnitudes saturate to +-448). Returns float32 values that are e4m3-exact."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)                     # subnormal range shares the 2^-9 step
+    step = np.exp2(e - 3.0)
+    r = np.round(a / step) * step               # numpy rounds halves to even
+    r = np.minimum(r, 448.0)
+    return (np.sign(x) * r).astype(np.float32)
+
+
+def e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """The uint8 e4m3 encodings of float32 values that are already e4m3-exact."""
+    x = np.asarray(x, dtype=np.float64)
+    sign = (np.signbit(x)).astype(np.uint8) << 7
+    a = np.abs(x)
+    normal = a >= 2.0 ** -6
+    e = np.floor(np.log2(np.where(normal, a, 1.0))).astype(np.int64)
+    mant_n = np.round((a / np.exp2(e) - 1.0) * 8).astype(np.int64)
+    code_n = ((e + 7) << 3) | mant_n
+    code_s = np.round(a / 2.0 ** -9).astype(np.int64)
+    return (sign | np.where(normal, code_n, code_s).astype(np.uint8)).astype(np.uint8)
+
+
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """The uint16 bfloat16 encodings of float32 values that are already bf16-exact."""
     bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
@@ -372,10 +399,35 @@ BLOCK_SPARSE = BlockSparseConfig(
     2, 32, 8, 16384, 128, 2048, 4, True, 7)
 
 
+@dataclass
+class Fp8Inputs:
+    q: np.ndarray  # [B, Hq, N, d] float32, e4m3-exact
+    k: np.ndarray  # [B, Hkv, N, d] float32, e4m3-exact
+    v: np.ndarray  # [B, Hkv, N, d] float32, bf16-exact
+    scale: float
+    causal: bool
+
+
+def fp8_fwd_inputs(B, Hq, Hkv, N, d, seed, causal=True, k_mult=1.0, scale=None):
+    """The forward inputs of `fwd_inputs` with Q and K rounded to e4m3 instead of bf16 (V stays
+    bf16): the same draws, a different rounding."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, N, d), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, N, d), dtype=np.float32)
+    if k_mult != 1.0:
+        k *= np.float32(k_mult)
+    v = rng.standard_normal((B, Hkv, N, d), dtype=np.float32)
+    return Fp8Inputs(round_to_e4m3(q), round_to_e4m3(k), round_to_bf16(v),
+                     1.0 / math.sqrt(d) if scale is None else scale, causal)
+
+
 def to_torch(x: np.ndarray, dtype: str, device="cuda"):
-    """Upload a float32 array as a torch tensor of ``dtype`` ("f32" or "bf16"), exactly."""
+    """Upload a float32 array as a torch tensor of ``dtype`` ("f32", "bf16" or "e4m3", the last
+    as uint8 codes), exactly."""
     import torch
 
+    if dtype == "e4m3":
+        return torch.from_numpy(e4m3_bits(x)).to(device).contiguous()
     if dtype == "bf16":
         bits = bf16_bits(x).view(np.int16)
         t = torch.from_numpy(bits).view(torch.bfloat16)

@@ -14,6 +14,8 @@
  *                     the FlashAttention-family table (Flash-Decoding, paged variants).
  *   fa_merge          merge of partial (m, l, O) results over disjoint key sets with the
  *                     online-softmax rescale; "FlashAttention", "Decode is a different problem".
+ *   fa_fwd_fp8        tiled forward with fp8 (e4m3) Q and K on the fp8 matrix cores; the
+ *                     FP8 row of the FlashAttention-family table ("FlashAttention").
  *   fa_bwd            backward by recomputation (dQ, dK, dV from Q, K, V, O, dO and the saved
  *                     row statistics); "FlashAttention, explained." (vibeengines.com),
  *                     backward-pass section.
@@ -116,6 +118,25 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int d, int page_size, int max_se
 
 /* The number of KV chunks the automatic plan gives the longest sequence (0 if invalid). */
 int fa_decode_plan_splits(int B, int Hkv, int page_size, int max_seq_len);
+
+/*
+ * fa_fwd_fp8 - tiled forward with fp8 queries and keys.
+ *
+ *   q : [B, Hq, N, d] OCP fp8 e4m3 (one byte per element: sign, 4 exponent bits with bias 7,
+ *       3 mantissa bits)
+ *   k : [B, Hkv, N, d] e4m3;  v : [B, Hkv, N, d] bf16;  o : [B, Hq, N, d] bf16
+ *   m_out, l_out : optional float32 [B, Hq, N] row statistics (NULL = not written)
+ *
+ * Computes what fa_fwd computes for the real values the codes stand for: the scores
+ * scale * q.k are exact products of e4m3 values accumulated in float32, so a per-tensor
+ * descale of q and k is passed by folding it into `scale` (finite, > 0). Softmax in float32,
+ * P rounded to bf16 for P V, float32 accumulation, bf16 output. causal as in fa_fwd.
+ * Supported: d = 128; Hq % Hkv == 0 (else FA_ERR_INVALID_ARGUMENT); N * d * 2 < 2^31.
+ * B, Hq or N equal to 0 is a valid empty call.
+ */
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* m_out,
+                     float* l_out, int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                     void* stream);
 
 /*
  * fa_bwd - gradients of fa_fwd's output with respect to q, k and v.

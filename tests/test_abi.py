@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_decode_splitk", "fa_merge", "fa_status_string",
               "fa_decode_workspace_bytes", "fa_decode_plan_splits", "fa_fwd_paged",
-              "fa_fwd_block_sparse", "fa_bwd", "fa_bwd_workspace_bytes"):
+              "fa_fwd_block_sparse", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_fp8"):
         assert n in names
 
 
@@ -191,6 +191,24 @@ def sparse(lib, dt=1, q=DEV, k=DEV, v=DEV, o=DEV, offs=DEV, idx=DEV, nnz=4, B=1,
 ])
 def test_fwd_block_sparse_validation(kwargs, code):
     assert sparse(fa.load_library(), **kwargs) == code
+
+
+def fp8(lib, q=DEV, k=DEV, v=DEV, o=DEV, B=1, Hq=4, Hkv=2, N=300, d=128, scale=0.1, causal=1):
+    return lib.fa_fwd_fp8(q, k, v, o, None, None, B, Hq, Hkv, N, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(d=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(Hq=3, Hkv=2), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(B=-1), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(k=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(v=MIS), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(N=1 << 23), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=0, q=NULL), fa.FA_OK),
+])
+def test_fwd_fp8_validation(kwargs, code):
+    assert fp8(fa.load_library(), **kwargs) == code
 
 
 def bwd(lib, dt=1, q=DEV, k=DEV, v=DEV, o=DEV, do=DEV, m=DEV, l=DEV, dq=DEV, dk=DEV, dv=DEV,

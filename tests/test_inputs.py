@@ -67,3 +67,22 @@ def test_decode_pages_gather_back_to_logical():
 def test_decode_lengths_drawn_inclusive_range():
     di = gen.decode_inputs(B=64, Hq=2, Hkv=1, d=4, page_size=16, seed=5, len_min=3, len_max=5)
     assert set(di.lens.tolist()) <= {3, 4, 5} and len(set(di.lens.tolist())) == 3
+
+
+def test_e4m3_rounding_and_codes():
+    """OCP e4m3: 1.0 = 0x38, 1.5 = 0x3c, 448 (largest finite) = 0x7e, 2^-6 (smallest normal) =
+    0x08, 2^-9 (smallest subnormal) = 0x01; ties round to even; magnitudes past 448 saturate."""
+    from exact_tiled_attention_24_amd import inputs as gen
+
+    vals = np.array([1.0, 1.5, 448.0, 2.0 ** -6, 2.0 ** -9, -3.0, 0.0], np.float32)
+    codes = [0x38, 0x3C, 0x7E, 0x08, 0x01, 0xC4, 0x00]
+    assert np.array_equal(gen.round_to_e4m3(vals), vals)
+    assert gen.e4m3_bits(vals).tolist() == codes
+    # 1 + 1/16 lies halfway between 1 and 1.125: to even (1.0); 1 + 3/16 -> 1.25
+    r = gen.round_to_e4m3(np.array([1.0625, 1.1875, 1000.0, -1000.0, 2.0 ** -10 * 3], np.float32))
+    assert r.tolist() == [1.0, 1.25, 448.0, -448.0, 2.0 ** -9 * 2]
+    # every code 0x00..0x7e decodes back to itself through the value grid
+    x = np.random.default_rng(0).standard_normal(10000).astype(np.float32) * 8
+    y = gen.round_to_e4m3(x)
+    assert np.all(np.abs(y - x) <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10) + 1e-12)
+    assert np.array_equal(gen.round_to_e4m3(y), y)
