@@ -124,6 +124,7 @@ TRAFFIC_KERNELS = {
     "fwd": ("fwd_bf16_sp_kernel<128, 0>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
     "paged": ("fwd_bf16_sp_kernel<128, 1>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
     "sparse": ("fwd_bf16_sp_kernel<128, 2>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
+    "fp8": ("fwd_bf16_sp_kernel<128, 3>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
     "decode": ("decode_mx_kernel", "exact_tiled_attention_24_amd/csrc/decode_mx.hip"),
 }
 COPY_KERNEL = "copyBuffer"
@@ -517,7 +518,7 @@ def main():
                          "peak": round(mixed_peak, 1), "unit": "TFLOP/s",
                          "frac": round(f_tflops / mixed_peak, 4),
                          "peak_note": "S on fp8 (5.0 PFLOP/s), P V on bf16 (2.5 PFLOP/s)",
-                         "kernel": "fwd_bf16_sp_kernel<128, 3>"},
+                         "traffic": traffic.get("fp8"), "kernel": "fwd_bf16_sp_kernel<128, 3>"},
         }
     if do_bwd:
         b_tflops = bwd_flops / (bwd_ms.mean() * 1e-3) / 1e12
