@@ -42,9 +42,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--fwd-config", type=int, default=3, choices=[2, 3, 4])
     ap.add_argument("--decode-splits", type=int, default=0, help="0 = the library's plan")
-    ap.add_argument("--kv-pools", type=int, default=1,
+    ap.add_argument("--kv-pools", type=int, default=2,
                     help="copies of the decode KV cache used in turn, so that no call finds the "
-                         "previous call's pages in the caches (1 = one cache)")
+                         "previous call's pages in L2 or the Infinity Cache (1 = one cache)")
     ap.add_argument("--decode-mx", default=None, metavar="W,S",
                     help="matrix-core decode variant: waves per workgroup, page slots per wave "
                          "(default 4,2)")
