@@ -231,8 +231,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
     __syncthreads();
     for (int it = 0; it < total; ++it) {
         if (it + 1 < total) load_chunk(it + 1);  // in flight during this chunk's products
-        size_t qoff_unused;
-        const int qc0 = chunk_rows(it, qoff_unused);
+        size_t qoff_chunk;  // (the head's row base; the chunk's rows are already staged)
+        const int qc0 = chunk_rows(it, qoff_chunk);
         const unsigned char* base = smem + (it & 1) * kBuf;
         lds_cptr const lq = (lds_cptr)base;
         lds_cptr const ldo = (lds_cptr)(base + S::kTile);

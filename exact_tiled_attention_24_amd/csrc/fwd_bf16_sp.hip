@@ -47,6 +47,11 @@
 // tile offsets feeds the loads as in the paged variant, and a short delay line of the tiles'
 // first key positions drives the masking of diagonal, ragged and invalid tiles.
 //
+// FP8 variant (kFp8, d = 128): e4m3 Q and K. S^T takes two v_mfma_f32_32x32x64_f8f6f4 per half
+// tile (a lane holds 32 consecutive head dimensions of its query; it reads the same 32 of
+// its K row), in an 8-slot step whose every slot holds one bf16 P V MFMA; softmax, P and O
+// as in bf16. K rows are 144 B in LDS (conflict free), a K stage 9 KiB.
+//
 // Paged variant (kPaged): chunked prefill over a paged KV cache, the paged rows of the
 // family table on the same page. The queries are the newest Nq tokens of each sequence, so
 // query i sits at position L - Nq + i of its L cached tokens and the causal diagonal is
@@ -121,9 +126,9 @@ struct Tile {
     static_assert(kStages * (kKStage + kVStage) <= 160 * 1024, "fits the LDS of one CU");
 };
 
-// Kernel arguments. Dense: k, v are [B, Hkv, N, d]. Paged: k, v are the caches
-// [num_pages, Hkv, 16, d], N is the query count Nq, and table / lens name the pages and the
-// cached length of each sequence.
+// Kernel arguments. Dense (and fp8, with e4m3 q and k): k, v are [B, Hkv, N, d]. Paged: k, v
+// are the caches [num_pages, Hkv, 16, d], N is the query count Nq, and table / lens name the
+// pages and the cached length of each sequence. Block-sparse: blk_off / blk_idx / nnz.
 struct FwdArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -289,7 +294,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     // K tile) always lies in it too; the next window's table entries are loaded one tile
     // before they are needed. Rows of the last page past the sequence end are cut per lane
     // in the V loads (K rows there only meet masked scores).
-    constexpr unsigned kPagePad = 0x80000000u;
+    constexpr unsigned kPagePad = 0x80000000u;  // an offset past every descriptor's range
     const int p_last = (Nk - 1) / kPageTok;                          // last page holding a row
     const int last_bytes = (Nk - kPageTok * p_last) * D * 2;         // its rows, in bytes
     const unsigned stride_bytes = (unsigned)Hkv * kPageTok * D * 2;  // one physical page
@@ -593,8 +598,9 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
             } else if (ph == 3) {
                 mx = pair32_vmax(vmax(t0, t3)) * scale_log2;
             } else if (ph == 4) {
-                // (the first half tile always holds a key every row sees, key 0, so its mx is
-                // finite: m_ref leaves -inf there, with alpha = 0 on a zero O and row sum)
+                // (m_ref starts at -1e30: the first finite row maximum always moves it, with
+                // alpha = 0 on a zero O and row sum; a row with no key yet keeps it and gets
+                // exp2(-inf) = 0 for its masked scores)
                 m_run = vmax(m_run, mx);
                 move = mx > m_ref + kLazy;
                 const float r_new = move ? mx : m_ref;
