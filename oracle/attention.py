@@ -151,28 +151,31 @@ def decode(q, k_seqs, v_seqs, scale):
     return out, m, l
 
 
-def prefill_paged(q, k_seqs, v_seqs, scale, causal, row_block=256):
-    """Attention of each sequence's newest Nq query rows against its whole (logical) K/V.
+def prefill_paged(q, k_seqs, v_seqs, scale, causal, row_block=256, q_lens=None):
+    """Attention of each sequence's newest query rows against its whole (logical) K/V.
 
-    q: [B, Hq, Nq, d]; k_seqs[b], v_seqs[b]: [Hkv, L_b, d]. The Nq queries of sequence b are
-    its last Nq tokens: query i sits at position pos_i = L_b - Nq + i, so the causal mask
-    admits key j iff j <= pos_i (the diagonal aligned to the bottom right of the L_b x Nq
-    score block); without the mask every j < L_b is admissible. A query with no admissible
-    key (pos_i < 0 when Nq > L_b, or L_b = 0) has O = 0, m = -inf, l = 0. S and P are
+    q: [B, Hq, Nq, d]; k_seqs[b], v_seqs[b]: [Hkv, L_b, d]; q_lens: optional per-sequence
+    query counts n_b <= Nq (default: Nq for every sequence). The n_b queries of sequence b are
+    its last n_b tokens, in rows 0 .. n_b - 1: query i sits at position pos_i = L_b - n_b + i,
+    so the causal mask admits key j iff j <= pos_i (the diagonal aligned to the bottom right of
+    the L_b x n_b score block); without the mask every j < L_b is admissible. A query with no
+    admissible key (pos_i < 0 when n_b > L_b, or L_b = 0) has O = 0, m = -inf, l = 0. Rows
+    i >= n_b are not queries: they come back as O = 0, m = -inf, l = 0. S and P are
     materialised in full-width blocks of ``row_block`` rows over all L_b keys.
 
     Returns O [B, Hq, Nq, d], m [B, Hq, Nq], l [B, Hq, Nq], float64.
     """
     q = _f64(q)
-    b_, hq, nq, d = q.shape
-    out = np.zeros((b_, hq, nq, d))
-    m_out = np.full((b_, hq, nq), -np.inf)
-    l_out = np.zeros((b_, hq, nq))
+    b_, hq, nq_all, d = q.shape
+    out = np.zeros((b_, hq, nq_all, d))
+    m_out = np.full((b_, hq, nq_all), -np.inf)
+    l_out = np.zeros((b_, hq, nq_all))
     for b in range(b_):
         kb = _f64(k_seqs[b])
         vb = _f64(v_seqs[b])
         n_keys = kb.shape[1]
         group = hq // kb.shape[0]
+        nq = nq_all if q_lens is None else int(min(max(int(q_lens[b]), 0), nq_all))
         pos = n_keys - nq + np.arange(nq)
         for h in range(hq):
             for r0 in range(0, nq, row_block):

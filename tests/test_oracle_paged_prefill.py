@@ -174,3 +174,32 @@ def test_prefill_pins_catch_alignment_mistakes(kind):
 def test_prefill_mutant_harness_passes_when_correct():
     for pin in PINS:
         pin(_mutant("none"))
+
+
+def test_varlen_queries_reduce_to_single_sequences():
+    """With per-sequence query counts, each sequence's rows equal prefill_paged on that
+    sequence alone with Nq = its count; the rows past it are empty; counts all equal to Nq
+    give the uniform result."""
+    rng = np.random.default_rng(45)
+    lens, Nq = [9, 14, 5, 0], 6
+    q, ks, vs = _draw(rng, lens, 4, 2, Nq, 3)
+    q_lens = [6, 3, 0, 2]
+    for causal in (True, False):
+        o, m, l = oracle.prefill_paged(q, ks, vs, 0.8, causal, q_lens=q_lens)
+        for b, n in enumerate(q_lens):
+            ob, mb, lb = oracle.prefill_paged(q[b:b + 1, :, :n], ks[b:b + 1], vs[b:b + 1], 0.8, causal)
+            np.testing.assert_allclose(o[b, :, :n], ob[0], atol=1e-13)
+            np.testing.assert_allclose(l[b, :, :n], lb[0], rtol=1e-12)
+            assert np.all(o[b, :, n:] == 0) and np.all(l[b, :, n:] == 0) and np.all(m[b, :, n:] == -np.inf)
+        ou, mu, lu = oracle.prefill_paged(q, ks, vs, 0.8, causal, q_lens=[Nq] * 4)
+        o0, m0, l0 = oracle.prefill_paged(q, ks, vs, 0.8, causal)
+        np.testing.assert_array_equal(ou, o0)
+        np.testing.assert_array_equal(lu, l0)
+    # a planted mistake: positions from Nq instead of the sequence's own count
+    o_bad = np.zeros_like(o)
+    for b, n in enumerate(q_lens):
+        if n:
+            ob, _, _ = oracle.prefill_paged(q[b:b + 1], ks[b:b + 1], vs[b:b + 1], 0.8, True)
+            o_bad[b, :, :n] = ob[0, :, :n]
+    o, _, _ = oracle.prefill_paged(q, ks, vs, 0.8, True, q_lens=q_lens)
+    assert not np.allclose(o_bad, o)
