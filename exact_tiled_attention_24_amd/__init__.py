@@ -63,8 +63,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_decode_plan_splits.argtypes = [i32, i32, i32, i32]
     lib.fa_decode_plan_splits.restype = i32
-    lib.fa_fwd_paged.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
-                                 i32, i32, i32, f32, i32, vp]
+    lib.fa_fwd_paged.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                 i32, i32, i32, i32, f32, i32, vp]
     lib.fa_fwd_paged.restype = i32
     lib.fa_fwd_block_sparse.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                         i32, i32, f32, i32, vp]
@@ -208,13 +208,15 @@ def fa_decode_splitk(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, sc
 
 
 def fa_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=True, out=None,
-                 return_stats=False):
+                 return_stats=False, q_lens=None):
     """Chunked prefill over a paged KV cache: each sequence's newest Nq tokens attend to its
     whole cache (query i at position seq_lens[b] - Nq + i).
 
     q: [B, Hq, Nq, d] bf16; k_cache, v_cache: [num_pages, Hkv, 16, d] bf16; block_table:
     int32 [B, max_pages_per_seq]; seq_lens: int32 [B] (all on the GPU). Returns O [B, Hq, Nq,
     d] bf16, or (O, m, l) with float32 [B, Hq, Nq] statistics when ``return_stats``.
+    ``q_lens`` (int32 [B] on the GPU): new tokens per sequence, in the first rows of q; the
+    other rows of the outputs are not written.
     """
     torch = _torch()
     lib = load_library()
@@ -233,14 +235,16 @@ def fa_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=
     if return_stats:
         m = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
         l = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    _require_gpu(q, k_cache, v_cache, block_table, seq_lens, o, m, l)
+    if q_lens is not None and (q_lens.dtype != torch.int32 or q_lens.shape != (B,)):
+        raise ValueError("q_lens must be int32 [B]")
+    _require_gpu(q, k_cache, v_cache, block_table, seq_lens, o, m, l, q_lens)
     if o.shape != q.shape or o.dtype != q.dtype:
         raise ValueError("out must match q in shape and dtype")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     with torch.cuda.device(q.device):
         code = lib.fa_fwd_paged(
             _dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-            _ptr(seq_lens), _ptr(o), _ptr(m), _ptr(l), B, Hq, Hkv, Nq, d, page_size, num_pages,
+            _ptr(seq_lens), _ptr(q_lens), _ptr(o), _ptr(m), _ptr(l), B, Hq, Hkv, Nq, d, page_size, num_pages,
             block_table.shape[1], scale, 1 if causal else 0, _stream(q.device))
     _check(code, "fa_fwd_paged")
     return (o, m, l) if return_stats else o

@@ -247,7 +247,8 @@ fa_status fa_fwd_block_sparse(fa_dtype dt, const void* q, const void* k, const v
 }
 
 fa_status fa_fwd_paged(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
-                       const int32_t* block_table, const int32_t* seq_lens, void* o,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       const int32_t* q_lens, void* o,
                        float* m_out, float* l_out, int B, int Hq, int Hkv, int Nq, int d,
                        int page_size, int num_pages, int max_pages_per_seq, float scale,
                        int causal, void* stream) {
@@ -269,7 +270,7 @@ fa_status fa_fwd_paged(fa_dtype dt, const void* q, const void* k_cache, const vo
     // the kernel addresses each cache with 32-bit byte offsets below 2^31
     if ((long long)num_pages * Hkv * page_size * d * 2 >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
     const hipError_t e = fa::launch_fwd_bf16_sp_paged(
-        q, k_cache, v_cache, block_table, seq_lens, o, m_out, l_out, B, Hq, Hkv, Nq, d, num_pages,
+        q, k_cache, v_cache, block_table, seq_lens, q_lens, o, m_out, l_out, B, Hq, Hkv, Nq, d, num_pages,
         max_pages_per_seq, scale, causal ? 1 : 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -22,10 +22,11 @@ hipError_t launch_fwd_bf16_sp(const void* q, const void* k, const void* v, void*
                               float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
                               int causal, hipStream_t stream);
 
-// Chunked prefill over a paged KV cache with the same kernel: the Nq queries of sequence b
-// are its newest tokens (bottom-right causal alignment); K/V pages through the block table.
+// Chunked prefill over a paged KV cache with the same kernel: the Nq (or q_lens[b]) queries of
+// sequence b are its newest tokens (bottom-right causal alignment); K/V through the table.
 hipError_t launch_fwd_bf16_sp_paged(const void* q, const void* k_cache, const void* v_cache,
-                                    const int32_t* block_table, const int32_t* seq_lens, void* o,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* q_lens, void* o,
                                     float* m_out, float* l_out, int B, int Hq, int Hkv, int Nq,
                                     int d, int num_pages, int max_pages_per_seq, float scale,
                                     int causal, hipStream_t stream);

@@ -138,6 +138,7 @@ struct FwdArgs {
     float* l_out;
     const int32_t* table;
     const int32_t* lens;
+    const int32_t* q_lens;   // paged: optional query rows per sequence (NULL: N each)
     const int32_t* blk_off;  // block-sparse: compressed rows of key-tile lists
     const int32_t* blk_idx;
     int nnz;                 // entries of blk_idx
@@ -185,11 +186,18 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     // Keys of this item's sequence and the position offset of its queries: query row i sits
     // at position i + off (dense: the N keys, off = 0; paged: the cached length L, clamped to
     // the table, and off = L - Nq, the bottom-right alignment).
-    int Nk = N, off = 0;
+    // (paged with per-sequence query counts: this sequence's queries are rows 0 .. nq - 1, and
+    // a block that starts past them is no work item at all)
+    int Nk = N, off = 0, nq = N;
     if constexpr (kPaged) {
         const int L = a.lens[b];
         Nk = __builtin_amdgcn_readfirstlane(L < 0 ? 0 : min_(L, a.max_pages * kPageTok));
-        off = Nk - N;
+        if (a.q_lens) {
+            const int n = a.q_lens[b];
+            nq = __builtin_amdgcn_readfirstlane(n < 0 ? 0 : min_(n, N));
+        }
+        off = Nk - nq;
+        if (qb * kBr >= nq) return;
     }
     // Block-sparse: this item's key tiles are blk_idx[list0 .. list0 + n_list) (clamped into
     // the array, so no read leaves it whatever the offsets hold).
@@ -776,7 +784,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
             for (int i = 0; i < D / 32; ++i) acc_o[i] = f32x16{};
         }
     }
-    if (qrow < N) {
+    if (qrow < nq) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         uint16_t* dst = o + qoff + (size_t)qrow * D;
 #pragma unroll
@@ -890,7 +898,8 @@ hipError_t launch_fwd_bf16_sp(const void* q, const void* k, const void* v, void*
 }
 
 hipError_t launch_fwd_bf16_sp_paged(const void* q, const void* k_cache, const void* v_cache,
-                                    const int32_t* block_table, const int32_t* seq_lens, void* o,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* q_lens, void* o,
                                     float* m_out, float* l_out, int B, int Hq, int Hkv, int Nq,
                                     int d, int num_pages, int max_pages_per_seq, float scale,
                                     int causal, hipStream_t stream) {
@@ -903,6 +912,7 @@ hipError_t launch_fwd_bf16_sp_paged(const void* q, const void* k_cache, const vo
     a.l_out = l_out;
     a.table = block_table;
     a.lens = seq_lens;
+    a.q_lens = q_lens;
     a.B = B, a.Hq = Hq, a.Hkv = Hkv, a.N = Nq;
     a.scale_log2 = scale * kLog2e;
     a.causal = causal;

@@ -200,11 +200,14 @@ fa_status fa_fwd_block_sparse(fa_dtype dt, const void* q, const void* k, const v
  *                 block_table[b][t / 16], slot t % 16; query head h reads KV head h / (Hq / Hkv)
  *   block_table : int32 [B, max_pages_per_seq], device memory
  *   seq_lens    : int32 [B], device memory: cached tokens of each sequence, chunk included
+ *   q_lens      : optional int32 [B], device memory: new tokens of each sequence, n_b =
+ *                 clamp(q_lens[b], 0, Nq), in rows 0 .. n_b - 1 of q and o (NULL: n_b = Nq);
+ *                 rows n_b .. Nq - 1 of o, m_out and l_out are not written
  *   m_out, l_out: optional float32 [B, Hq, Nq] row statistics (NULL = not written)
  *
- * causal != 0 admits key j for query i iff j <= seq_lens[b] - Nq + i (the diagonal aligned to
+ * causal != 0 admits key j for query i iff j <= seq_lens[b] - n_b + i (the diagonal aligned to
  * the bottom right); causal == 0 admits every j < seq_lens[b]. A query that admits no key
- * (seq_lens[b] < Nq, causal, or seq_lens[b] == 0) yields O = 0, m = -inf, l = 0. `scale`
+ * (seq_lens[b] < n_b, causal, or seq_lens[b] == 0) yields O = 0, m = -inf, l = 0. `scale`
  * must be finite and > 0. bf16 inputs, float32 accumulation and softmax, bf16 output.
  *
  * Caller preconditions that are not checked on the device: block_table[b][p] in
@@ -218,7 +221,8 @@ fa_status fa_fwd_block_sparse(fa_dtype dt, const void* q, const void* k, const v
  * B, Hq or Nq equal to 0 is a valid empty call.
  */
 fa_status fa_fwd_paged(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
-                       const int32_t* block_table, const int32_t* seq_lens, void* o,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       const int32_t* q_lens, void* o,
                        float* m_out, float* l_out, int B, int Hq, int Hkv, int Nq, int d,
                        int page_size, int num_pages, int max_pages_per_seq, float scale,
                        int causal, void* stream);

@@ -137,7 +137,7 @@ def test_decode_workspace_and_plan():
 
 def paged(lib, dt=1, q=DEV, kc=DEV, vc=DEV, table=DEV, lens=DEV, o=DEV, B=2, Hq=8, Hkv=2, Nq=64,
           d=128, page=16, num_pages=10, max_pages=8, scale=0.1, causal=1):
-    return lib.fa_fwd_paged(dt, q, kc, vc, table, lens, o, None, None, B, Hq, Hkv, Nq, d, page,
+    return lib.fa_fwd_paged(dt, q, kc, vc, table, lens, None, o, None, None, B, Hq, Hkv, Nq, d, page,
                             num_pages, max_pages, scale, causal, None)
 
 

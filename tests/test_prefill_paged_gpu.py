@@ -209,3 +209,33 @@ def test_prefill_paged_empty_calls_are_noops(dev):
     lens = torch.zeros((0,), dtype=torch.int32, device=dev)
     o = fa.fa_fwd_paged(q, kc, kc, tab, lens)
     assert o.shape == q.shape
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_prefill_paged_per_sequence_query_counts(d, dev):
+    """Different numbers of new tokens per sequence (q_lens), including none, more rows than
+    one query block, and more new tokens than cached keys (its first rows see nothing): rows
+    past a sequence's count keep what the output held."""
+    import torch
+
+    B, Hq, Hkv, Nq = 5, 8, 2, 600
+    lens = [700, 300, 2000, 50, 90]
+    q_lens = [600, 100, 257, 0, 120]
+    log_case(f"fa_fwd_paged q_lens={q_lens} lens={lens} d={d}")
+    x = gen.prefill_paged_inputs(B, Hq, Hkv, Nq, d, 16, seed=660 + d, lens=lens,
+                                 max_pages_per_seq=-(-max(lens) // 16) + 1)
+    t = upload(x, dev)
+    ql = torch.tensor(q_lens, dtype=torch.int32, device=dev)
+    sentinel = 7.0
+    o = torch.full(t["q"].shape, sentinel, dtype=torch.bfloat16, device=dev)
+    o, m, l = fa.fa_fwd_paged(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["seq_lens"],
+                              scale=x.scale, causal=True, out=o, return_stats=True, q_lens=ql)
+    torch.cuda.synchronize()
+    o_ref, m_ref, l_ref = oracle.prefill_paged(x.q, x.k_seqs, x.v_seqs, x.scale, True, q_lens=q_lens)
+    o, m, l = to_np(o), to_np(m), to_np(l)
+    for b, n in enumerate(q_lens):
+        if n:
+            assert_close(o[b, :, :n], o_ref[b, :, :n], "bf16", f"sequence {b} O")
+            check_stats(torch.from_numpy(m[b, :, :n]), torch.from_numpy(l[b, :, :n]),
+                        m_ref[b, :, :n], l_ref[b, :, :n])
+        assert np.all(o[b, :, n:] == sentinel), f"sequence {b}: rows past {n} were written"
