@@ -254,17 +254,30 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
                 dp[u] = mfma_32x32x16(rows_frag<D>(tdo, lane, kk), vf[kk], dp[u]);
             }
         }
+        // No score of this chunk is masked when the wave's 32 keys and the chunk's queries all
+        // lie inside the sequence and (causal) the chunk's first query follows the wave's last
+        // key; then the probabilities take no predicate (a wave-uniform branch)
+        const int kw0 = kb0 + 32 * wave;
+        const bool plain = kw0 + 32 <= N && qc0 + kChunk <= N && (!a.causal || qc0 >= kw0 + 31);
 #pragma unroll
         for (int u = 0; u < kSub; ++u) {
             float p[16], ds[16];
+            if (plain) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qr = 32 * u + acc_row(r, h);
-                const int qi = qc0 + qr;
-                const bool ok = key < N && qi < N && (!a.causal || key <= qi);
-                p[r] = ok ? exp2_hw(__builtin_fmaf(sc[u][r], a.scale_log2, -s_l[qr])) : 0.f;
-                ds[r] = p[r] * (dp[u][r] - s_d[qr]);
+                for (int r = 0; r < 16; ++r)
+                    p[r] = exp2_hw(__builtin_fmaf(sc[u][r], a.scale_log2, -s_l[32 * u + acc_row(r, h)]));
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qr = 32 * u + acc_row(r, h);
+                    const int qi = qc0 + qr;
+                    const bool ok = key < N && qi < N && (!a.causal || key <= qi);
+                    const float e = exp2_hw(__builtin_fmaf(sc[u][r], a.scale_log2, -s_l[qr]));
+                    p[r] = ok ? e : 0.f;
+                }
             }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ds[r] = p[r] * (dp[u][r] - s_d[32 * u + acc_row(r, h)]);
             // dV^T += dO^T P and dK^T += Q^T dS (K-dim = the sub-chunk's queries)
             const lds_cptr tq = lq + 32 * u * S::kRow, tdo = ldo + 32 * u * S::kRow;
 #pragma unroll
@@ -370,15 +383,26 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
                 dp[u] = mfma_32x32x16(rows_frag<D>(tv, lane, kk), dof[kk], dp[u]);
             }
         }
+        // No score of this chunk is masked when the wave's 32 queries and the chunk's keys all
+        // lie inside the sequence and (causal) the chunk's last key precedes the wave's first
+        // query; then the probabilities take no predicate (a wave-uniform branch)
+        const int qw0 = qb0 + 32 * wave;
+        const bool plain = qw0 + 32 <= N && kc0 + kChunk <= N && (!a.causal || kc0 + kChunk - 1 <= qw0);
 #pragma unroll
         for (int u = 0; u < kSub; ++u) {
             float ds[16];
+            if (plain) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int kj = kc0 + 32 * u + acc_row(r, h);
-                const bool ok = kj < N && query < N && (!a.causal || kj <= query);
-                const float p = ok ? exp2_hw(__builtin_fmaf(sc[u][r], a.scale_log2, -lse)) : 0.f;
-                ds[r] = p * (dp[u][r] - dsum);
+                for (int r = 0; r < 16; ++r)
+                    ds[r] = exp2_hw(__builtin_fmaf(sc[u][r], a.scale_log2, -lse)) * (dp[u][r] - dsum);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kj = kc0 + 32 * u + acc_row(r, h);
+                    const bool ok = kj < N && query < N && (!a.causal || kj <= query);
+                    const float e = exp2_hw(__builtin_fmaf(sc[u][r], a.scale_log2, -lse));
+                    ds[r] = (ok ? e : 0.f) * (dp[u][r] - dsum);
+                }
             }
             // dQ^T += K^T dS^T (K-dim = the sub-chunk's keys)
             const lds_cptr tk = lk + 32 * u * S::kRow;
