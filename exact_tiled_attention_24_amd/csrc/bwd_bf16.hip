@@ -49,11 +49,22 @@ __device__ __forceinline__ int acc_row(int r, int h) { return 16 * (r >> 3) + 8 
 template <int D, int SUB>
 struct Stage {
     static constexpr int kChunk = 32 * SUB;  // rows of a staged chunk
-    static constexpr int kRow = D * 2 + 16;  // padded row, bytes
+    static constexpr int kRow = D * 2;       // row, bytes (unpadded; chunks swizzled)
     static constexpr int kTile = kChunk * kRow;
 };
 
-// A chunk of 32 rows x D bf16 travels global memory -> registers -> LDS (padded rows); the
+// A staged row's 16-byte chunk c sits at chunk position c ^ swz(row). With 64 four-byte
+// banks this keeps every access of a tile conflict-free: the row reads (16 lanes, 16 rows,
+// one chunk) find 16 different bank groups, and so do the transposing reads (32 lanes, 4 rows,
+// 4 adjacent chunks each), which a row pad cannot give together with the row reads.
+// d = 128 (a row fills the banks once): the chunk index is XORed with (row bits 0-1) << 2 |
+// row bits 2-3. d = 64 (two rows per bank line): with row bit 1 << 2 | row bits 2-3.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// A chunk of 32 rows x D bf16 travels global memory -> registers -> LDS (swizzled rows); the
 // registers let the next chunk's loads fly while the current chunk is computed. Thread i
 // holds the 16-byte pieces i, i + 256, ... of the chunk; rows past n read as zero.
 template <int D, int SUB>
@@ -77,7 +88,7 @@ struct ChunkRegs {
         for (int p = 0; p < kPieces; ++p) {
             const int i = threadIdx.x + kThreads * p;
             const int r = i / kPer, c = i - r * kPer;
-            *reinterpret_cast<u32x4*>(dst + r * Stage<D, SUB>::kRow + 16 * c) = v[p];
+            *reinterpret_cast<u32x4*>(dst + r * Stage<D, SUB>::kRow + 16 * (c ^ swz<D>(r))) = v[p];
         }
     }
 };
@@ -85,8 +96,9 @@ struct ChunkRegs {
 // A operand of a 32 x 16 slice (K-dim chunk kk) of a staged tile, rows in kappa order.
 template <int D>
 __device__ __forceinline__ bf16x8 rows_frag(lds_cptr tile, int lane, int kk) {
-    return *reinterpret_cast<const lds_bf16x8*>(tile + kappa(lane & 31) * Stage<D, 1>::kRow + 32 * kk +
-                                                 16 * (lane >> 5));
+    const int r = kappa(lane & 31);
+    return *reinterpret_cast<const lds_bf16x8*>(tile + r * Stage<D, 1>::kRow +
+                                                 16 * ((2 * kk + (lane >> 5)) ^ swz<D>(r)));
 }
 
 // A operand of the transposed tile X^T (rows = head dimensions 32 db .., K-dim = the tile's
@@ -95,10 +107,15 @@ __device__ __forceinline__ bf16x8 rows_frag(lds_cptr tile, int lane, int kk) {
 template <int D>
 __device__ __forceinline__ bf16x8 trans_frag(lds_cptr tile, int lane, int t, int db) {
     constexpr int R = Stage<D, 1>::kRow;
-    const lds_cptr p = tile + (8 * (lane >> 5) + ((lane & 15) >> 2)) * R +
-                       (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2 + 16 * t * R + 64 * db;
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * R));
+    // the lane's 8 bytes: row r (+ 4 for the second read), head dimensions 32 db + 16 g +
+    // 4 (lane & 3) .., i.e. chunk 4 db + 2 g + (lane & 3) / 2, byte 8 (lane & 1) of it
+    const int r = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const lds_cptr row = tile + 16 * t * R + 8 * (lane & 1);
+    const lds_cptr plo = row + r * R + 16 * (c ^ swz<D>(r));
+    const lds_cptr phi = row + (r + 4) * R + 16 * (c ^ swz<D>(r + 4));
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)plo);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)phi);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -315,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
 
 // ---- dQ: workgroup = 128 queries of one query head; wave = 32 queries ----
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     constexpr int kSub = kSubQ;
     using S = Stage<D, kSub>;
     constexpr int kChunk = S::kChunk;
