@@ -127,6 +127,17 @@ __device__ __forceinline__ bf16x8 acc_operand(const float (&x)[16], int t) {
     return __builtin_bit_cast(bf16x8, w);
 }
 
+// Workgroups are dealt to the 8 XCDs round robin by linear id. xcd_position maps the linear
+// id to a position in (head, block) order so that each XCD receives a contiguous run of
+// positions: the ~32 workgroups one XCD runs at a time then share one or two heads, whose
+// staged operands (4 MiB per head at N = 8192, d = 128) its L2 can hold. A bijection on
+// 0 .. total - 1: XCD k holds the ids k, k + 8, .. and gets positions k q + min(k, r) on.
+__device__ __forceinline__ int xcd_position(int total) {
+    const int id = blockIdx.x + gridDim.x * blockIdx.y;
+    const int k = id & 7, j = id >> 3, q = total >> 3, r = total & 7;
+    return k * q + min_(k, r) + j;
+}
+
 // ---- D_i = rowsum(dO * O) and L_i = (m_i + ln l_i) log2 e, 4 threads per row ----
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const uint16_t* __restrict__ o,
@@ -187,9 +198,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kBuf];
 
     const int N = a.N, G = a.Hq / a.Hkv;
-    const int bk = blockIdx.y;  // b * Hkv + kvh
+    const int pos = xcd_position(gridDim.x * gridDim.y);
+    const int bk = pos / gridDim.x;  // b * Hkv + kvh
     const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
-    const int kb0 = blockIdx.x * kBlock;
+    const int kb0 = (pos - bk * gridDim.x) * kBlock;  // (causal: the first blocks see the most queries)
     const int lane = threadIdx.x & 63, h = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int key = kb0 + 32 * wave + (lane & 31);  // this lane's key (accumulator column)
@@ -340,10 +352,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[4 * S::kTile];
 
     const int N = a.N, G = a.Hq / a.Hkv;
-    const int bh = blockIdx.y;  // b * Hq + hq
+    const int pos = xcd_position(gridDim.x * gridDim.y);
+    const int bh = pos / gridDim.x;  // b * Hq + hq
     const int b = bh / a.Hq, hq = bh - b * a.Hq;
     const int kvh = hq / G;
-    const int qb0 = blockIdx.x * kBlock;
+    // last query block first: under the causal mask it sees the most keys
+    const int qb0 = (gridDim.x - 1 - (pos - bh * gridDim.x)) * kBlock;
     const int lane = threadIdx.x & 63, h = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int query = qb0 + 32 * wave + (lane & 31);  // this lane's query (accumulator column)
