@@ -38,6 +38,9 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef const __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef const __attribute__((address_space(3))) unsigned char* lds_cptr;
 
+// Word 3 of a raw buffer descriptor (no format, no swizzle) for the loads into LDS.
+constexpr int kRsrcWord3 = 0x00020000;
+
 __device__ __forceinline__ int kappa(int m) {
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
@@ -226,40 +229,75 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
     const int q_first = a.causal ? (kb0 / kChunk) * kChunk : 0;
     const int nch = (N - q_first + kChunk - 1) / kChunk;
     const int total = G * nch;
-    ChunkRegs<D, kSub> rq, rdo;
     float rl = INFINITY, rd = 0.f;
     auto chunk_rows = [&](int it, size_t& qoff) {  // first query row; qoff = head's row base
         const int g = it / nch;
         qoff = ((size_t)b * a.Hq + kvh * G + g) * N;
         return q_first + (it - g * nch) * kChunk;
     };
-    auto load_chunk = [&](int it) {
+    // The Q and dO rows of a chunk go straight from global memory into LDS (buffer_load ...
+    // lds, 1 KiB per instruction, no registers held while they fly). Instruction k of a tensor
+    // fills tile bytes 1024 k ..: lane l writes the 16 bytes at 1024 k + 16 l, i.e. row
+    // (1024 k + 16 l) / R at chunk position p, so it loads that row's logical chunk
+    // p ^ swz(row). Rows past N lie beyond the descriptor's range and read as zeros. Each
+    // wave issues a quarter of each tensor's instructions; L and D go through registers.
+    constexpr int R = S::kRow;
+    constexpr int kDmaPerWave = kChunk * R / 1024 / 4;  // per tensor
+    static_assert(kChunk * R % 4096 == 0, "whole 1 KiB loads per wave");
+    unsigned dma_off[kDmaPerWave];
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) {
+        const int byte = 1024 * (wave * kDmaPerWave + j) + 16 * lane;
+        const int row = byte / R, p = (byte - row * R) / 16;
+        dma_off[j] = (unsigned)(row * R + 16 * (p ^ swz<D>(row)));
+    }
+    const unsigned lds_base = (unsigned)(size_t)(lds_cptr)smem;
+    const int head_bytes = N * D * 2;
+    auto load_chunk = [&](int it, int buf) {
         size_t qoff;
         const int qc0 = chunk_rows(it, qoff);
-        rq.load(a.q + qoff * D, qc0, N);
-        rdo.load(a.dout + qoff * D, qc0, N);
+        const __amdgpu_buffer_rsrc_t rsq =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + qoff * D), (short)0, head_bytes, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rsdo =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.dout + qoff * D), (short)0, head_bytes, kRsrcWord3);
+        const unsigned row0 = (unsigned)qc0 * R;
+        const unsigned dst = lds_base + (unsigned)(buf * kBuf) + 1024u * (unsigned)(wave * kDmaPerWave);
+#pragma unroll
+        for (int j = 0; j < kDmaPerWave; ++j)
+            asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :
+                         : "v"(row0 + dma_off[j]), "s"(rsq), "{m0}"(dst + 1024u * j)
+                         : "memory");
+#pragma unroll
+        for (int j = 0; j < kDmaPerWave; ++j)
+            asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :
+                         : "v"(row0 + dma_off[j]), "s"(rsdo), "{m0}"(dst + (unsigned)S::kTile + 1024u * j)
+                         : "memory");
         if (threadIdx.x < kChunk) {
             const int qi = qc0 + threadIdx.x;
             rl = qi < N ? a.lse2[qoff + qi] : INFINITY;
             rd = qi < N ? a.dsum[qoff + qi] : 0.f;
         }
     };
+    // L and D into LDS; then this wave's loads into LDS are waited for (vmcnt counts the
+    // wave's vector loads in issue order) before the barrier that publishes the chunk
     auto store_chunk = [&](int buf) {
         unsigned char* base = smem + buf * kBuf;
-        rq.store(base);
-        rdo.store(base + S::kTile);
         if (threadIdx.x < kChunk) {
             reinterpret_cast<float*>(base + 2 * S::kTile)[threadIdx.x] = rl;
             reinterpret_cast<float*>(base + 2 * S::kTile)[kChunk + threadIdx.x] = rd;
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
     if (total > 0) {
-        load_chunk(0);
+        load_chunk(0, 0);
         store_chunk(0);
     }
     __syncthreads();
     for (int it = 0; it < total; ++it) {
-        if (it + 1 < total) load_chunk(it + 1);  // in flight during this chunk's products
+        // the other buffer was last read before the previous barrier
+        if (it + 1 < total) load_chunk(it + 1, (it + 1) & 1);  // in flight during this chunk's products
         size_t qoff_chunk;  // (the head's row base; the chunk's rows are already staged)
         const int qc0 = chunk_rows(it, qoff_chunk);
         const unsigned char* base = smem + (it & 1) * kBuf;
@@ -319,7 +357,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
                 }
             }
         }
-        // the other buffer was last read before the previous barrier
         if (it + 1 < total) store_chunk((it + 1) & 1);
         __syncthreads();
     }
