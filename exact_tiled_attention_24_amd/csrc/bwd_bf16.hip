@@ -67,32 +67,37 @@ __device__ __forceinline__ int swz(int r) {
     return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
-// A chunk of 32 rows x D bf16 travels global memory -> registers -> LDS (swizzled rows); the
-// registers let the next chunk's loads fly while the current chunk is computed. Thread i
-// holds the 16-byte pieces i, i + 256, ... of the chunk; rows past n read as zero.
+// A staged tile loaded straight from global memory into LDS (buffer_load ... lds, 1 KiB per
+// instruction, no registers held while the data flies). Instruction k fills tile bytes
+// 1024 k ..: lane l writes the 16 bytes at 1024 k + 16 l, i.e. row (1024 k + 16 l) / R at
+// chunk position p, so it loads that row's logical chunk p ^ swz(row). Rows past the end of
+// the descriptor's range read as zeros. Each of the 4 waves issues a quarter of the
+// instructions; the caller waits with s_waitcnt vmcnt before the barrier that publishes the
+// tile.
 template <int D, int SUB>
-struct ChunkRegs {
-    static constexpr int kChunk = Stage<D, SUB>::kChunk;
-    static constexpr int kPer = D * 2 / 16;  // 16-byte pieces per row
-    static constexpr int kPieces = kChunk * kPer / kThreads;
-    static_assert(kChunk * kPer % kThreads == 0, "whole pieces per thread");
-    u32x4 v[kPieces];
-    __device__ __forceinline__ void load(const uint16_t* src, int row0, int n) {
+struct TileDma {
+    static constexpr int kRow = Stage<D, SUB>::kRow;
+    static constexpr int kPerWave = Stage<D, SUB>::kTile / 1024 / 4;
+    static_assert(Stage<D, SUB>::kTile % 4096 == 0, "whole 1 KiB loads per wave");
+    unsigned off[kPerWave];  // this lane's byte offset in the tile's rows, per instruction
+    __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-        for (int p = 0; p < kPieces; ++p) {
-            const int i = threadIdx.x + kThreads * p;
-            const int r = i / kPer, c = i - r * kPer;
-            v[p] = u32x4{0u, 0u, 0u, 0u};
-            if (row0 + r < n) v[p] = *reinterpret_cast<const u32x4*>(src + (size_t)(row0 + r) * D + 8 * c);
+        for (int j = 0; j < kPerWave; ++j) {
+            const int byte = 1024 * (wave * kPerWave + j) + 16 * lane;
+            const int row = byte / kRow, p = (byte - row * kRow) / 16;
+            off[j] = (unsigned)(row * kRow + 16 * (p ^ swz<D>(row)));
         }
     }
-    __device__ __forceinline__ void store(unsigned char* dst) const {
+    // rows from byte row0 of the buffer r into the tile at LDS address lds_tile
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, unsigned row0, unsigned lds_tile,
+                                          int wave) const {
+        const unsigned dst = lds_tile + 1024u * (unsigned)(wave * kPerWave);
 #pragma unroll
-        for (int p = 0; p < kPieces; ++p) {
-            const int i = threadIdx.x + kThreads * p;
-            const int r = i / kPer, c = i - r * kPer;
-            *reinterpret_cast<u32x4*>(dst + r * Stage<D, SUB>::kRow + 16 * (c ^ swz<D>(r))) = v[p];
-        }
+        for (int j = 0; j < kPerWave; ++j)
+            asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :
+                         : "v"(row0 + off[j]), "s"(r), "{m0}"(dst + 1024u * j)
+                         : "memory");
     }
 };
 
@@ -235,22 +240,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
         qoff = ((size_t)b * a.Hq + kvh * G + g) * N;
         return q_first + (it - g * nch) * kChunk;
     };
-    // The Q and dO rows of a chunk go straight from global memory into LDS (buffer_load ...
-    // lds, 1 KiB per instruction, no registers held while they fly). Instruction k of a tensor
-    // fills tile bytes 1024 k ..: lane l writes the 16 bytes at 1024 k + 16 l, i.e. row
-    // (1024 k + 16 l) / R at chunk position p, so it loads that row's logical chunk
-    // p ^ swz(row). Rows past N lie beyond the descriptor's range and read as zeros. Each
-    // wave issues a quarter of each tensor's instructions; L and D go through registers.
+    // The Q and dO rows of a chunk go straight into LDS; L and D go through registers.
     constexpr int R = S::kRow;
-    constexpr int kDmaPerWave = kChunk * R / 1024 / 4;  // per tensor
-    static_assert(kChunk * R % 4096 == 0, "whole 1 KiB loads per wave");
-    unsigned dma_off[kDmaPerWave];
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) {
-        const int byte = 1024 * (wave * kDmaPerWave + j) + 16 * lane;
-        const int row = byte / R, p = (byte - row * R) / 16;
-        dma_off[j] = (unsigned)(row * R + 16 * (p ^ swz<D>(row)));
-    }
+    TileDma<D, kSub> dma;
+    dma.init(wave, lane);
     const unsigned lds_base = (unsigned)(size_t)(lds_cptr)smem;
     const int head_bytes = N * D * 2;
     auto load_chunk = [&](int it, int buf) {
@@ -260,20 +253,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
             __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + qoff * D), (short)0, head_bytes, kRsrcWord3);
         const __amdgpu_buffer_rsrc_t rsdo =
             __builtin_amdgcn_make_buffer_rsrc((void*)(a.dout + qoff * D), (short)0, head_bytes, kRsrcWord3);
-        const unsigned row0 = (unsigned)qc0 * R;
-        const unsigned dst = lds_base + (unsigned)(buf * kBuf) + 1024u * (unsigned)(wave * kDmaPerWave);
-#pragma unroll
-        for (int j = 0; j < kDmaPerWave; ++j)
-            asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
-                         :
-                         : "v"(row0 + dma_off[j]), "s"(rsq), "{m0}"(dst + 1024u * j)
-                         : "memory");
-#pragma unroll
-        for (int j = 0; j < kDmaPerWave; ++j)
-            asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
-                         :
-                         : "v"(row0 + dma_off[j]), "s"(rsdo), "{m0}"(dst + (unsigned)S::kTile + 1024u * j)
-                         : "memory");
+        const unsigned row0 = (unsigned)qc0 * R, tile = lds_base + (unsigned)(buf * kBuf);
+        dma.issue(rsq, row0, tile, wave);
+        dma.issue(rsdo, row0, tile + (unsigned)S::kTile, wave);
         if (threadIdx.x < kChunk) {
             const int qi = qc0 + threadIdx.x;
             rl = qi < N ? a.lse2[qoff + qi] : INFINITY;
@@ -418,21 +400,29 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
     const int k_end = a.causal ? min_(N, qb0 + kBlock) : N;  // keys past the block's last query
     const int total = (k_end + kChunk - 1) / kChunk;
-    ChunkRegs<D, kSub> rk, rv;
+    // K and V chunks go straight into LDS (two buffers, each: K chunk, V chunk)
+    TileDma<D, kSub> dma;
+    dma.init(wave, lane);
+    const unsigned lds_base = (unsigned)(size_t)(lds_cptr)smem;
+    const int head_bytes = N * D * 2;
+    const __amdgpu_buffer_rsrc_t rsk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + kvoff), (short)0, head_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rsv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + kvoff), (short)0, head_bytes, kRsrcWord3);
     auto load_chunk = [&](int it) {
-        rk.load(a.k + kvoff, it * kChunk, N);
-        rv.load(a.v + kvoff, it * kChunk, N);
+        const unsigned row0 = (unsigned)(it * kChunk * S::kRow);
+        const unsigned tile = lds_base + (unsigned)(2 * (it & 1) * S::kTile);
+        dma.issue(rsk, row0, tile, wave);
+        dma.issue(rsv, row0, tile + (unsigned)S::kTile, wave);
     };
-    auto store_chunk = [&](int buf) {
-        rk.store(smem + 2 * buf * S::kTile);
-        rv.store(smem + (2 * buf + 1) * S::kTile);
-    };
+    auto store_chunk = [&](int) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
     if (total > 0) {
         load_chunk(0);
         store_chunk(0);
     }
     __syncthreads();
     for (int it = 0; it < total; ++it) {
+        // the other buffer was last read before the previous barrier
         if (it + 1 < total) load_chunk(it + 1);  // in flight during this chunk's products
         const int kc0 = it * kChunk;
         lds_cptr const lk = (lds_cptr)(smem + 2 * (it & 1) * S::kTile);
