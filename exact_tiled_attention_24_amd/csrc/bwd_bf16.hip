@@ -10,12 +10,12 @@
 //  * bwd_prep: D_i and the log2-domain normaliser L_i = (m_i + ln l_i) log2 e of every query
 //    row, so that P = exp2(scale log2e q.k - L) (L = +inf for a row with no key: P = 0).
 //  * bwd_dkdv: one workgroup per (128-key block, KV head); each wave keeps its 32 keys' K and V
-//    in registers and walks the query chunks (64 rows of Q and dO staged in LDS, computed as
-//    two 32-row sub-chunks) of every query head of the KV group, accumulating dV^T and dK^T.
+//    in registers and walks the query chunks (32 rows of Q and dO staged in LDS) of every
+//    query head of the KV group, accumulating dV^T and dK^T.
 //  * bwd_dq: one workgroup per (128-query block, query head); each wave keeps its 32 queries'
 //    Q and dO in registers and walks the key chunks (32 rows of K and V in LDS).
-// Chunks are double-buffered: the next chunk's global loads go to registers before the current
-// chunk's products and to the other LDS buffer after them, with one barrier per chunk.
+// Chunks are double-buffered: the next chunk's rows load straight into the other LDS buffer
+// while the current chunk's products run, with one barrier per chunk.
 // All products use v_mfma_f32_32x32x16_bf16. As in the forward kernel, the score tile is
 // computed with the rows of its A operand read in an order that swaps bits 2 and 3 of the row
 // index, so that the accumulator, rounded to bf16, is directly the B operand of the next
@@ -28,9 +28,10 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;  // 4 waves
-// 32-row sub-chunks per staged chunk: two for dK/dV (their products interleave), one for dQ
-// (two would cost it its second wave per SIMD)
-constexpr int kSubKV = 2, kSubQ = 1;
+// 32-row sub-chunks per staged chunk: one in both kernels, so that each fits two waves per
+// SIMD (two sub-chunks in dK/dV interleave their products but leave it one wave per SIMD,
+// which measured slower)
+constexpr int kSubKV = 1, kSubQ = 1;
 constexpr int kBlock = 128;    // keys (dK/dV) or queries (dQ) per workgroup: 32 per wave
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -196,8 +197,9 @@ struct BwdArgs {
 };
 
 // ---- dK, dV: workgroup = 128 keys of one KV head; wave = 32 keys ----
+// (two waves per SIMD: the register budget is 256 per lane, with a small spill)
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     constexpr int kSub = kSubKV;
     using S = Stage<D, kSub>;
     constexpr int kChunk = S::kChunk;
