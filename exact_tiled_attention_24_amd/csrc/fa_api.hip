@@ -212,7 +212,8 @@ fa_status fa_bwd(fa_dtype dt, const void* q, const void* k, const void* v, const
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
         !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
         return FA_ERR_INVALID_ARGUMENT;
-    if ((long long)N * d >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    // a head's rows (N d bf16 values) are addressed with 32-bit signed byte counts
+    if ((long long)N * d * 2 >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
     if ((long long)B * Hq >= 65536 || ((long long)N + 127) / 128 >= (1LL << 31))
         return FA_ERR_UNSUPPORTED;  // grid y holds (batch, head)
     if (workspace_bytes < fa_bwd_workspace_bytes(B, Hq, N)) return FA_ERR_WORKSPACE_TOO_SMALL;

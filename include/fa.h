@@ -151,8 +151,8 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float
  * by several query heads receives the sum of their gradients. `causal` and `scale` must be the
  * forward's. float32 accumulation; dq, dk, dv rounded to bf16 once. Rows with l = 0 contribute
  * nothing. Supported: dt = FA_BF16; d in {64, 128}; Hq % Hkv == 0 (else
- * FA_ERR_INVALID_ARGUMENT); N * d < 2^31; B * Hq < 65536. B, Hq or N equal to 0 is a valid
- * empty call.
+ * FA_ERR_INVALID_ARGUMENT); N * d < 2^30 (a head's bytes fit a signed 32-bit count);
+ * B * Hq < 65536. B, Hq or N equal to 0 is a valid empty call.
  */
 fa_status fa_bwd(fa_dtype dt, const void* q, const void* k, const void* v, const void* o,
                  const void* dout, const float* m, const float* l, void* dq, void* dk, void* dv,

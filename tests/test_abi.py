@@ -230,6 +230,8 @@ def bwd(lib, dt=1, q=DEV, k=DEV, v=DEV, o=DEV, do=DEV, m=DEV, l=DEV, dq=DEV, dk=
     (dict(ws=NULL), fa.FA_ERR_INVALID_ARGUMENT),
     (dict(dq=MIS), fa.FA_ERR_INVALID_ARGUMENT),
     (dict(ws_bytes=2 * 4 * 300 * 4 - 1), fa.FA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(N=1 << 23), fa.FA_ERR_UNSUPPORTED),            # N d = 2^30
+    (dict(N=1 << 23, d=64), fa.FA_ERR_WORKSPACE_TOO_SMALL),  # N d = 2^29 passes the size check
     (dict(B=0, q=NULL), fa.FA_OK),
 ])
 def test_bwd_validation(kwargs, code):
