@@ -292,6 +292,12 @@ def fa_bwd(q, k, v, o, dout, m, l, scale=None, causal=False, workspace=None):
         raise ValueError("shape mismatch")
     if m.shape != (B, Hq, N) or l.shape != (B, Hq, N) or m.dtype != torch.float32 or l.dtype != torch.float32:
         raise ValueError("m and l must be float32 [B, Hq, N]")
+    if q.dtype != torch.bfloat16:
+        raise TypeError(f"fa_bwd takes bfloat16 tensors, got q of dtype {q.dtype}")
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}; fa_bwd needs every tensor in q's dtype "
+                            f"({q.dtype})")
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)

@@ -18,8 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ("fa_api.hip", "fwd_bf16.hip", "fwd_bf16_sp.hip", "fwd_f32.hip", "decode.hip", "decode_mx.hip", "merge.hip",
-           "bwd_bf16.hip")
+SOURCES = ("fa_api.hip", "fwd_bf16_sp.hip", "fwd_f32.hip", "decode_mx.hip", "merge.hip", "bwd_bf16.hip")
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are disabled for all device code.

@@ -28,11 +28,18 @@
 //    behind them may hold anything).
 //  * Softmax per query: one exchange with lanes l ^ 16 and l ^ 32 gives the page maximum; the
 //    exponent reference moves only when it is beaten by more than 2^8 (then O is rescaled).
-//  * At the end the waves' states are merged through LDS and one normalised float32 partial
-//    (m in log2 units, l, O) per (chunk, query head) is written to the workspace; the merge
-//    kernel (merge.hip) combines the chunks.
-#include <stdio.h>
-#include <stdlib.h>
+//  * At the end the waves' states are merged through LDS. A sequence of one chunk writes its
+//    output directly. Otherwise each chunk writes a normalised float32 partial (m in log2
+//    units, l, O) per query head to the workspace and counts itself done on the completion
+//    word of its (sequence, KV head); the last chunk to arrive merges the partials with the
+//    same rule, in chunk order (so the result does not depend on which chunk is last), and
+//    writes the output. No second launch.
+//  * The completion word holds a tag of the call in its high bits and the arrivals in the low
+//    bits: an arrival that finds another tag counts as the first, so the words need no
+//    clearing between calls and the workspace contents on entry do not matter.
+#include <atomic>
+#include <mutex>
+#include <random>
 
 #include "fa_internal.hpp"
 #include "gfx950.hpp"
@@ -48,6 +55,11 @@ constexpr int kSlot = 2 * kPiece;               // K then V
 constexpr int kLoadsPerPage = 2 * kPiece / 1024;  // 1 KiB per load instruction
 constexpr float kTau = 8.f;                     // lazy-rescale threshold, log2 units
 constexpr int kBufferDword3 = 0x00020000;
+constexpr int kWaves = 4;                       // waves per workgroup
+constexpr int kSlots = 2;                       // page slots per wave (one page in flight)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCountBits = 24;                  // completion word: tag << 24 | arrivals
+constexpr unsigned long long kCountMask = (1ull << kCountBits) - 1;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -63,19 +75,53 @@ __device__ __forceinline__ float xlane_sum(float x) {
     return x + __shfl_xor(x, 32);
 }
 
-// W waves per workgroup, S page slots per wave (S - 1 pages in flight while one is consumed).
-template <int W, int S>
-__global__ __launch_bounds__(64 * W) void decode_mx_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, const int32_t* __restrict__ table,
-    const int32_t* __restrict__ lens, float* __restrict__ ws_o, float* __restrict__ ws_m,
-    float* __restrict__ ws_l, int Hq, int Hkv, int G, int num_pages, int max_pages,
-    int len_cap, float scale_log2, int chunk_pages) {
-    constexpr int kWaves = W, kSlots = S, kThreads = 64 * W;
-    static_assert(S >= 2 && (S - 1) * kLoadsPerPage <= 63, "vmcnt holds at most 63 loads");
+struct DecodeArgs {
+    const uint16_t* q;
+    const uint16_t* kc;
+    const uint16_t* vc;
+    const int32_t* table;
+    const int32_t* lens;
+    uint16_t* o;
+    float* ws_o;                // partial O [S][B * Hq][d], normalised
+    float* ws_m;                // partial m [S][B * Hq], log2 units
+    float* ws_l;                // partial l [S][B * Hq]
+    unsigned long long* done;   // completion words [B * Hkv]
+    unsigned long long tag;     // this call's tag, < 2^40
+    int Hq, Hkv, G, num_pages, max_pages, len_cap, chunk_pages;
+    float scale_log2;
+};
+
+// Counts one arrival on a completion word and reports whether it was the n-th of this call.
+// Vector (global) atomics at device scope, relaxed: the caller orders the partials around it
+// with explicit fences. The loop ends because every failed exchange means another
+// workgroup's arrival succeeded.
+__device__ bool arrive(unsigned long long* word, unsigned long long tag, int n) {
+    unsigned long long old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+        const unsigned long long cnt = (old >> kCountBits) == tag ? (old & kCountMask) : 0;
+        const unsigned long long next = (tag << kCountBits) | (cnt + 1);
+        if (__hip_atomic_compare_exchange_strong(word, &old, next, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            return cnt + 1 == (unsigned long long)n;
+    }
+}
+
+// Partial values go through device-scope stores and loads: coherent across the XCDs' L2s
+// on their own, without a cache write-back or invalidate.
+__device__ __forceinline__ void publish(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float collect(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(kThreads) void decode_mx_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * kSlots * kSlot];
+    __shared__ int last_flag;
     lds_cptr const lds = (lds_cptr)smem;
     const unsigned lds_addr = (unsigned)(size_t)lds;
+    const int Hq = a.Hq, Hkv = a.Hkv, G = a.G, num_pages = a.num_pages;
+    const float scale_log2 = a.scale_log2;
 
     // x = sequence x KV head (KV head fastest: the KV heads of one page sit next to each
     // other in memory and are streamed side by side), y = chunk
@@ -86,14 +132,16 @@ __global__ __launch_bounds__(64 * W) void decode_mx_kernel(
     const int R = gridDim.x / Hkv * Hq;  // B * Hq
     const int row0 = b * Hq + kvh * G;
 
-    int L = lens[b];
-    L = L < 0 ? 0 : (L > len_cap ? len_cap : L);
+    int L = a.lens[b];
+    L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
     const int npages = (L + kPage - 1) / kPage;
     // This sequence gets ceil(npages / chunk_pages) chunks of near-equal size (they differ by
-    // at most one page); splits past the sequence's chunk count are empty.
-    const int n_chunks = (npages + chunk_pages - 1) / chunk_pages;
-    const int p_begin = split < n_chunks ? (int)((long long)split * npages / n_chunks) : npages;
-    const int p_end = split < n_chunks ? (int)((long long)(split + 1) * npages / n_chunks) : npages;
+    // at most one page). Workgroups past its chunk count have nothing to do; an empty
+    // sequence keeps chunk 0, which writes O = 0.
+    const int n_chunks = (npages + a.chunk_pages - 1) / a.chunk_pages;
+    if (split >= max_(n_chunks, 1)) return;
+    const int p_begin = n_chunks > 0 ? (int)((long long)split * npages / n_chunks) : 0;
+    const int p_end = n_chunks > 0 ? (int)((long long)(split + 1) * npages / n_chunks) : 0;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -116,7 +164,7 @@ __global__ __launch_bounds__(64 * W) void decode_mx_kernel(
         for (int m = 0; m < kD / 32; ++m) {
             qb[m] = bf16x8{};
             if (l16 < G)
-                qb[m] = *reinterpret_cast<const bf16x8*>(q + (size_t)(row0 + l16) * kD + 32 * m + 8 * g4);
+                qb[m] = *reinterpret_cast<const bf16x8*>(a.q + (size_t)(row0 + l16) * kD + 32 * m + 8 * g4);
         }
 #pragma unroll
         for (int m = 0; m < kD / 32; ++m) asm volatile("" : "+v"(qb[m]));
@@ -146,7 +194,7 @@ __global__ __launch_bounds__(64 * W) void decode_mx_kernel(
         }
 
         const size_t page_stride = (size_t)Hkv * kPage * kD;  // elements per physical page
-        const int32_t* trow = table + (size_t)b * max_pages;
+        const int32_t* trow = a.table + (size_t)b * a.max_pages;
         const unsigned wave_lds = lds_addr + wave * kSlots * kSlot;
         // Block-table entries of this wave's pages, 64 at a time, read back with v_readlane
         // (scalar page bases). `ent` covers pages [w0, w0 + 64) of the wave's list.
@@ -171,9 +219,9 @@ __global__ __launch_bounds__(64 * W) void decode_mx_kernel(
             const size_t off = ((size_t)(ok ? phys : 0) * page_stride + (size_t)kvh * kPage * kD);
             const int bytes = __builtin_amdgcn_readfirstlane(ok ? kPiece : 0);
             const __amdgpu_buffer_rsrc_t rk =
-                __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, bytes, kBufferDword3);
+                __builtin_amdgcn_make_buffer_rsrc((void*)(a.kc + off), (short)0, bytes, kBufferDword3);
             const __amdgpu_buffer_rsrc_t rv =
-                __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, bytes, kBufferDword3);
+                __builtin_amdgcn_make_buffer_rsrc((void*)(a.vc + off), (short)0, bytes, kBufferDword3);
             const unsigned dst = wave_lds + s * kSlot;
 #pragma unroll
             for (int c = 0; c < kPiece / 1024; ++c)
@@ -220,9 +268,9 @@ __global__ __launch_bounds__(64 * W) void decode_mx_kernel(
                 m_ref = m_new;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float a = __shfl(alpha, 4 * g4 + r);
+                    const float f = __shfl(alpha, 4 * g4 + r);
 #pragma unroll
-                    for (int blk = 0; blk < kD / 16; ++blk) acc[blk][r] *= a;
+                    for (int blk = 0; blk < kD / 16; ++blk) acc[blk][r] *= f;
                 }
             }
             float p[4];
@@ -276,8 +324,7 @@ __global__ __launch_bounds__(64 * W) void decode_mx_kernel(
     }
     __syncthreads();  // the slots are reused below
 
-    // ---- merge the waves (lanes of a query: l16 = g, all g4) and write this chunk's
-    // normalised partial ----
+    // ---- merge the waves (lanes of a query: l16 = g, all g4) ----
     float* sm_o = reinterpret_cast<float*>(smem);          // [wave][query][kD]
     float* sm_m = sm_o + kWaves * kQ * kD;                  // [wave][query]
     float* sm_l = sm_m + kWaves * kQ;
@@ -296,6 +343,7 @@ __global__ __launch_bounds__(64 * W) void decode_mx_kernel(
         }
     }
     __syncthreads();
+    // This chunk's (m, l, O) per query head: thread idx handles (g, d) = divmod(idx, kD).
     for (int idx = tid; idx < G * kD; idx += kThreads) {
         const int g = idx / kD;
         const int d = idx - g * kD;
@@ -314,13 +362,84 @@ __global__ __launch_bounds__(64 * W) void decode_mx_kernel(
                 ot = __builtin_fmaf(rs, sm_o[(w * kQ + g) * kD + d], ot);
             }
         }
-        const size_t prow = (size_t)split * R + row0 + g;
-        ws_o[prow * kD + d] = lt > 0.f ? ot / lt : 0.f;
-        if (d == 0) {
-            ws_m[prow] = lt > 0.f ? m : -INFINITY;
-            ws_l[prow] = lt;
+        const float od = lt > 0.f ? ot / lt : 0.f;
+        if (n_chunks <= 1) {
+            // the sequence's only chunk: this is the output
+            a.o[(size_t)(row0 + g) * kD + d] = (uint16_t)(pack_bf16x2(od, 0.f) & 0xffffu);
+        } else {
+            const size_t prow = (size_t)split * R + row0 + g;
+            publish(a.ws_o + prow * kD + d, od);
+            if (d == 0) {
+                publish(a.ws_m + prow, lt > 0.f ? m : -INFINITY);
+                publish(a.ws_l + prow, lt);
+            }
         }
     }
+    if (n_chunks <= 1) return;
+
+    // ---- count this chunk done; the last of the (sequence, KV head) merges ----
+    // The partials were written with device-scope stores, which complete only once they are
+    // visible to every XCD; each wave waits for its own, so after the barrier the whole
+    // partial is visible before the arrival is counted. The merging workgroup reads the
+    // partials with device-scope loads, which do not hit stale lines of its XCD's L2. (A
+    // device-scope release / acquire pair would write back and invalidate whole L2s, which
+    // stalls the XCDs while other workgroups still stream.)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) last_flag = arrive(a.done + bk, a.tag, n_chunks) ? 1 : 0;
+    __syncthreads();
+    if (!last_flag) return;
+
+    // m = max_s m_s over the partials that hold weight; w_s = l_s 2^(m_s - m);
+    // O = sum_s w_s O_s / sum_s w_s, taken in chunk order (the result does not depend on
+    // which chunk arrived last). Chunks go in groups of 8 whose loads are issued together; a
+    // group that raises the maximum rescales the running sums.
+    constexpr int kGroup = 8;
+    for (int idx = tid; idx < G * kD; idx += kThreads) {
+        const int g = idx / kD, d = idx - g * kD;
+        const size_t row = (size_t)row0 + g;
+        float M = -INFINITY, lt = 0.f, ot = 0.f;
+        for (int s0 = 0; s0 < n_chunks; s0 += kGroup) {
+            float ms[kGroup], ls[kGroup], os[kGroup];
+#pragma unroll
+            for (int j = 0; j < kGroup; ++j) {
+                const size_t prow = (size_t)min_(s0 + j, n_chunks - 1) * R + row;  // (clamped)
+                ms[j] = collect(a.ws_m + prow);
+                ls[j] = collect(a.ws_l + prow);
+                os[j] = collect(a.ws_o + prow * kD + d);
+            }
+            float mb = M;
+#pragma unroll
+            for (int j = 0; j < kGroup; ++j)
+                if (s0 + j < n_chunks && ls[j] > 0.f) mb = fmaxf(mb, ms[j]);
+            if (mb == -INFINITY) continue;
+            const float f = M == -INFINITY ? 0.f : exp2_hw(M - mb);
+            lt *= f;
+            ot *= f;
+#pragma unroll
+            for (int j = 0; j < kGroup; ++j) {
+                if (s0 + j < n_chunks && ls[j] > 0.f) {
+                    const float w = ls[j] * exp2_hw(ms[j] - mb);
+                    lt += w;
+                    ot = __builtin_fmaf(w, os[j], ot);
+                }
+            }
+            M = mb;
+        }
+        const float od = lt > 0.f ? ot / lt : 0.f;
+        a.o[row * kD + d] = (uint16_t)(pack_bf16x2(od, 0.f) & 0xffffu);
+    }
+}
+
+// A tag no earlier call of this process used: a per-process random start plus a call count,
+// kept to 40 bits (the completion word's high bits).
+unsigned long long next_tag() {
+    static std::atomic<unsigned long long> count{0};
+    static const unsigned long long start = [] {
+        std::random_device rd;
+        return ((unsigned long long)rd() << 32) ^ rd();
+    }();
+    return (start + count.fetch_add(1, std::memory_order_relaxed)) & ((1ull << 40) - 1);
 }
 
 }  // namespace
@@ -329,27 +448,27 @@ hipError_t launch_decode_bf16_mx(const void* q, const void* k_cache, const void*
                                  const int32_t* block_table, const int32_t* seq_lens, void* o,
                                  int B, int Hq, int Hkv, int d, int num_pages,
                                  int max_pages_per_seq, int len_cap, float scale, int splits,
-                                 int chunk_pages, float* ws_o, float* ws_m, float* ws_l,
-                                 hipStream_t stream) {
+                                 int chunk_pages, const DecodeWorkspace& ws, hipStream_t stream) {
     (void)d;
-    const dim3 grid((unsigned)(B * Hkv), (unsigned)splits);
-    int W = 4, S = 2;
-    if (const char* e = getenv("FA_DECODE_MX")) sscanf(e, "%d,%d", &W, &S);
-#define FA_MX_CASE(w, s)                                                                         \
-    if (W == w && S == s) {                                                                      \
-        hipLaunchKernelGGL((decode_mx_kernel<w, s>), grid, dim3(64 * w), 0, stream,              \
-                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache), \
-                           static_cast<const uint16_t*>(v_cache), block_table, seq_lens, ws_o,   \
-                           ws_m, ws_l, Hq, Hkv, Hq / Hkv, num_pages, max_pages_per_seq, len_cap, \
-                           scale * kLog2e, chunk_pages);                                         \
-    } else
-    FA_MX_CASE(2, 3) FA_MX_CASE(2, 4) FA_MX_CASE(3, 3) FA_MX_CASE(3, 4) FA_MX_CASE(4, 3)
-    FA_MX_CASE(4, 4) FA_MX_CASE(5, 4) FA_MX_CASE(6, 3) FA_MX_CASE(8, 2) FA_MX_CASE(4, 2)
-    return hipErrorInvalidValue;
-#undef FA_MX_CASE
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_merge(ws_o, ws_m, ws_l, o, 1, nullptr, nullptr, splits, B * Hq, kD, 1, stream);
+    DecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.kc = static_cast<const uint16_t*>(k_cache);
+    a.vc = static_cast<const uint16_t*>(v_cache);
+    a.table = block_table;
+    a.lens = seq_lens;
+    a.o = static_cast<uint16_t*>(o);
+    a.ws_o = ws.o;
+    a.ws_m = ws.m;
+    a.ws_l = ws.l;
+    a.done = ws.done;
+    a.tag = next_tag();
+    a.Hq = Hq, a.Hkv = Hkv, a.G = Hq / Hkv;
+    a.num_pages = num_pages, a.max_pages = max_pages_per_seq, a.len_cap = len_cap;
+    a.chunk_pages = chunk_pages;
+    a.scale_log2 = scale * kLog2e;
+    hipLaunchKernelGGL(decode_mx_kernel, dim3((unsigned)(B * Hkv), (unsigned)splits),
+                       dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace fa

@@ -2,6 +2,8 @@
 // kernel dispatch. Validation happens before any HIP call, so a rejected request neither
 // touches the device nor needs one.
 #include <math.h>
+
+#include <atomic>
 #include <stdlib.h>
 #include <string.h>
 
@@ -12,18 +14,11 @@ namespace {
 
 constexpr int kDecodePage = 16;
 constexpr int kDecodeD = 128;
-constexpr int kDecodeTargetWGs = 2 * fa::kPlanCUs;  // one round of 4-wave chunks
 
-// Forward kernel choice. Default: the software-pipelined, persistent 8-wave kernel (faster
-// for d = 128 and d = 64 alike). The environment variable FA_FWD_KERNEL=tiled|sp selects
-// one explicitly (a tuning and testing switch, read at every call).
-enum FwdKernel { kFwdAuto = 0, kFwdTiled = 1, kFwdSoftPipe = 2 };
-FwdKernel fwd_kernel_override() {
-    const char* e = getenv("FA_FWD_KERNEL");
-    if (e && strcmp(e, "tiled") == 0) return kFwdTiled;
-    if (e && strcmp(e, "sp") == 0) return kFwdSoftPipe;
-    return kFwdAuto;
-}
+// The bf16 forward kernels address one head's K or V rows with 32-bit byte offsets and keep
+// offsets at or above 2^31 (and, block-sparse, at 2^30) as "past the range" markers, so a
+// head's rows may span at most 2^30 bytes: N d <= 2^29 (4M tokens at d = 128).
+bool head_fits(long long N, long long d) { return N * d * 2 <= (1LL << 30); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
@@ -35,10 +30,11 @@ struct DecodePlan {
     int bound;         // upper bound of `splits` over every Hkv >= 1 and shorter tables
 };
 
-// Chunks for the longest sequence: enough workgroups to fill the CUs several times, since
-// with few (sequence, KV head) pairs most CUs would otherwise idle; never more chunks than
-// pages. A fixed plan keeps results deterministic.
+// Chunks for the longest sequence: about two workgroups per CU of the device (one round of
+// 4-wave chunks), since with few (sequence, KV head) pairs most CUs would otherwise idle;
+// never more chunks than pages. A fixed plan keeps results deterministic.
 DecodePlan plan_decode(int B, int Hkv, int max_pages_per_seq, int max_seq_len, int num_splits) {
+    const long long target_wgs = 2LL * fa::device_cus();
     DecodePlan p;
     const long long cap = (long long)max_pages_per_seq * kDecodePage;
     p.len_cap = (int)(max_seq_len < cap ? max_seq_len : cap);
@@ -48,7 +44,7 @@ DecodePlan plan_decode(int B, int Hkv, int max_pages_per_seq, int max_seq_len, i
         s = num_splits;
     } else {
         const long long units = (long long)B * Hkv;
-        s = units > 0 ? (int)((kDecodeTargetWGs + units - 1) / units) : 1;
+        s = units > 0 ? (int)((target_wgs + units - 1) / units) : 1;
     }
     if (s > pages) s = pages;
     if (s < 1) s = 1;
@@ -58,12 +54,39 @@ DecodePlan plan_decode(int B, int Hkv, int max_pages_per_seq, int max_seq_len, i
     return p;
 }
 
-// Partials: O [S][B*Hq][d], then m [S][B*Hq], then l [S][B*Hq], all float32.
+// Workspace: completion words (one 8-byte word per query head, enough for every KV head),
+// then the partials O [S][B*Hq][d], m [S][B*Hq] and l [S][B*Hq], all float32.
+size_t decode_done_bytes(int B, int Hq) { return (size_t)B * (size_t)Hq * 8; }
 size_t decode_ws_bytes(int B, int Hq, int d, int splits) {
-    return (size_t)splits * (size_t)B * (size_t)Hq * ((size_t)d + 2) * sizeof(float);
+    return decode_done_bytes(B, Hq) +
+           (size_t)splits * (size_t)B * (size_t)Hq * ((size_t)d + 2) * sizeof(float);
+}
+fa::DecodeWorkspace decode_ws_layout(void* ws, int B, int Hq, int d, int splits) {
+    fa::DecodeWorkspace w;
+    w.done = static_cast<unsigned long long*>(ws);
+    w.o = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + decode_done_bytes(B, Hq));
+    w.m = w.o + (size_t)splits * B * Hq * d;
+    w.l = w.m + (size_t)splits * B * Hq;
+    return w;
 }
 
 }  // namespace
+
+namespace fa {
+int device_cus() {
+    static std::atomic<int> cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kDefaultCUs;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n < 8)
+            n = kDefaultCUs;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+}  // namespace fa
 
 extern "C" {
 
@@ -89,7 +112,8 @@ fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void*
     if (B == 0 || Hq == 0 || N == 0) return FA_OK;
     if (!q || !k || !v || !o) return FA_ERR_INVALID_ARGUMENT;
     if ((long long)N * d >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
-    const long long rows_per_wg = dt == FA_BF16 ? 128 : 64;
+    if (dt == FA_BF16 && !head_fits(N, d)) return FA_ERR_UNSUPPORTED;
+    const long long rows_per_wg = dt == FA_BF16 ? 256 : 64;
     if (((long long)N + rows_per_wg - 1) / rows_per_wg * B * Hq >= (1LL << 31))
         return FA_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -97,13 +121,8 @@ fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void*
     if (dt == FA_BF16) {
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
             return FA_ERR_INVALID_ARGUMENT;
-        FwdKernel kern = fwd_kernel_override();
-        if (kern == kFwdAuto) kern = kFwdSoftPipe;
-        e = kern == kFwdSoftPipe
-                ? fa::launch_fwd_bf16_sp(q, k, v, o, m_out, l_out, B, Hq, Hkv, N, d, scale,
-                                         causal ? 1 : 0, st)
-                : fa::launch_fwd_bf16(q, k, v, o, m_out, l_out, B, Hq, Hkv, N, d, scale,
-                                      causal ? 1 : 0, st);
+        e = fa::launch_fwd_bf16_sp(q, k, v, o, m_out, l_out, B, Hq, Hkv, N, d, scale,
+                                   causal ? 1 : 0, st);
     } else {
         e = fa::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                static_cast<const float*>(v), static_cast<float*>(o), m_out, l_out,
@@ -155,22 +174,10 @@ fa_status fa_decode_splitk(fa_dtype dt, const void* q, const void* k_cache, cons
     const DecodePlan p = plan_decode(B, Hkv, max_pages_per_seq, max_seq_len, num_splits);
     const size_t need = decode_ws_bytes(B, Hq, d, p.splits);
     if (workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
-    float* ws_o = static_cast<float*>(workspace);
-    float* ws_m = ws_o + (size_t)p.splits * B * Hq * d;
-    float* ws_l = ws_m + (size_t)p.splits * B * Hq;
-    // Decode kernel: the matrix-core one by default; FA_DECODE_KERNEL=valu selects the vector
-    // ALU one (a tuning and testing switch, read at every call).
-    const char* dk = getenv("FA_DECODE_KERNEL");
-    const bool valu = dk && strcmp(dk, "valu") == 0;
-    const hipError_t e =
-        valu ? fa::launch_decode_bf16(q, k_cache, v_cache, block_table, seq_lens, o, B, Hq, Hkv,
-                                      d, num_pages, max_pages_per_seq, p.len_cap, scale,
-                                      p.splits, p.chunk_pages, ws_o, ws_m, ws_l,
-                                      static_cast<hipStream_t>(stream))
-             : fa::launch_decode_bf16_mx(q, k_cache, v_cache, block_table, seq_lens, o, B, Hq,
-                                         Hkv, d, num_pages, max_pages_per_seq, p.len_cap, scale,
-                                         p.splits, p.chunk_pages, ws_o, ws_m, ws_l,
-                                         static_cast<hipStream_t>(stream));
+    const hipError_t e = fa::launch_decode_bf16_mx(
+        q, k_cache, v_cache, block_table, seq_lens, o, B, Hq, Hkv, d, num_pages, max_pages_per_seq,
+        p.len_cap, scale, p.splits, p.chunk_pages, decode_ws_layout(workspace, B, Hq, d, p.splits),
+        static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -185,7 +192,7 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float
     if (!q || !k || !v || !o) return FA_ERR_INVALID_ARGUMENT;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return FA_ERR_INVALID_ARGUMENT;
-    if ((long long)N * d * 2 >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    if (!head_fits(N, d)) return FA_ERR_UNSUPPORTED;
     if (((long long)N + 255) / 256 * B * Hq >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
     const hipError_t e = fa::launch_fwd_fp8qk_sp(q, k, v, o, m_out, l_out, B, Hq, Hkv, N, d, scale,
                                                  causal ? 1 : 0, static_cast<hipStream_t>(stream));
@@ -239,7 +246,7 @@ fa_status fa_fwd_block_sparse(fa_dtype dt, const void* q, const void* k, const v
         return FA_ERR_INVALID_ARGUMENT;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return FA_ERR_INVALID_ARGUMENT;
-    if ((long long)N * d >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    if (!head_fits(N, d)) return FA_ERR_UNSUPPORTED;
     if (((long long)N + 255) / 256 * B * Hq >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
     const hipError_t e = fa::launch_fwd_bf16_sp_block_sparse(
         q, k, v, o, m_out, l_out, block_offsets, block_indices, nnz, B, Hq, Hkv, N, d, scale,
@@ -265,7 +272,7 @@ fa_status fa_fwd_paged(fa_dtype dt, const void* q, const void* k_cache, const vo
     if (num_pages > 0 && (!k_cache || !v_cache)) return FA_ERR_INVALID_ARGUMENT;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
         return FA_ERR_INVALID_ARGUMENT;
-    if ((long long)Nq * d >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    if (!head_fits(Nq, d)) return FA_ERR_UNSUPPORTED;
     if (((long long)Nq + 255) / 256 * B * Hq >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
     if ((long long)max_pages_per_seq * page_size >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
     // the kernel addresses each cache with 32-bit byte offsets below 2^31

@@ -9,12 +9,11 @@
 
 namespace fa {
 
-// Number of compute units the split plan targets (MI355X: 256 CUs in 8 XCDs).
-constexpr int kPlanCUs = 256;
+// Compute units assumed when the device cannot be queried (MI355X: 256 CUs in 8 XCDs).
+constexpr int kDefaultCUs = 256;
 
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* m_out,
-                           float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
-                           int causal, hipStream_t stream);
+// Compute units of the current device, queried once per device and cached.
+int device_cus();
 
 // Software-pipelined: 8 waves, 256 query rows; MFMAs of neighbouring half tiles overlap
 // each half tile's softmax within every wave.
@@ -56,21 +55,23 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
                           int causal, hipStream_t stream);
 
-// Split-K paged decode: writes float32 partials (log2-domain m) for `splits` chunks of
-// `chunk_pages` pages per (sequence, KV head) into the workspace, then merges them into o.
-hipError_t launch_decode_bf16(const void* q, const void* k_cache, const void* v_cache,
-                              const int32_t* block_table, const int32_t* seq_lens, void* o,
-                              int B, int Hq, int Hkv, int d, int num_pages, int max_pages_per_seq,
-                              int len_cap, float scale, int splits, int chunk_pages,
-                              float* ws_o, float* ws_m, float* ws_l, hipStream_t stream);
+// Caller workspace of the split-K decode: completion words [B * Hkv] (any contents), then
+// float32 partials O [S][B * Hq][d], m [S][B * Hq] (log2 units), l [S][B * Hq].
+struct DecodeWorkspace {
+    unsigned long long* done;
+    float* o;
+    float* m;
+    float* l;
+};
 
-// The same with both products on the matrix cores (query heads per KV head <= 16).
+// Split-K paged decode with both products on the matrix cores (query heads per KV head
+// <= 16): each chunk of `chunk_pages` pages of a (sequence, KV head) yields a partial, and
+// the last chunk to finish merges them into o, in the same launch.
 hipError_t launch_decode_bf16_mx(const void* q, const void* k_cache, const void* v_cache,
                                  const int32_t* block_table, const int32_t* seq_lens, void* o,
                                  int B, int Hq, int Hkv, int d, int num_pages,
                                  int max_pages_per_seq, int len_cap, float scale, int splits,
-                                 int chunk_pages, float* ws_o, float* ws_m, float* ws_l,
-                                 hipStream_t stream);
+                                 int chunk_pages, const DecodeWorkspace& ws, hipStream_t stream);
 
 // Row-wise merge of S partials. log2_units != 0: m is in log2 units (internal workspace);
 // otherwise natural-log units (public fa_merge). out_bf16 selects the output type.

@@ -74,7 +74,9 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;  // query rows per workgroup
 constexpr int kBc = 64;           // keys per tile (two 32-key half tiles)
-constexpr int kPadOffset = 1 << 30;  // buffer offset beyond every tile descriptor's range
+// Buffer offset past every descriptor's range: a head's K or V rows span at most 2^30 bytes
+// (and a paged cache less than 2^31), and a pad offset plus any tile offset stays below 2^32.
+constexpr unsigned kPadOffset = 0x80000000u;
 constexpr int kStages = 4;       // LDS stages of K and of V
 constexpr int kXcds = 8;
 constexpr float kLazy = 8.f;
@@ -269,7 +271,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     // fetch nothing and fill zeros (as do the negative tile offsets of the prologue).
     // Paged: chunk c of a stage belongs to page c / (chunks per page) of the tile (the same
     // for all lanes: wave-uniform); the lane offset is relative to that page's 16 x d block.
-    int dma_src[T::kDmaPerWave];
+    unsigned dma_src[T::kDmaPerWave];
     unsigned dma_dst[T::kDmaPerWave];
     int dma_pg[T::kDmaPerWave];
 #pragma unroll
@@ -284,13 +286,13 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
             dma_pg[i] = cc / cpp;
             const int slot = 1024 * (cc - dma_pg[i] * cpp) + 16 * lane;
             const int row = slot / row_b, col = slot - row * row_b;
-            dma_src[i] = row < kPageTok && col < D * 2 ? row * D * 2 + col : kPadOffset;
+            dma_src[i] = row < kPageTok && col < D * 2 ? unsigned(row * D * 2 + col) : kPadOffset;
         } else {
             const int slot = 1024 * cc + 16 * lane;
             const int row = slot / row_b, col = slot - row * row_b;
             const int rb = is_k ? D * T::kKElem : D * 2;  // HBM row bytes
-            dma_src[i] = (col < rb ? row * rb + col : kPadOffset) +
-                         (kSparse ? 0 : (is_k ? 3 * kKTile : 2 * kVTile));
+            dma_src[i] = (col < rb ? unsigned(row * rb + col) : kPadOffset) +
+                         unsigned(kSparse ? 0 : (is_k ? 3 * kKTile : 2 * kVTile));
             dma_pg[i] = 0;
         }
     }
@@ -302,7 +304,9 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     // K tile) always lies in it too; the next window's table entries are loaded one tile
     // before they are needed. Rows of the last page past the sequence end are cut per lane
     // in the V loads (K rows there only meet masked scores).
-    constexpr unsigned kPagePad = 0x80000000u;  // an offset past every descriptor's range
+    // (block-sparse: 2^30, past a head's rows and below the pad offset, so pad + 2^30 stays
+    // past the range as well; paged: 2^31, past the cache, with pad lanes cut separately)
+    constexpr unsigned kPagePad = kSparse ? 0x40000000u : 0x80000000u;
     const int p_last = (Nk - 1) / kPageTok;                          // last page holding a row
     const int last_bytes = (Nk - kPageTok * p_last) * D * 2;         // its rows, in bytes
     const unsigned stride_bytes = (unsigned)Hkv * kPageTok * D * 2;  // one physical page
@@ -385,12 +389,11 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
             // page 4 t + pg of the sequence, t = j + 3 (K) or j + 2 (V)
             const int pg = dma_pg[i];
             const unsigned po = __builtin_amdgcn_readlane(win, (is_k ? kidx : vidx) + pg);
-            unsigned src = (unsigned)dma_src[i] + po;
-            if (!all_k) {
-                const int page = 4 * (j + (is_k ? 3 : 2)) + pg;
-                const unsigned lim = !is_k && page == p_last ? (unsigned)last_bytes : 0xffffffffu;
-                src = (unsigned)dma_src[i] < lim ? src : kPagePad;
-            }
+            // (pad lanes, and V rows past the end of the last page, take the out-of-range
+            // offset: a pad offset plus a page offset could wrap back into the cache)
+            const int page = 4 * (j + (is_k ? 3 : 2)) + pg;
+            const unsigned lim = !all_k && !is_k && page == p_last ? (unsigned)last_bytes : kPadOffset;
+            const unsigned src = dma_src[i] < lim ? dma_src[i] + po : kPagePad;
             const __amdgpu_buffer_rsrc_t r = is_k ? rsrc_k : rsrc_v;
             asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                          :
@@ -402,13 +405,14 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
             const __amdgpu_buffer_rsrc_t r = is_k ? rsrc_k : rsrc_v;
             asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                          :
-                         : "v"((unsigned)dma_src[i] + po), "s"(r), "{m0}"(dma_dst[i] + stage)
+                         : "v"(dma_src[i] + po), "s"(r), "{m0}"(dma_dst[i] + stage)
                          : "memory");
         } else {
             const __amdgpu_buffer_rsrc_t r = is_k ? rsrc_k : rsrc_v;
             asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                          :
-                         : "v"(dma_src[i] + j * (is_k ? kKTile : kVTile)), "s"(r), "{m0}"(dma_dst[i] + stage)
+                         : "v"(dma_src[i] + unsigned(j * (is_k ? kKTile : kVTile))), "s"(r),
+                           "{m0}"(dma_dst[i] + stage)
                          : "memory");
         }
     };
@@ -847,25 +851,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(FwdArgs a) {
 
 }  // namespace
 
-// Compute units of the current device (cached per device; 256 on MI355X).
-int persistent_cus() {
-    static int cached[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kPlanCUs;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < kXcds)
-            n = kPlanCUs;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 namespace {
 template <int kMode>
 hipError_t launch_sp(const FwdArgs& a, int d, hipStream_t stream) {
     const long long items = (long long)a.nqb * a.B * a.Hq;
-    const long long slots = (long long)(persistent_cus() / kXcds) * kXcds;
+    const long long slots = (long long)(device_cus() / kXcds) * kXcds;
     long long grid = (items + kXcds - 1) / kXcds * kXcds;
     if (grid > slots) grid = slots;
     if (d == 128)

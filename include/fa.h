@@ -75,8 +75,11 @@ typedef enum {
  * (must be finite and > 0).
  * dt = FA_BF16: bf16 inputs, float32 accumulation and softmax, bf16 output.
  * dt = FA_F32: float32 throughout.
- * Supported: d in {64, 128}; Hq % Hkv == 0; N * d < 2^31. B, Hq or N equal to 0 is a
- * valid empty call (nothing is launched).
+ * Supported: d in {64, 128}; Hq % Hkv == 0; N * d < 2^31, and for FA_BF16 N * d * 2 <= 2^30
+ * (a head's K or V rows span at most 2^30 bytes: the kernel addresses them with 32-bit
+ * offsets and keeps offsets at 2^31 and above as "outside the tile"; N <= 4M at d = 128);
+ * else FA_ERR_UNSUPPORTED. B, Hq or N equal to 0 is a valid empty call (nothing is
+ * launched).
  */
 fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void* o,
                  float* m_out, float* l_out, int B, int Hq, int Hkv, int N, int d,
@@ -95,7 +98,14 @@ fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void*
  *   num_splits  : 0 = automatic; otherwise the number of KV chunks the longest sequence is
  *                 split into (clamped to [1, pages of the longest sequence])
  *   workspace   : device scratch of at least fa_decode_workspace_bytes(...) bytes holding
- *                 the float32 partial (m, l, O) of every chunk; contents on entry are ignored
+ *                 one completion word per (sequence, KV head) and the float32 partial
+ *                 (m, l, O) of every chunk; contents on entry are ignored (a completion
+ *                 word carries a tag of the call that wrote it, so stale or arbitrary words
+ *                 count as empty)
+ *
+ * One launch: each chunk of a sequence's pages yields a partial; the last chunk of each
+ * (sequence, KV head) to finish merges the partials, in chunk order, into o. Calls that
+ * share one workspace must not overlap in time (enqueue them on one stream).
  *
  * Caller preconditions that are not checked on the device: seq_lens[b] <= max_seq_len, and
  * block_table[b][p] in [0, num_pages) for p < ceil(seq_lens[b] / page_size). The kernel
@@ -131,7 +141,7 @@ int fa_decode_plan_splits(int B, int Hkv, int page_size, int max_seq_len);
  * scale * q.k are exact products of e4m3 values accumulated in float32, so a per-tensor
  * descale of q and k is passed by folding it into `scale` (finite, > 0). Softmax in float32,
  * P rounded to bf16 for P V, float32 accumulation, bf16 output. causal as in fa_fwd.
- * Supported: d = 128; Hq % Hkv == 0 (else FA_ERR_INVALID_ARGUMENT); N * d * 2 < 2^31.
+ * Supported: d = 128; Hq % Hkv == 0 (else FA_ERR_INVALID_ARGUMENT); N * d * 2 <= 2^30.
  * B, Hq or N equal to 0 is a valid empty call.
  */
 fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* m_out,
@@ -183,7 +193,7 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int N);
  * outside block_indices. Every listed block is computed: blocks that lie wholly above the
  * causal diagonal cost time and contribute nothing.
  * Supported: dt = FA_BF16; d in {64, 128}; Hq % Hkv == 0 (else FA_ERR_INVALID_ARGUMENT);
- * N * d < 2^31; nnz >= 0. B, Hq or N equal to 0 is a valid empty call.
+ * N * d * 2 <= 2^30 (as fa_fwd); nnz >= 0. B, Hq or N equal to 0 is a valid empty call.
  */
 fa_status fa_fwd_block_sparse(fa_dtype dt, const void* q, const void* k, const void* v, void* o,
                               float* m_out, float* l_out, const int32_t* block_offsets,
@@ -216,7 +226,7 @@ fa_status fa_fwd_block_sparse(fa_dtype dt, const void* q, const void* k, const v
  * (its page reads as zeros), so a violated precondition gives a wrong result, never an
  * out-of-bounds access. Entries past a sequence's last page are not used.
  * Supported: dt = FA_BF16; d in {64, 128}; page_size = 16; Hq % Hkv == 0 (else
- * FA_ERR_INVALID_ARGUMENT); Nq * d < 2^31; each cache under 2 GiB (num_pages * Hkv * 16 *
+ * FA_ERR_INVALID_ARGUMENT); Nq * d * 2 <= 2^30; each cache under 2 GiB (num_pages * Hkv * 16 *
  * d * 2 bytes < 2^31, about 1M tokens at Hkv = 8, d = 128), else FA_ERR_UNSUPPORTED.
  * B, Hq or Nq equal to 0 is a valid empty call.
  */

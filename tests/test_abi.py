@@ -78,6 +78,10 @@ def fwd(lib, dt=1, q=DEV, k=DEV, v=DEV, o=DEV, B=1, Hq=2, Hkv=1, N=8, d=64, scal
     (dict(o=NULL), fa.FA_ERR_INVALID_ARGUMENT),
     (dict(k=MIS), fa.FA_ERR_INVALID_ARGUMENT),
     (dict(N=1 << 24, d=128), fa.FA_ERR_UNSUPPORTED),
+    # bf16: a head's K or V rows may span at most 2^30 bytes (N d <= 2^29)
+    (dict(N=(1 << 22) + 1, d=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=1 << 23, d=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=(1 << 23) + 1, d=64), fa.FA_ERR_UNSUPPORTED),
     # empty problems are valid no-ops, even with NULL pointers
     (dict(B=0, q=NULL, k=NULL, v=NULL, o=NULL), fa.FA_OK),
     (dict(N=0, q=NULL), fa.FA_OK),
@@ -127,7 +131,8 @@ def test_decode_workspace_and_plan():
     assert fa.fa_decode_plan_splits(8, 8, 32, 100) == 0  # unsupported page size
     need = fa.fa_decode_workspace_bytes(8, 32, 128, 16, 32768, 0)
     assert need >= s * 8 * 32 * 130 * 4
-    assert fa.fa_decode_workspace_bytes(8, 32, 128, 16, 32768, 5) == 5 * 8 * 32 * 130 * 4
+    # completion words (8 bytes per query head) and the float32 partials of 5 chunks
+    assert fa.fa_decode_workspace_bytes(8, 32, 128, 16, 32768, 5) == 8 * 8 * 32 + 5 * 8 * 32 * 130 * 4
     assert fa.fa_decode_workspace_bytes(8, 32, 128, 16, 32768, -1) == 0
     # the exact workspace is accepted by validation (rejected by nothing but a bad argument)
     lib = fa.load_library()
@@ -161,6 +166,7 @@ def paged(lib, dt=1, q=DEV, kc=DEV, vc=DEV, table=DEV, lens=DEV, o=DEV, B=2, Hq=
     (dict(o=MIS), fa.FA_ERR_INVALID_ARGUMENT),
     (dict(max_pages=1 << 28), fa.FA_ERR_UNSUPPORTED),
     (dict(num_pages=1 << 16, Hkv=8, Hq=8), fa.FA_ERR_UNSUPPORTED),   # a 2 GiB cache
+    (dict(Nq=(1 << 22) + 1), fa.FA_ERR_UNSUPPORTED),                 # Nq d > 2^29
     (dict(Nq=0, q=NULL, o=NULL), fa.FA_OK),
     (dict(B=0, q=NULL, o=NULL), fa.FA_OK),
 ])
@@ -187,6 +193,9 @@ def sparse(lib, dt=1, q=DEV, k=DEV, v=DEV, o=DEV, offs=DEV, idx=DEV, nnz=4, B=1,
     (dict(v=NULL), fa.FA_ERR_INVALID_ARGUMENT),
     (dict(k=MIS), fa.FA_ERR_INVALID_ARGUMENT),
     (dict(N=1 << 25), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=1 << 23), fa.FA_ERR_UNSUPPORTED),         # N d = 2^30: past 2^30 bytes per head
+    (dict(N=(1 << 22) + 1), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=(1 << 23) + 1, d=64), fa.FA_ERR_UNSUPPORTED),
     (dict(N=0, q=NULL), fa.FA_OK),
 ])
 def test_fwd_block_sparse_validation(kwargs, code):
@@ -205,6 +214,7 @@ def fp8(lib, q=DEV, k=DEV, v=DEV, o=DEV, B=1, Hq=4, Hkv=2, N=300, d=128, scale=0
     (dict(k=NULL), fa.FA_ERR_INVALID_ARGUMENT),
     (dict(v=MIS), fa.FA_ERR_INVALID_ARGUMENT),
     (dict(N=1 << 23), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=(1 << 22) + 1), fa.FA_ERR_UNSUPPORTED),
     (dict(N=0, q=NULL), fa.FA_OK),
 ])
 def test_fwd_fp8_validation(kwargs, code):
@@ -267,6 +277,21 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fa_fwd(q, q, q)
+
+
+@pytest.mark.parametrize("which", ["k", "v", "o", "dout"])
+def test_bwd_binding_rejects_mixed_dtypes(which):
+    """fa_bwd reads every tensor as q's dtype (bf16): another dtype is refused on the host."""
+    import torch
+
+    t = {n: torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16) for n in ("q", "k", "v", "o", "dout")}
+    t[which] = t[which].to(torch.float16)
+    m = torch.zeros(1, 2, 8, dtype=torch.float32)
+    with pytest.raises(TypeError, match=which):
+        fa.fa_bwd(t["q"], t["k"], t["v"], t["o"], t["dout"], m, m.clone())
+    t[which] = t[which].to(torch.uint8)
+    with pytest.raises(TypeError):
+        fa.fa_bwd(t["q"], t["k"], t["v"], t["o"], t["dout"], m, m.clone())
 
 
 def test_missing_library_fails_loudly(tmp_path):

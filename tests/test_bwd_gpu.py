@@ -68,3 +68,40 @@ def test_bwd_deterministic(dev):
     torch.cuda.synchronize()
     for u, w in zip(a, b):
         assert torch.equal(u, w)
+
+
+@pytest.mark.timeout(1200)
+def test_bwd_bench_shape(dev):
+    """The backward the bench times: B=2, H=32, N=8192, d=128, causal, K scaled by 2, with the
+    bench's seeded dO. Two runs must agree bitwise; dQ, dK and dV of six heads (the first and
+    last of each batch, two drawn) are compared in full with the oracle's gradients of that
+    head (query and key/value heads coincide here: Hq = Hkv)."""
+    import torch
+
+    from oracle import pool
+
+    cfg = gen.CONFIGS[3]
+    log_case(f"fa_bwd bench shape: backward of {cfg.name}")
+    x = gen.config_fwd_inputs(cfg)
+    dout = gen.round_to_bf16(np.random.default_rng(cfg.seed + 100).standard_normal(
+        x.q.shape, dtype=np.float32))
+    q, k, v, do = (gen.to_torch(t, "bf16", dev) for t in (x.q, x.k, x.v, dout))
+    o, m, l = fa.fa_fwd(q, k, v, scale=x.scale, causal=True, return_stats=True)
+    a = fa.fa_bwd(q, k, v, o, do, m, l, scale=x.scale, causal=True)
+    b2 = fa.fa_bwd(q, k, v, o, do, m, l, scale=x.scale, causal=True)
+    torch.cuda.synchronize()
+    for u, w in zip(a, b2):
+        assert torch.equal(u, w), "two backward runs differ"
+    rng = np.random.default_rng(77)
+    heads = [(0, 0), (0, cfg.Hq - 1), (1, 0), (1, cfg.Hq - 1)]
+    heads += [(int(bb), int(hh)) for bb, hh in zip(rng.integers(0, cfg.B, 2), rng.integers(1, cfg.Hq - 1, 2))]
+    got = {(bb, hh): tuple(t[bb, hh].float().cpu().numpy() for t in a) for bb, hh in heads}
+    del q, k, v, do, o, m, l, a, b2
+    torch.cuda.empty_cache()
+    refs = pool.attention_backward_heads(
+        ((x.q[bb, hh], x.k[bb, hh], x.v[bb, hh], dout[bb, hh]) for bb, hh in heads), x.scale, True,
+        workers=min(6, pool.worker_count()))
+    for (bb, hh), ref in zip(heads, refs):
+        for name, g, r in zip(("dq", "dk", "dv"), got[(bb, hh)], ref):
+            st = assert_close(g, r, "bf16", f"backward {name}[b={bb},h={hh}]")
+            log_case(f"fa_bwd bench shape {name}[b={bb},h={hh}] max |err| {st['max_abs']:.3e}")

@@ -62,15 +62,13 @@ def test_decode_small(case, splits, dev):
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"B{c[0]}-Hq{c[1]}-Hkv{c[2]}")
-@pytest.mark.parametrize("kernel", ["valu", "mx"])
-@pytest.mark.parametrize("splits", [0, 2])
-def test_decode_each_kernel(case, kernel, splits, dev, monkeypatch):
-    """The fixed-chunk plan on both decode kernels (vector-ALU and matrix-core), with its
-    automatic split count and with an explicit one, against the oracle."""
-    monkeypatch.setenv("FA_DECODE_KERNEL", kernel)
+@pytest.mark.parametrize("splits", [3, 16])
+def test_decode_split_counts(case, splits, dev):
+    """Explicit split counts (the last chunk of every (sequence, KV head) merges in the same
+    launch), against the oracle, on tables wider than the sequences."""
     B, Hq, Hkv, lens = case
     seed = 300 + SMALL.index(case)
-    log_case(f"fa_decode_splitk {kernel} {case} splits={splits} seed={seed}")
+    log_case(f"fa_decode_splitk {case} splits={splits} seed={seed}")
     x = gen.decode_inputs(B, Hq, Hkv, 128, 16, seed=seed, lens=lens,
                           max_pages_per_seq=-(-max(lens) // 16) + 3)
     t = upload(x, dev)
@@ -144,11 +142,42 @@ def test_decode_config5_full(dev):
     assert torch.equal(o, o2), "two runs differ: the kernel is not deterministic"
     o_ref, _, _ = oracle.decode(x.q, x.k_seqs, x.v_seqs, x.scale)
     assert_close(to_np(o), o_ref, "bf16", "config 5 O")
-    for s in (1, 7):
+    for s in (1, 2, 7):
         log_case(f"fa_decode_splitk config 5 num_splits={s}")
         assert_close(to_np(run_decode(t, cfg.len_max, x.scale, s)), o_ref, "bf16", f"splits={s}")
     del t, o, o2
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fill", ["zeros", "ones", "random"])
+def test_decode_workspace_contents_do_not_matter(fill, dev):
+    """The workspace may hold anything on entry (the completion words included): the result
+    is bitwise that of a fresh call, on every split count and on repeated calls."""
+    import torch
+
+    log_case(f"fa_decode_splitk workspace filled with {fill}")
+    x = gen.decode_inputs(5, 32, 8, 128, 16, seed=305, lens=[3000, 17, 1500, 2049, 640])
+    t = upload(x, dev)
+    o_ref, _, _ = oracle.decode(x.q, x.k_seqs, x.v_seqs, x.scale)
+    for splits in (0, 2, 5):
+        need = fa.fa_decode_workspace_bytes(5, 32, 128, 16, x.max_seq_len, splits)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        outs = []
+        for rep in range(3):
+            if fill == "zeros":
+                ws.zero_()
+            elif fill == "ones":
+                ws.fill_(255)
+            else:
+                g = torch.Generator(device="cpu").manual_seed(1000 * splits + rep)
+                ws.copy_(torch.randint(0, 256, (need,), dtype=torch.uint8, generator=g))
+            o = fa.fa_decode_splitk(t["q"], t["k_cache"], t["v_cache"], t["block_table"],
+                                    t["seq_lens"], x.max_seq_len, scale=x.scale,
+                                    num_splits=splits, workspace=ws)
+            torch.cuda.synchronize()
+            outs.append(o)
+        assert all(torch.equal(outs[0], u) for u in outs[1:])
+        assert_close(to_np(outs[0]), o_ref, "bf16", f"splits={splits}")
 
 
 def test_decode_physical_page_order_does_not_matter(dev):

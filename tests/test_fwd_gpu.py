@@ -8,7 +8,7 @@ import pytest
 import oracle
 import exact_tiled_attention_24_amd as fa
 from exact_tiled_attention_24_amd import inputs as gen
-from helpers import assert_close, cuda_device, log_case, to_np
+from helpers import assert_close, cuda_device, log_case, to_np, L_RTOL_BF16
 
 pytestmark = pytest.mark.gpu
 
@@ -63,24 +63,7 @@ def test_fwd_small_shapes(case, dev):
     o_ref, m_ref, l_ref = oracle.attention(x.q, x.k, x.v, x.scale, causal)
     assert_close(to_np(o), o_ref, dtype, "O")
     np.testing.assert_allclose(to_np(m), m_ref, atol=1e-5 if dtype == "f32" else 1e-3, rtol=0)
-    np.testing.assert_allclose(to_np(l), l_ref, rtol=1e-5 if dtype == "f32" else 2e-3)
-
-
-@pytest.mark.parametrize("kernel", ["tiled", "sp"])
-@pytest.mark.parametrize("case", [c for c in SMALL if c[0] == "bf16"], ids=lambda c: "-".join(map(str, c)))
-def test_fwd_each_bf16_kernel(case, kernel, dev, monkeypatch):
-    """Both bf16 forward kernels (the library picks one per head size; FA_FWD_KERNEL forces
-    either) against the oracle on the same cases."""
-    dtype, B, Hq, Hkv, N, d, causal = case
-    seed = 100 + SMALL.index(case)
-    log_case(f"fa_fwd kernel={kernel} {case} seed={seed}")
-    monkeypatch.setenv("FA_FWD_KERNEL", kernel)
-    x = gen.fwd_inputs(B, Hq, Hkv, N, d, seed=seed, dtype=dtype, causal=causal)
-    o, m, l = run_fwd(x, dev)
-    o_ref, m_ref, l_ref = oracle.attention(x.q, x.k, x.v, x.scale, causal)
-    assert_close(to_np(o), o_ref, dtype, "O")
-    np.testing.assert_allclose(to_np(m), m_ref, atol=1e-3, rtol=0)
-    np.testing.assert_allclose(to_np(l), l_ref, rtol=2e-3)
+    np.testing.assert_allclose(to_np(l), l_ref, rtol=1e-5 if dtype == "f32" else L_RTOL_BF16)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -114,7 +97,7 @@ def test_fwd_worked_example(dtype, dev):
     if dtype == "f32":
         np.testing.assert_allclose(to_np(l)[0, 0], 1.5530, atol=5e-5)
     else:
-        np.testing.assert_allclose(to_np(l)[0, 0], 1.5530, rtol=2e-3)
+        np.testing.assert_allclose(to_np(l)[0, 0], 1.5530, rtol=L_RTOL_BF16)
 
 
 def test_config1_full(dev):
@@ -135,22 +118,21 @@ def test_config2_full(dev):
     o_ref, m_ref, l_ref = oracle.attention(x.q, x.k, x.v, x.scale, cfg.causal)
     assert_close(to_np(o), o_ref, "bf16", "config 2 O")
     np.testing.assert_allclose(to_np(m), m_ref, atol=1e-3)
-    np.testing.assert_allclose(to_np(l), l_ref, rtol=2e-3)
+    np.testing.assert_allclose(to_np(l), l_ref, rtol=L_RTOL_BF16)
 
 
-def sampled_rows(N, rng, extra=12):
-    fixed = {0, 1, 63, 64, 127, 128, N // 2, N - 129, N - 128, N - 2, N - 1}
-    rows = sorted(r for r in fixed | set(rng.integers(0, N, extra).tolist()) if 0 <= r < N)
-    return np.array(rows)
-
-
+@pytest.mark.timeout(1200)
 @pytest.mark.parametrize("cfg_id", [3, 4])
-def test_config_full_size_sampled_rows(cfg_id, dev):
-    """Full-size run in the bench's launch configuration; rows sampled for the oracle."""
+def test_config_full_size_every_row(cfg_id, dev):
+    """The full-size workload in the bench's launch configuration: every row of every head of
+    O, m and l against the oracle (run head by head in worker processes), plus a second run
+    that must be bitwise identical."""
     import torch
 
+    from oracle import pool
+
     cfg = gen.CONFIGS[cfg_id]
-    log_case(f"fa_fwd config: {cfg.name}")
+    log_case(f"fa_fwd config: {cfg.name} (every row)")
     x = gen.config_fwd_inputs(cfg)
     q = gen.to_torch(x.q, "bf16", dev)
     k = gen.to_torch(x.k, "bf16", dev)
@@ -159,20 +141,21 @@ def test_config_full_size_sampled_rows(cfg_id, dev):
     o2 = fa.fa_fwd(q, k, v, scale=x.scale, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o, o2), "two runs differ: the kernel is not deterministic"
-    assert torch.isfinite(o.float()).all()
-    rng = np.random.default_rng(cfg_id)
-    G = cfg.Hq // cfg.Hkv
-    heads = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq)]
-    pick = [heads[i] for i in sorted(set(rng.integers(0, len(heads), 8).tolist()) | {0, len(heads) - 1})]
-    for b, h in pick:
-        rows = sampled_rows(cfg.N, rng)
-        o_ref, m_ref, l_ref = oracle.attention_head(x.q[b, h], x.k[b, h // G], x.v[b, h // G],
-                                                    x.scale, True, rows=rows)
-        assert_close(to_np(o[b, h])[rows], o_ref, "bf16", f"config {cfg_id} O[b={b},h={h}]")
-        np.testing.assert_allclose(to_np(m[b, h])[rows], m_ref, atol=2e-3)
-        np.testing.assert_allclose(to_np(l[b, h])[rows], l_ref, rtol=2e-3)
+    o_np, m_np, l_np = o.float().cpu().numpy(), m.cpu().numpy(), l.cpu().numpy()
     del q, k, v, o, o2, m, l
     torch.cuda.empty_cache()
+    G = cfg.Hq // cfg.Hkv
+    heads = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq)]
+    refs = pool.attention_heads(((x.q[b, h], x.k[b, h // G], x.v[b, h // G]) for b, h in heads),
+                                x.scale, True)
+    worst = 0.0
+    for n, ((b, h), (o_ref, m_ref, l_ref)) in enumerate(zip(heads, refs)):
+        st = assert_close(o_np[b, h], o_ref, "bf16", f"config {cfg_id} O[b={b},h={h}]")
+        worst = max(worst, st["max_abs"])
+        np.testing.assert_allclose(m_np[b, h], m_ref, atol=2e-3, rtol=0)
+        np.testing.assert_allclose(l_np[b, h], l_ref, rtol=L_RTOL_BF16)
+        if n % 8 == 7:
+            log_case(f"config {cfg_id}: {n + 1} of {len(heads)} heads match; max |err| {worst:.3e}")
 
 
 def test_fwd_deterministic_and_gqa_equals_repeated_heads(dev):
