@@ -9,6 +9,7 @@ raises.
 Entry points (same names as the C ABI):
     fa_fwd(q, k, v, scale=None, causal=False, out=None, return_stats=False)
     fa_decode_splitk(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, ...)
+    fa_decode_splitk_noalloc(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, out, ...)
     fa_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=True, ...)
     fa_fwd_block_sparse(q, k, v, block_offsets, block_indices, scale=None, causal=False, ...)
     fa_bwd(q, k, v, o, dout, m, l, scale=None, causal=False, workspace=None)
@@ -61,6 +62,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode_splitk.restype = i32
     lib.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_decode_splitk_noalloc.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                             i32, i32, i32, f32, i32, vp]
+    lib.fa_decode_splitk_noalloc.restype = i32
+    lib.fa_decode_noalloc_max_bytes.argtypes = []
+    lib.fa_decode_noalloc_max_bytes.restype = sz
     lib.fa_decode_plan_splits.argtypes = [i32, i32, i32, i32]
     lib.fa_decode_plan_splits.restype = i32
     lib.fa_fwd_paged.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
@@ -205,6 +211,40 @@ def fa_decode_splitk(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, sc
             workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(code, "fa_decode_splitk")
     return o
+
+
+def fa_decode_noalloc_max_bytes() -> int:
+    return int(load_library().fa_decode_noalloc_max_bytes())
+
+
+def fa_decode_splitk_noalloc(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, out,
+                             scale=None, num_splits=0):
+    """fa_decode_splitk without a workspace: the library's static per-device scratch holds the
+    partials, and nothing is allocated (``out``, bf16 [B, Hq, d], is the caller's). Calls that
+    overlap in time on one device race on that scratch: keep them on one stream."""
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B, Hq, d]; caches [num_pages, Hkv, page_size, d]")
+    B, Hq, d = q.shape
+    num_pages, Hkv, page_size, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("head dimension mismatch between q and the cache")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages_per_seq] and seq_lens [B]")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    _require_gpu(q, k_cache, v_cache, block_table, seq_lens, out)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        code = lib.fa_decode_splitk_noalloc(
+            _dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(seq_lens), _ptr(out), B, Hq, Hkv, d, page_size, num_pages, block_table.shape[1],
+            int(max_seq_len), scale, int(num_splits), _stream(q.device))
+    _check(code, "fa_decode_splitk_noalloc")
+    return out
 
 
 def fa_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=True, out=None,

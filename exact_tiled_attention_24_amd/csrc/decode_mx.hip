@@ -431,6 +431,13 @@ __global__ __launch_bounds__(kThreads) void decode_mx_kernel(DecodeArgs a) {
     }
 }
 
+// Scratch of the allocation-free entry point: the completion words and partials of one call
+// (the same layout as a caller's workspace), resident on every device the library runs on
+// until the process ends. Host code never uses this name as an address: the device address
+// comes from hipGetSymbolAddress, once per device (see decode_scratch).
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 // A tag no earlier call of this process used: a per-process random start plus a call count,
 // kept to 40 bits (the completion word's high bits).
 unsigned long long next_tag() {
@@ -443,6 +450,27 @@ unsigned long long next_tag() {
 }
 
 }  // namespace
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+hipError_t decode_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with `dev` current
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_decode_bf16_mx(const void* q, const void* k_cache, const void* v_cache,
                                  const int32_t* block_table, const int32_t* seq_lens, void* o,

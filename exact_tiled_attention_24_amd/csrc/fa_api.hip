@@ -149,11 +149,11 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int d, int page_size, int max_se
     return decode_ws_bytes(B, Hq, d, p.bound);
 }
 
-fa_status fa_decode_splitk(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
-                           const int32_t* block_table, const int32_t* seq_lens, void* o, int B,
-                           int Hq, int Hkv, int d, int page_size, int num_pages,
-                           int max_pages_per_seq, int max_seq_len, float scale, int num_splits,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+// Checks shared by both decode entry points (everything but the workspace).
+static fa_status decode_check(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, const int32_t* seq_lens, void* o, int B, int Hq,
+                       int Hkv, int d, int page_size, int num_pages, int max_pages_per_seq,
+                       int max_seq_len, float scale, int num_splits) {
     if (dt != FA_F32 && dt != FA_BF16) return FA_ERR_INVALID_ARGUMENT;
     if (B < 0 || Hq < 1 || Hkv < 1 || d < 1 || page_size < 1 || num_pages < 0 ||
         max_pages_per_seq < 0 || max_seq_len < 0 || num_splits < 0)
@@ -165,18 +165,54 @@ fa_status fa_decode_splitk(fa_dtype dt, const void* q, const void* k_cache, cons
         (G != 1 && G != 2 && G != 4 && G != 8))
         return FA_ERR_UNSUPPORTED;
     if (B == 0) return FA_OK;
-    if (!q || !o || !block_table || !seq_lens || !workspace) return FA_ERR_INVALID_ARGUMENT;
+    if (!q || !o || !block_table || !seq_lens) return FA_ERR_INVALID_ARGUMENT;
     if (num_pages > 0 && (!k_cache || !v_cache)) return FA_ERR_INVALID_ARGUMENT;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
-        !aligned16(workspace))
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
         return FA_ERR_INVALID_ARGUMENT;
     if ((long long)B * Hkv >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+fa_status fa_decode_splitk(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* seq_lens, void* o, int B,
+                           int Hq, int Hkv, int d, int page_size, int num_pages,
+                           int max_pages_per_seq, int max_seq_len, float scale, int num_splits,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    const fa_status st = decode_check(dt, q, k_cache, v_cache, block_table, seq_lens, o, B, Hq,
+                                      Hkv, d, page_size, num_pages, max_pages_per_seq,
+                                      max_seq_len, scale, num_splits);
+    if (st != FA_OK || B == 0) return st;
+    if (!workspace) return FA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(workspace)) return FA_ERR_INVALID_ARGUMENT;
     const DecodePlan p = plan_decode(B, Hkv, max_pages_per_seq, max_seq_len, num_splits);
     const size_t need = decode_ws_bytes(B, Hq, d, p.splits);
     if (workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
     const hipError_t e = fa::launch_decode_bf16_mx(
         q, k_cache, v_cache, block_table, seq_lens, o, B, Hq, Hkv, d, num_pages, max_pages_per_seq,
         p.len_cap, scale, p.splits, p.chunk_pages, decode_ws_layout(workspace, B, Hq, d, p.splits),
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_decode_noalloc_max_bytes(void) { return fa::decode_scratch_bytes(); }
+
+fa_status fa_decode_splitk_noalloc(fa_dtype dt, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_table,
+                                   const int32_t* seq_lens, void* o, int B, int Hq, int Hkv, int d,
+                                   int page_size, int num_pages, int max_pages_per_seq,
+                                   int max_seq_len, float scale, int num_splits, void* stream) {
+    const fa_status st = decode_check(dt, q, k_cache, v_cache, block_table, seq_lens, o, B, Hq,
+                                      Hkv, d, page_size, num_pages, max_pages_per_seq,
+                                      max_seq_len, scale, num_splits);
+    if (st != FA_OK || B == 0) return st;
+    const DecodePlan p = plan_decode(B, Hkv, max_pages_per_seq, max_seq_len, num_splits);
+    if (decode_ws_bytes(B, Hq, d, p.splits) > fa::decode_scratch_bytes())
+        return FA_ERR_WORKSPACE_TOO_SMALL;
+    void* scratch = nullptr;  // this device's copy of the library's static scratch
+    if (fa::decode_scratch(&scratch) != hipSuccess) return FA_ERR_HIP;
+    const hipError_t e = fa::launch_decode_bf16_mx(
+        q, k_cache, v_cache, block_table, seq_lens, o, B, Hq, Hkv, d, num_pages, max_pages_per_seq,
+        p.len_cap, scale, p.splits, p.chunk_pages, decode_ws_layout(scratch, B, Hq, d, p.splits),
         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

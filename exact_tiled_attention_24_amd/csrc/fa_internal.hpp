@@ -73,6 +73,11 @@ hipError_t launch_decode_bf16_mx(const void* q, const void* k_cache, const void*
                                  int max_pages_per_seq, int len_cap, float scale, int splits,
                                  int chunk_pages, const DecodeWorkspace& ws, hipStream_t stream);
 
+// The decode scratch of the allocation-free entry point: its size, and its device address on
+// the current device (looked up once per device; no allocation).
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** ptr);
+
 // Row-wise merge of S partials. log2_units != 0: m is in log2 units (internal workspace);
 // otherwise natural-log units (public fa_merge). out_bf16 selects the output type.
 hipError_t launch_merge(const float* o_parts, const float* m_parts, const float* l_parts, void* o,

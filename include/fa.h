@@ -122,6 +122,30 @@ fa_status fa_decode_splitk(fa_dtype dt, const void* q, const void* k_cache, cons
                            int max_pages_per_seq, int max_seq_len, float scale, int num_splits,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_decode_splitk_noalloc - fa_decode_splitk without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). Same arguments (minus workspace), semantics and results.
+ *
+ * The completion words and partials live in a static scratch array of the library, one copy
+ * per device, of fa_decode_noalloc_max_bytes() bytes (16 MiB), held until the process ends.
+ * A request whose partials would not fit (fa_decode_workspace_bytes(...) > that size, about
+ * B * Hq * splits > 31K at d = 128) returns FA_ERR_WORKSPACE_TOO_SMALL and launches nothing.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library routine); its
+ * first call on a device looks up that device's scratch address once.
+ * Every call on one device shares that device's scratch: calls that overlap in time on one
+ * device (on different streams, or from different threads) race and give wrong results.
+ * Enqueue them on one stream, or use fa_decode_splitk with a workspace per stream.
+ */
+fa_status fa_decode_splitk_noalloc(fa_dtype dt, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_table,
+                                   const int32_t* seq_lens, void* o, int B, int Hq, int Hkv, int d,
+                                   int page_size, int num_pages, int max_pages_per_seq,
+                                   int max_seq_len, float scale, int num_splits, void* stream);
+
+/* Bytes of the static scratch fa_decode_splitk_noalloc uses (its largest workspace). */
+size_t fa_decode_noalloc_max_bytes(void);
+
 /* Workspace bytes fa_decode_splitk needs for these sizes (0 for an invalid request). */
 size_t fa_decode_workspace_bytes(int B, int Hq, int d, int page_size, int max_seq_len,
                                  int num_splits);

@@ -297,3 +297,30 @@ def test_bwd_binding_rejects_mixed_dtypes(which):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         fa.load_library(str(tmp_path / "libfa.so"))
+
+
+def test_decode_noalloc_limits():
+    """The allocation-free decode rejects, before any HIP call, a request whose partials would
+    not fit its static scratch, and validates like fa_decode_splitk."""
+    lib = fa.load_library()
+    cap = fa.fa_decode_noalloc_max_bytes()
+    assert cap == 16 << 20
+
+    def noalloc(**kw):
+        a = dict(dt=1, q=DEV, kc=DEV, vc=DEV, table=DEV, lens=DEV, o=DEV, B=2, Hq=8, Hkv=2, d=128,
+                 page=16, num_pages=10, max_pages=5, max_len=80, scale=0.08, splits=0)
+        a.update(kw)
+        return lib.fa_decode_splitk_noalloc(a["dt"], a["q"], a["kc"], a["vc"], a["table"],
+                                            a["lens"], a["o"], a["B"], a["Hq"], a["Hkv"], a["d"],
+                                            a["page"], a["num_pages"], a["max_pages"],
+                                            a["max_len"], a["scale"], a["splits"], None)
+
+    # 64 sequences x 64 query heads x 64 chunks of 130 floats: 136 MB of partials
+    big = dict(B=64, Hq=64, Hkv=8, max_pages=4096, max_len=65536, splits=64)
+    assert fa.fa_decode_workspace_bytes(64, 64, 128, 16, 65536, 64) > cap
+    assert noalloc(**big) == fa.FA_ERR_WORKSPACE_TOO_SMALL
+    assert noalloc(dt=0) == fa.FA_ERR_UNSUPPORTED
+    assert noalloc(Hq=7) == fa.FA_ERR_INVALID_ARGUMENT
+    assert noalloc(q=NULL) == fa.FA_ERR_INVALID_ARGUMENT
+    assert noalloc(kc=MIS) == fa.FA_ERR_INVALID_ARGUMENT
+    assert noalloc(B=0, q=NULL, o=NULL) == fa.FA_OK
