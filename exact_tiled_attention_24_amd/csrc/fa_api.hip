@@ -185,6 +185,7 @@ fa_status fa_decode_splitk(fa_dtype dt, const void* q, const void* k_cache, cons
     if (!workspace) return FA_ERR_INVALID_ARGUMENT;
     if (!aligned16(workspace)) return FA_ERR_INVALID_ARGUMENT;
     const DecodePlan p = plan_decode(B, Hkv, max_pages_per_seq, max_seq_len, num_splits);
+    if (p.splits > 65535) return FA_ERR_UNSUPPORTED;  // grid y holds the chunk
     const size_t need = decode_ws_bytes(B, Hq, d, p.splits);
     if (workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
     const hipError_t e = fa::launch_decode_bf16_mx(
@@ -206,6 +207,7 @@ fa_status fa_decode_splitk_noalloc(fa_dtype dt, const void* q, const void* k_cac
                                       max_seq_len, scale, num_splits);
     if (st != FA_OK || B == 0) return st;
     const DecodePlan p = plan_decode(B, Hkv, max_pages_per_seq, max_seq_len, num_splits);
+    if (p.splits > 65535) return FA_ERR_UNSUPPORTED;  // grid y holds the chunk
     if (decode_ws_bytes(B, Hq, d, p.splits) > fa::decode_scratch_bytes())
         return FA_ERR_WORKSPACE_TOO_SMALL;
     void* scratch = nullptr;  // this device's copy of the library's static scratch
