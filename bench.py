@@ -3,16 +3,22 @@
 
 One step = one pass of the whole path over one batch of synthetic input:
   1. fa_fwd on causal multi-head prefill, bf16, B=2, H=32, N=8192, d=128 (K scaled by 2);
-  2. fa_decode_splitk (split-K paged decode + partial merge) on B=8 sequences, 32 query
-     heads over 8 KV heads, d=128, lengths uniform in [16384, 32768], 16-token pages.
-Inputs are generated once (seeded) and are resident in HBM before timing starts.
+  2. fa_decode_splitk (split-K paged decode, partials merged in the same launch) on B=8
+     sequences, 32 query heads over 8 KV heads, d=128, lengths uniform in [16384, 32768],
+     16-token pages.
+Inputs are generated once (seeded) and are resident in HBM before timing starts. After the
+steps, each in a loop of its own: fa_fwd on the other two prefill workloads (causal B=4 H=16
+N=2048 d=64, and causal GQA B=1 Hq=32 Hkv=8 N=32768 d=128), chunked prefill over the paged
+cache, the block-sparse forward, the backward and the fp8 forward.
 
 Prints ONE JSON line. `value` is the forward's algorithmic TFLOP/s (4*d per admissible
 (query, key) pair, causal tiles skipped by the method are not counted) over the timed
 steps; the decode's algorithmic HBM GB/s (K and V read once per KV head, plus q, o, the
 block table and the lengths) is reported next to it. Kernel durations come from HIP
 events recorded on the stream the kernels are launched on. `cpu_baseline` times the
-float64 CPU oracle on a bounded sample of the same forward workload.
+float64 CPU oracle (one worker process per core of this process's affinity set, at most 16)
+on bounded samples of the prefill and decode workloads and compares its results with the GPU
+outputs of the timed runs element by element.
 """
 
 from __future__ import annotations
@@ -45,13 +51,11 @@ def parse():
     ap.add_argument("--kv-pools", type=int, default=2,
                     help="copies of the decode KV cache used in turn, so that no call finds the "
                          "previous call's pages in L2 or the Infinity Cache (1 = one cache)")
-    ap.add_argument("--decode-mx", default=None, metavar="W,S",
-                    help="matrix-core decode variant: waves per workgroup, page slots per wave "
-                         "(default 4,2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=64,
-                    help="heads of the forward workload the oracle is timed on")
-    ap.add_argument("--only", choices=["fwd", "decode", "paged", "sparse", "bwd", "fp8"], default=None,
+    ap.add_argument("--cpu-heads4", type=int, default=32,
+                    help="heads of the N=32768 GQA workload the oracle runs on (of 32)")
+    ap.add_argument("--only", choices=["fwd", "decode", "fwd2", "fwd4", "paged", "sparse", "bwd",
+                                       "fp8"], default=None,
                     help="time one kernel only (profiling runs)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling)")
@@ -220,13 +224,15 @@ def main():
     do_sparse = args.only in (None, "sparse")
     do_bwd = args.only in (None, "bwd")
     do_fp8 = args.only in (None, "fp8")
+    do_fwd2 = args.only in (None, "fwd2") and args.fwd_config != 2
+    do_fwd4 = args.only in (None, "fwd4") and args.fwd_config != 4
 
     # ---- inputs, resident in HBM ----
     fcfg = gen.CONFIGS[args.fwd_config]
     dcfg = gen.CONFIGS[5]
     fwd_flops = fcfg.flops()
     fx = None
-    if do_fwd or not args.no_cpu_baseline:
+    if do_fwd:
         fx = gen.config_fwd_inputs(fcfg)
     if do_fwd:
         q = gen.to_torch(fx.q, "bf16", dev)
@@ -235,8 +241,6 @@ def main():
         o = torch.empty_like(q)
 
     dec_bytes, splits, lens_sum = None, None, None
-    if args.decode_mx:
-        os.environ["FA_DECODE_MX"] = args.decode_mx
     if do_dec:
         dx = gen.config_decode_inputs(dcfg)
         dq = gen.to_torch(dx.q, "bf16", dev)
@@ -255,7 +259,7 @@ def main():
         dec_bytes = (dx.kv_bytes() + dq.numel() * 2 + do.numel() * 2
                      + 4 * int(sum(-(-int(L) // 16) for L in dx.lens)) + 4 * dcfg.B)
         dec_scale = dx.scale
-        del dx
+        dec_inputs = dx
 
     paged_flops = None
     if do_paged:
@@ -303,6 +307,15 @@ def main():
         bwd_flops = 2.5 * bcfg.flops()
         bwd_scale = bx.scale
         del bx
+
+    # the other prefill workloads, timed in loops of their own after the steps
+    extra_fwd = {}
+    for cid, on in ((2, do_fwd2), (4, do_fwd4)):
+        if on:
+            c = gen.CONFIGS[cid]
+            x = gen.config_fwd_inputs(c)
+            tq, tk, tv = (gen.to_torch(t, "bf16", dev) for t in (x.q, x.k, x.v))
+            extra_fwd[cid] = dict(cfg=c, x=x, q=tq, k=tk, v=tv, o=torch.empty_like(tq))
 
     fp8_flops = None
     if do_fp8:
@@ -374,6 +387,25 @@ def main():
         for _ in range(3):
             copy_dst.copy_(copy_src)
         torch.cuda.synchronize()
+
+    def timed_loop(fn, reps, warmup):
+        for _ in range(warmup):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])
+
+    fwd_extra_ms = {}
+    for cid, e in extra_fwd.items():
+        def run(e=e):
+            fa.fa_fwd(e["q"], e["k"], e["v"], scale=e["x"].scale, causal=e["cfg"].causal,
+                      out=e["o"])
+        fwd_extra_ms[cid] = timed_loop(run, max(10, args.steps), args.warmup)
 
     # chunked prefill over the paged cache: timed on its own, after the steps
     paged_ms = None
@@ -484,6 +516,19 @@ def main():
         },
         "fwd_tokens_per_s": round(fcfg.B * fcfg.N / (fwd_ms.mean() * 1e-3), 1) if do_fwd else None,
     }
+    if fwd_extra_ms:
+        result["fwd_configs"] = {}
+    for cid, ms in fwd_extra_ms.items():
+        c = extra_fwd[cid]["cfg"]
+        tf = c.flops() / (ms.mean() * 1e-3) / 1e12
+        result["fwd_configs"][str(cid)] = {
+            "workload": c.name, "algorithmic_flops": c.flops(), "value": round(tf, 2),
+            "unit": "TFLOP/s", "avg_call_ms": round(float(ms.mean()), 5), "calls": int(ms.size),
+            "tokens_per_s": round(c.B * c.N / (ms.mean() * 1e-3), 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "kernel": f"fwd_bf16_sp_kernel<{c.d}, 0>"},
+        }
     if do_paged:
         p_tflops = paged_flops / (paged_ms.mean() * 1e-3) / 1e12
         result["paged_prefill"] = {
@@ -536,8 +581,21 @@ def main():
     except (OSError, ValueError):
         result["choices"] = None
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(fx, fcfg, args.cpu_heads)
+        legs = {}
+        if do_fwd:
+            legs[fcfg_id(fcfg)] = (fx, fcfg, o, fwd_ms, None)
+        for cid, e in extra_fwd.items():
+            heads = args.cpu_heads4 if cid == 4 else None
+            legs[cid] = (e["x"], e["cfg"], e["o"], fwd_extra_ms[cid], heads)
+        dec_leg = (dec_inputs, do, dec_ms) if do_dec else None
+        result["cpu_baseline"] = cpu_baseline(legs, dec_leg, main_cfg=fcfg_id(fcfg))
     print(json.dumps(result), flush=True)
+
+
+def fcfg_id(cfg):
+    from exact_tiled_attention_24_amd import inputs as gen
+
+    return next(k for k, c in gen.CONFIGS.items() if c is cfg)
 
 
 def load_traffic():
@@ -557,27 +615,66 @@ def load_traffic():
     return out
 
 
-def cpu_baseline(fx, fcfg, heads):
-    """Time the float64 oracle on `heads` whole heads of the forward workload."""
+def cpu_baseline(legs, dec_leg, main_cfg):
+    """The float64 oracle on bounded samples of the workloads, timed on this host's cores.
+
+    `legs`: {config id: (inputs, config, GPU output tensor, GPU call times in ms, heads)}; the
+    oracle runs `heads` evenly spaced heads (all when None) of each, one head per task in a
+    pool of worker processes (one per core of the affinity set, at most 16, one BLAS thread
+    each), and its results are compared with the GPU output of the timed calls. `dec_leg`:
+    (decode inputs, GPU output, call times) for the decode workload (all sequences).
+    """
+    from oracle import pool
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        cores = os.cpu_count() or 1
-    G = fcfg.Hq // fcfg.Hkv
-    t0 = time.perf_counter()
-    for i in range(heads):
-        b, h = divmod(i, fcfg.Hq)
-        oracle.attention_head(fx.q[b, h], fx.k[b, h // G], fx.v[b, h // G], fx.scale, fcfg.causal)
-    dt = time.perf_counter() - t0
-    flops = fcfg.flops() / (fcfg.B * fcfg.Hq) * heads
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"{heads} of {fcfg.B * fcfg.Hq} heads of the forward workload "
-                      f"(causal N={fcfg.N}, d={fcfg.d}), float64 numpy"}
+    workers = pool.worker_count()
+    per = {}
+    total_s = 0.0
+    for cid, (x, c, o_gpu, ms, heads) in legs.items():
+        G = c.Hq // c.Hkv
+        all_heads = [(b, h) for b in range(c.B) for h in range(c.Hq)]
+        n = len(all_heads) if heads is None else max(1, min(int(heads), len(all_heads)))
+        pick = [all_heads[int(round(i * (len(all_heads) - 1) / max(1, n - 1)))] for i in range(n)]
+        pick = sorted(set(pick))
+        t0 = time.perf_counter()
+        refs = list(pool.attention_heads(((x.q[b, h], x.k[b, h // G], x.v[b, h // G])
+                                          for b, h in pick), x.scale, c.causal, workers=workers))
+        dt = time.perf_counter() - t0
+        total_s += dt
+        err = 0.0
+        for (b, h), (o_ref, _, _) in zip(pick, refs):
+            got = o_gpu[b, h].float().cpu().numpy().astype(np.float64)
+            err = max(err, float(np.abs(got - o_ref).max()))
+        flops = c.flops() / len(all_heads) * len(pick)
+        oracle_tflops = flops / dt / 1e12
+        gpu_tflops = c.flops() / (ms.mean() * 1e-3) / 1e12
+        per[str(cid)] = {
+            "workload": c.name, "heads": f"{len(pick)} of {len(all_heads)}",
+            "seconds": round(dt, 3), "value": round(oracle_tflops, 6), "unit": "TFLOP/s",
+            "max_abs_err_vs_gpu": err, "gpu_over_oracle": round(gpu_tflops / oracle_tflops, 1),
+            "extrapolated": len(pick) < len(all_heads),
+        }
+    if dec_leg is not None:
+        dx, o_gpu, ms = dec_leg
+        t0 = time.perf_counter()
+        o_ref, _, _ = oracle.decode(dx.q, dx.k_seqs, dx.v_seqs, dx.scale)
+        dt = time.perf_counter() - t0
+        total_s += dt
+        err = float(np.abs(o_gpu.float().cpu().numpy().astype(np.float64) - o_ref).max())
+        kv = dx.kv_bytes()
+        per["5"] = {"workload": "paged split-K decode (all sequences)", "seconds": round(dt, 3),
+                    "value": round(kv / dt / 1e9, 3), "unit": "GB/s of K and V",
+                    "max_abs_err_vs_gpu": err,
+                    "gpu_over_oracle": round((kv / (ms.mean() * 1e-3)) / (kv / dt), 1),
+                    "extrapolated": False, "cores": 1}
+    main = per.get(str(main_cfg), next(iter(per.values())) if per else {})
+    return {"value": main.get("value"), "unit": main.get("unit", "TFLOP/s"), "cores": workers,
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle, one head per task on {workers} worker processes: "
+                      + "; ".join(f"workload {k}: {v.get('heads', 'all sequences')}"
+                                  for k, v in per.items()),
+            "seconds": round(total_s, 3), "gpu_over_oracle": main.get("gpu_over_oracle"),
+            "per_config": per}
 
 
 if __name__ == "__main__":
