@@ -152,8 +152,12 @@ struct FwdArgs {
 
 // One work item: the 256-row query block and head that `item` names in the work list
 // (KV group, query block heaviest first, head in group). `smem` is the workgroup's LDS.
-template <int D, int kMode>
-__device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned char* smem) {
+// kStats: the caller asked for the row statistics (m needs every tile's row maximum);
+// without them the softmax skips the per-tile maximum (see `step`).
+// Returns false (and writes nothing) when the softmax without statistics found its exponent
+// reference stale; the caller then runs the item again with statistics.
+template <int D, int kMode, bool kStats>
+__device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned char* smem) {
     constexpr bool kPaged = kMode == kModePaged, kSparse = kMode == kModeSparse;
     constexpr bool kFp8 = kMode == kModeFp8;
     using T = Tile<D, kPaged, kFp8>;
@@ -199,7 +203,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
             nq = __builtin_amdgcn_readfirstlane(n < 0 ? 0 : min_(n, N));
         }
         off = Nk - nq;
-        if (qb * kBr >= nq) return;
+        if (qb * kBr >= nq) return true;
     }
     // Block-sparse: this item's key tiles are blk_idx[list0 .. list0 + n_list) (clamped into
     // the array, so no read leaves it whatever the offsets hold).
@@ -212,7 +216,10 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
         n_list = __builtin_amdgcn_readfirstlane(e1 - e0);
     }
 
-    const int tid = threadIdx.x;
+    // (opaque per item: values derived from the thread index are not hoisted out of the
+    // item loop, where two item bodies would hold theirs at once)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l32 = lane & 31;
@@ -513,6 +520,24 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
             for (int i = 0; i < D / 32; ++i) acc_o[i] *= alpha;
         }
     };
+    // Causal / ragged mask of half tile hi (first key: block-sparse, of the listed tile at
+    // key position kv_tile) on scores s: the key of register r is kv0 + 16 (r >> 3) + 8 hh +
+    // (r & 7); it is masked when it lies after the query (causal) or at or past the end.
+    auto mask_half = [&](f32x16& s, int hi, int kv_tile) {
+        const int kv0 = kSparse ? kv_tile + 32 * (hi & 1) : 32 * hi;
+        const int lim = (causal ? min_(qrow + off, Nk - 1) : Nk - 1) - kv0 - 8 * hh;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int c = 16 * (r >> 3) + (r & 7);
+            s[r] = c > lim ? -INFINITY : s[r];
+        }
+    };
+    // After a step's MFMAs (which added the previous half tile into O): with statistics, the
+    // lazy O rescale. Without statistics the exponent reference never moves (see the
+    // prologue), so there is nothing to do.
+    auto after_step = [&](bool move, float alpha) {
+        if constexpr (kStats) rescale(move, alpha);
+    };
     // Operand rows of step hi (H8 = hi mod 8, so stages are compile-time): K of half tile
     // hi+1 and V of half tile hi-1.
     struct Bases {
@@ -568,18 +593,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
         bool move = false;
         float e0[8], e1[8];  // exp2 of score pair k (held until packed)
         uint32_t wk[8];      // packed pair k (held until summed)
-        auto mask_scores = [&]() {
-            // first key of this half tile (block-sparse: of the listed tile)
-            const int kv0 = kSparse ? kv_tile + 32 * (hi & 1) : 32 * hi;
-            // key of register r is kv0 + 16 (r >> 3) + 8 hh + (r & 7); masked: key > qrow
-            // (causal) or key >= N, i.e. c > lim
-            const int lim = (causal ? min_(qrow + off, Nk - 1) : Nk - 1) - kv0 - 8 * hh;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int c = 16 * (r >> 3) + (r & 7);
-                s_cur[r] = c > lim ? -INFINITY : s_cur[r];
-            }
-        };
+        auto mask_scores = [&]() { mask_half(s_cur, hi, kv_tile); };
         // pair k: exp2 in phase ph_e + k, packed one phase later, summed one phase after that
         auto pair_stages = [&](int ph, int ph_e) {
             const int ke = ph - ph_e, kp = ke - 1, ks = ke - 2;
@@ -596,6 +610,12 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
             }
         };
         auto phase = [&](int ph) {
+            if constexpr (!kStats) {
+                // no row maximum: the exponentials start at once against the current reference
+                if (ph == 0 && __builtin_expect(masked, 0)) mask_scores();
+                pair_stages(ph, 5);
+                return;
+            }
             if (ph == 0) {
                 if (__builtin_expect(masked, 0)) mask_scores();
                 t0 = vmax(vmax(s_cur[0], s_cur[1]), s_cur[2]);
@@ -652,7 +672,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
                 __builtin_amdgcn_sched_barrier(0);
             }
             asm volatile("" : "+v"(pk_cur[0]), "+v"(pk_cur[1]), "+v"(l_part));
-            rescale(move, alpha);
+            after_step(move, alpha);
             return;
         }
 #pragma unroll
@@ -683,7 +703,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
         // The probabilities are first used by the next step; without this the compiler sinks
         // their exponentials past the rescale branch, away from the MFMAs they overlap.
         asm volatile("" : "+v"(pk_cur[0]), "+v"(pk_cur[1]), "+v"(l_part));
-        rescale(move, alpha);
+        after_step(move, alpha);
     };
     // Tiles before n_plain need no mask in any wave of the workgroup: all their keys precede
     // the workgroup's first query row (causal) and the end of the sequence. The others mask
@@ -732,6 +752,21 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
         }
     }
     advance(3);
+    if constexpr (!kStats) {
+        // Without statistics the exponent reference is fixed for the whole item at the row
+        // maximum of the first half tile's admissible scores (a row with none there starts at
+        // -1e30). It is a maximum of real scores, so the row's largest weight stays at least 1
+        // and a weight that underflows is negligible next to it; a score far above it makes
+        // the row sum overflow, which the end of the item detects.
+        const bool masked0 = kSparse ? kvq0 >= n_plain * kBc : n_plain == 0;
+        f32x16 t = sa;
+        if (masked0) mask_half(t, 0, kvq0);
+        float u = t[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) u = vmax(u, t[r]);
+        u = pair32_vmax(u) * scale_log2;
+        m_ref = u > -1e30f ? u : -1e30f;
+    }
     {
         const bool masked0 = kSparse ? kvq0 >= n_plain * kBc : n_plain == 0;
         step(0, kvq0, std::integral_constant<int, 0>{}, sa, sb, pb, pa, masked0, fr, kq, No{}, Yes{});
@@ -776,7 +811,6 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
     wait_dma_all();  // no load may still be writing LDS when the item ends
     barrier_lds();   // and no wave still reads it when the next item's loads start
     }
-
     // ---- epilogue: O / l, bf16, optional row statistics ----
     float l_tot = pair32_sum(l_part);
     if constexpr (kPaged) {
@@ -806,6 +840,26 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
             if (l_out) l_out[ridx] = (l_tot > 0.f) ? l_tot * exp2_hw(m_ref - m_run) : 0.f;
         }
     }
+    if constexpr (!kStats) {
+        // Every weight stayed at most 2^100 (and finite) iff the row sums did: then no
+        // product overflowed. Otherwise the whole workgroup runs the item again with
+        // statistics, which rewrites every output row the garbage above went to (the decision
+        // must be uniform: the item's loads and barriers are shared).
+        // Each wave reports in one word of the tile area, idle at this point (no load in
+        // flight, no wave reading it); the second barrier keeps the next item's loads from
+        // overwriting the words before every wave has read them.
+        int* flags = reinterpret_cast<int*>(smem);
+        const bool bad = __any(!(l_part <= 0x1p100f));
+        if ((threadIdx.x & 63) == 0) flags[wave] = bad ? 1 : 0;
+        barrier_lds();
+        int any = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) any |= flags[w];
+        barrier_lds();
+        if (any) return false;
+    }
+
+    return true;
 }
 
 // Persistent grid: one workgroup per CU (the LDS allows no second one), a multiple of the 8
@@ -815,10 +869,11 @@ __device__ __forceinline__ void fwd_item(const FwdArgs& a, int item, unsigned ch
 // r * W + j (r even) or r * W + W - 1 - j (r odd). The list runs heaviest query block first,
 // so the snake pairs heavy with light items and the workgroups finish together; and a
 // workgroup moves to its next item without a new launch.
-template <int D, int kMode>
+template <int D, int kMode, bool kStats>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(FwdArgs a) {
     using T = Tile<D, kMode == kModePaged, kMode == kModeFp8>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * (T::kKStage + T::kVStage)];
+
     const int per_unit = a.nqb * (a.Hq / a.Hkv);  // items of one KV group
     const int n_kvg = a.B * a.Hkv;
     const int total = n_kvg * per_unit;
@@ -845,7 +900,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(FwdArgs a) {
         } else {
             item = seg0 + local;
         }
-        fwd_item<D, kMode>(a, item, smem);
+        if (!fwd_item<D, kMode, kStats>(a, item, smem)) fwd_item<D, kMode, true>(a, item, smem);
     }
 }
 
@@ -858,14 +913,21 @@ hipError_t launch_sp(const FwdArgs& a, int d, hipStream_t stream) {
     const long long slots = (long long)(device_cus() / kXcds) * kXcds;
     long long grid = (items + kXcds - 1) / kXcds * kXcds;
     if (grid > slots) grid = slots;
-    if (d == 128)
-        hipLaunchKernelGGL((fwd_bf16_sp_kernel<128, kMode>), dim3((unsigned)grid), dim3(kThreads), 0,
-                           stream, a);
-    else if constexpr (kMode != kModeFp8)
-        hipLaunchKernelGGL((fwd_bf16_sp_kernel<64, kMode>), dim3((unsigned)grid), dim3(kThreads), 0,
-                           stream, a);
-    else
+    const bool stats = a.m_out != nullptr || a.l_out != nullptr;
+    const dim3 g((unsigned)grid), blk(kThreads);
+    if (d == 128) {
+        if (stats)
+            hipLaunchKernelGGL((fwd_bf16_sp_kernel<128, kMode, true>), g, blk, 0, stream, a);
+        else
+            hipLaunchKernelGGL((fwd_bf16_sp_kernel<128, kMode, false>), g, blk, 0, stream, a);
+    } else if constexpr (kMode != kModeFp8) {
+        if (stats)
+            hipLaunchKernelGGL((fwd_bf16_sp_kernel<64, kMode, true>), g, blk, 0, stream, a);
+        else
+            hipLaunchKernelGGL((fwd_bf16_sp_kernel<64, kMode, false>), g, blk, 0, stream, a);
+    } else {
         return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 }  // namespace

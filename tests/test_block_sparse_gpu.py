@@ -18,7 +18,9 @@ def dev():
     return cuda_device()
 
 
-def run(x, rows, dev, causal):
+def run(x, rows, dev, causal, stats=True):
+    """Returns ((O, m, l) or O alone when not `stats`), offsets, indices. Without statistics the
+    library runs its softmax without per-tile row maxima (another kernel instance)."""
     import torch
 
     offs, idx = gen.block_csr(rows)
@@ -27,7 +29,7 @@ def run(x, rows, dev, causal):
     it = torch.from_numpy(idx if idx.size else np.zeros(1, np.int32)).to(dev)
     if not idx.size:
         it = it[:0]
-    res = fa.fa_fwd_block_sparse(q, k, v, ot, it, scale=x.scale, causal=causal, return_stats=True)
+    res = fa.fa_fwd_block_sparse(q, k, v, ot, it, scale=x.scale, causal=causal, return_stats=stats)
     torch.cuda.synchronize()
     return res, offs, idx
 
@@ -66,6 +68,9 @@ def test_block_sparse_random_masks(case, dev):
         rows[2] = [nkb - 1, 0, 3 % nkb]           # out of order, with the ragged last block
     res, offs, idx = run(x, rows, dev, causal)
     check(res, x, offs, idx, causal, "block-sparse O")
+    o2, _, _ = run(x, rows, dev, causal, stats=False)
+    o_ref, _, _ = oracle.attention_block_sparse(x.q, x.k, x.v, x.scale, causal, offs, idx, BQ, BK)
+    assert_close(to_np(o2), o_ref, "bf16", "block-sparse O without statistics")
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -85,6 +90,10 @@ def test_block_sparse_full_lists_equal_dense_bitwise(causal, d, dev):
     o_d, m_d, l_d = fa.fa_fwd(q, k, v, scale=x.scale, causal=causal, return_stats=True)
     torch.cuda.synchronize()
     assert torch.equal(o, o_d) and torch.equal(m, m_d) and torch.equal(l, l_d)
+    o2, _, _ = run(x, rows, dev, causal, stats=False)
+    o2_d = fa.fa_fwd(q, k, v, scale=x.scale, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o2_d)
 
 
 def test_block_sparse_local_global_pattern(dev):
@@ -121,6 +130,7 @@ def test_block_sparse_workload_sampled_rows(dev):
     (o, m, l), offs, idx = run(x, rows, dev, cfg.causal)
     o, m, l = to_np(o), to_np(m), to_np(l)
     assert np.isfinite(o).all()
+    o2 = to_np(run(x, rows, dev, cfg.causal, stats=False)[0])  # the launch the bench times
     rng = np.random.default_rng(730)
     nqb = cfg.N // BQ
     G = cfg.Hq // cfg.Hkv
@@ -132,5 +142,6 @@ def test_block_sparse_workload_sampled_rows(dev):
         o_ref, m_ref, l_ref = oracle.attention_head(x.q[b, h, i:i + 1], x.k[b, h // G][keys],
                                                     x.v[b, h // G][keys], x.scale, False)
         assert_close(o[b, h, i], o_ref[0], "bf16", f"row (b={b}, h={h}, i={i})")
+        assert_close(o2[b, h, i], o_ref[0], "bf16", f"row (b={b}, h={h}, i={i}) without statistics")
         assert abs(m[b, h, i] - m_ref[0]) <= 2e-3
-        assert abs(l[b, h, i] - l_ref[0]) <= 2e-3 * l_ref[0]
+        assert abs(l[b, h, i] - l_ref[0]) <= L_RTOL_BF16 * l_ref[0]

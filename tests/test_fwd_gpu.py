@@ -64,6 +64,8 @@ def test_fwd_small_shapes(case, dev):
     assert_close(to_np(o), o_ref, dtype, "O")
     np.testing.assert_allclose(to_np(m), m_ref, atol=1e-5 if dtype == "f32" else 1e-3, rtol=0)
     np.testing.assert_allclose(to_np(l), l_ref, rtol=1e-5 if dtype == "f32" else L_RTOL_BF16)
+    # without statistics (bf16: the softmax without per-tile row maxima)
+    assert_close(to_np(run_fwd(x, dev, stats=False)), o_ref, dtype, "O without statistics")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -124,9 +126,10 @@ def test_config2_full(dev):
 @pytest.mark.timeout(1200)
 @pytest.mark.parametrize("cfg_id", [3, 4])
 def test_config_full_size_every_row(cfg_id, dev):
-    """The full-size workload in the bench's launch configuration: every row of every head of
-    O, m and l against the oracle (run head by head in worker processes), plus a second run
-    that must be bitwise identical."""
+    """The full-size workload: every row of every head of O, m and l (the kernel instance with
+    row statistics) and of O from the launch the bench times (no statistics: the softmax
+    without per-tile row maxima) against the oracle, run head by head in worker processes;
+    a second run of the latter must be bitwise identical."""
     import torch
 
     from oracle import pool
@@ -139,10 +142,12 @@ def test_config_full_size_every_row(cfg_id, dev):
     v = gen.to_torch(x.v, "bf16", dev)
     o, m, l = fa.fa_fwd(q, k, v, scale=x.scale, causal=True, return_stats=True)
     o2 = fa.fa_fwd(q, k, v, scale=x.scale, causal=True)
+    o3 = fa.fa_fwd(q, k, v, scale=x.scale, causal=True)
     torch.cuda.synchronize()
-    assert torch.equal(o, o2), "two runs differ: the kernel is not deterministic"
+    assert torch.equal(o2, o3), "two runs differ: the kernel is not deterministic"
     o_np, m_np, l_np = o.float().cpu().numpy(), m.cpu().numpy(), l.cpu().numpy()
-    del q, k, v, o, o2, m, l
+    o2_np = o2.float().cpu().numpy()
+    del q, k, v, o, o2, o3, m, l
     torch.cuda.empty_cache()
     G = cfg.Hq // cfg.Hkv
     heads = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq)]
@@ -151,7 +156,9 @@ def test_config_full_size_every_row(cfg_id, dev):
     worst = 0.0
     for n, ((b, h), (o_ref, m_ref, l_ref)) in enumerate(zip(heads, refs)):
         st = assert_close(o_np[b, h], o_ref, "bf16", f"config {cfg_id} O[b={b},h={h}]")
-        worst = max(worst, st["max_abs"])
+        st2 = assert_close(o2_np[b, h], o_ref, "bf16",
+                           f"config {cfg_id} O[b={b},h={h}] without statistics")
+        worst = max(worst, st["max_abs"], st2["max_abs"])
         np.testing.assert_allclose(m_np[b, h], m_ref, atol=2e-3, rtol=0)
         np.testing.assert_allclose(l_np[b, h], l_ref, rtol=L_RTOL_BF16)
         if n % 8 == 7:
@@ -212,3 +219,23 @@ def test_fwd_peaky_rows_large_scores(dev):
     o_ref, m_ref, l_ref = oracle.attention(x.q, x.k, x.v, x.scale, False)
     assert_close(to_np(o), o_ref, "bf16", "peaky O")
     assert math.isfinite(float(to_np(m).max()))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [128, 64])
+def test_fwd_without_stats_recovers_from_a_stale_reference(causal, d, dev):
+    """Without statistics the exponent reference is the first half tile's row maximum. Keys
+    past the first 32 whose scores lie hundreds of log2 units above it overflow the row sums;
+    the work item is then computed again with per-tile maxima. The result must still match the
+    oracle, with and without statistics, and across a first tile that some rows see only
+    partly (causal)."""
+    log_case(f"fa_fwd stale reference d={d} causal={causal}")
+    x = gen.fwd_inputs(1, 4, 2, 700, d, seed=12, dtype="bf16", causal=causal, scale=1.0)
+    x.k[:, :, :32] *= np.float32(0.01)   # the first half tile: scores near 0
+    x.k[:, :, 32:] *= np.float32(4.0)    # the rest: scores of a few hundred
+    x.k[:] = gen.round_to_bf16(x.k)
+    o_ref, _, _ = oracle.attention(x.q, x.k, x.v, x.scale, causal)
+    o = run_fwd(x, dev, stats=False)
+    assert_close(to_np(o), o_ref, "bf16", "O without statistics")
+    o2, m2, l2 = run_fwd(x, dev, stats=True)
+    assert_close(to_np(o2), o_ref, "bf16", "O with statistics")

@@ -33,11 +33,12 @@ def upload(x, dev):
     )
 
 
-def run(t, scale, causal):
+def run(t, scale, causal, stats=True):
+    """(O, m, l), or O alone when not `stats` (the softmax without per-tile row maxima)."""
     import torch
 
     res = fa.fa_fwd_paged(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["seq_lens"],
-                          scale=scale, causal=causal, return_stats=True)
+                          scale=scale, causal=causal, return_stats=stats)
     torch.cuda.synchronize()
     return res
 
@@ -75,6 +76,8 @@ def test_prefill_paged_small(case, dev):
     o_ref, m_ref, l_ref = oracle.prefill_paged(x.q, x.k_seqs, x.v_seqs, x.scale, causal)
     assert_close(to_np(o), o_ref, "bf16", "paged prefill O")
     check_stats(m, l, m_ref, l_ref)
+    assert_close(to_np(run(t, x.scale, causal, stats=False)), o_ref, "bf16",
+                 "paged prefill O without statistics")
 
 
 def test_prefill_paged_matches_dense_forward_bitwise(dev):
@@ -93,6 +96,10 @@ def test_prefill_paged_matches_dense_forward_bitwise(dev):
     torch.cuda.synchronize()
     assert torch.equal(o_p, o_d)
     assert torch.equal(m_p, m_d) and torch.equal(l_p, l_d)
+    o2_p = run(t, x.scale, True, stats=False)
+    o2_d = fa.fa_fwd(t["q"], k, v, scale=x.scale, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o2_p, o2_d)
 
 
 def _shared_prefix_inputs(B, Hkv, d, P, suffix_lens, seed):
@@ -184,6 +191,7 @@ def test_prefill_paged_workload_sampled_rows(dev):
     o, m, l = run(t, x.scale, cfg.causal)
     o, m, l = to_np(o), to_np(m), to_np(l)
     assert np.isfinite(o).all()
+    o2 = to_np(run(t, x.scale, cfg.causal, stats=False))  # the launch the bench times
     rng = np.random.default_rng(650)
     G = cfg.Hq // cfg.Hkv
     for _ in range(48):
@@ -196,8 +204,9 @@ def test_prefill_paged_workload_sampled_rows(dev):
         vs = [x.v_seqs[b][h // G:h // G + 1, :pos + 1]]
         o_ref, m_ref, l_ref = oracle.prefill_paged(x.q[b:b + 1, h:h + 1, i:i + 1], ks, vs, x.scale, True)
         assert_close(o[b, h, i], o_ref[0, 0, 0], "bf16", f"row (b={b}, h={h}, i={i})")
+        assert_close(o2[b, h, i], o_ref[0, 0, 0], "bf16", f"row (b={b}, h={h}, i={i}) without statistics")
         assert abs(m[b, h, i] - m_ref[0, 0, 0]) <= 2e-3
-        assert abs(l[b, h, i] - l_ref[0, 0, 0]) <= 2e-3 * l_ref[0, 0, 0]
+        assert abs(l[b, h, i] - l_ref[0, 0, 0]) <= L_RTOL_BF16 * l_ref[0, 0, 0]
 
 
 def test_prefill_paged_empty_calls_are_noops(dev):
