@@ -613,7 +613,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
             if constexpr (!kStats) {
                 // no row maximum: the exponentials start at once against the current reference
                 if (ph == 0 && __builtin_expect(masked, 0)) mask_scores();
-                pair_stages(ph, 5);
+                pair_stages(ph, 6);
                 return;
             }
             if (ph == 0) {
