@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--cpu-heads4", type=int, default=32,
                     help="heads of the N=32768 GQA workload the oracle runs on (of 32)")
     ap.add_argument("--only", choices=["fwd", "decode", "fwd2", "fwd4", "paged", "sparse", "bwd",
-                                       "fp8"], default=None,
+                                       "fp8", "fp8v"], default=None,
                     help="time one kernel only (profiling runs)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter scaling)")
@@ -125,10 +125,11 @@ def summarize(paths, kernel=None):
 
 # Kernels whose HBM traffic is reported, with the source file each is compiled from.
 TRAFFIC_KERNELS = {
-    "fwd": ("fwd_bf16_sp_kernel<128, 0>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
-    "paged": ("fwd_bf16_sp_kernel<128, 1>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
-    "sparse": ("fwd_bf16_sp_kernel<128, 2>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
-    "fp8": ("fwd_bf16_sp_kernel<128, 3>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
+    "fwd": ("fwd_bf16_sp_kernel<128, 0, false>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
+    "paged": ("fwd_bf16_sp_kernel<128, 1, false>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
+    "sparse": ("fwd_bf16_sp_kernel<128, 2, false>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
+    "fp8": ("fwd_bf16_sp_kernel<128, 3, false>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
+    "fp8v": ("fwd_bf16_sp_kernel<128, 4, false>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
     "decode": ("decode_mx_kernel", "exact_tiled_attention_24_amd/csrc/decode_mx.hip"),
 }
 COPY_KERNEL = "copyBuffer"
@@ -224,6 +225,7 @@ def main():
     do_sparse = args.only in (None, "sparse")
     do_bwd = args.only in (None, "bwd")
     do_fp8 = args.only in (None, "fp8")
+    do_fp8v = args.only in (None, "fp8v")
     do_fwd2 = args.only in (None, "fwd2") and args.fwd_config != 2
     do_fwd4 = args.only in (None, "fwd4") and args.fwd_config != 4
 
@@ -332,6 +334,20 @@ def main():
 
     def run_fp8():
         fa.fa_fwd_fp8(f8_q, f8_k, f8_v, scale=fp8_scale, causal=f8cfg.causal, out=f8_o)
+
+    if do_fp8v:
+        # the forward workload with Q, K and V in e4m3 (P rounded to e4m3, P V on fp8 too)
+        v8cfg = gen.CONFIGS[args.fwd_config]
+        v8x = gen.fp8_fwd_inputs(v8cfg.B, v8cfg.Hq, v8cfg.Hkv, v8cfg.N, v8cfg.d, v8cfg.seed,
+                                 causal=v8cfg.causal, k_mult=v8cfg.k_mult, v_fp8=True)
+        v8_q, v8_k, v8_v = (gen.to_torch(t, "e4m3", dev) for t in (v8x.q, v8x.k, v8x.v))
+        v8_o = torch.empty(v8x.q.shape, dtype=torch.bfloat16, device=dev)
+        fp8v_flops = v8cfg.flops()
+        fp8v_scale = v8x.scale
+        del v8x
+
+    def run_fp8v():
+        fa.fa_fwd_fp8(v8_q, v8_k, v8_v, scale=fp8v_scale, causal=v8cfg.causal, out=v8_o)
 
     def run_bwd():
         fa.fa_bwd(b_q, b_k, b_v, b_o, b_do, b_m, b_l, scale=bwd_scale, causal=bcfg.causal,
@@ -447,6 +463,19 @@ def main():
         torch.cuda.synchronize()
         fp8_ms = np.array([a.elapsed_time(b) for a, b in fev])
 
+    fp8v_ms = None
+    if do_fp8v:
+        for _ in range(args.warmup):
+            run_fp8v()
+        vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in vev:
+            a.record(stream)
+            run_fp8v()
+            b.record(stream)
+        torch.cuda.synchronize()
+        fp8v_ms = np.array([a.elapsed_time(b) for a, b in vev])
+
     bwd_ms = None
     if do_bwd:
         for _ in range(min(args.warmup, 2)):
@@ -496,7 +525,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4) if fwd_tflops else None,
             "traffic": traffic.get("fwd"),
-            "kernel": "fwd_bf16_sp_kernel<128, 0>",
+            "kernel": "fwd_bf16_sp_kernel<128, 0, false>",
             "avg_launch_ms": round(float(fwd_ms.mean()), 5) if do_fwd else None,
         },
         "decode": {
@@ -527,7 +556,7 @@ def main():
             "tokens_per_s": round(c.B * c.N / (ms.mean() * 1e-3), 1),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                         "kernel": f"fwd_bf16_sp_kernel<{c.d}, 0>"},
+                         "kernel": f"fwd_bf16_sp_kernel<{c.d}, 0, false>"},
         }
     if do_paged:
         p_tflops = paged_flops / (paged_ms.mean() * 1e-3) / 1e12
@@ -538,7 +567,7 @@ def main():
             "tokens_per_s": round(pcfg.B * pcfg.Nq / (paged_ms.mean() * 1e-3), 1),
             "roofline": {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4),
-                         "traffic": traffic.get("paged"), "kernel": "fwd_bf16_sp_kernel<128, 1>"},
+                         "traffic": traffic.get("paged"), "kernel": "fwd_bf16_sp_kernel<128, 1, false>"},
         }
     if do_sparse:
         s_tflops = sparse_flops / (sparse_ms.mean() * 1e-3) / 1e12
@@ -549,7 +578,7 @@ def main():
             "tokens_per_s": round(scfg.B * scfg.N / (sparse_ms.mean() * 1e-3), 1),
             "roofline": {"bound": "mfma", "achieved": round(s_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(s_tflops / PEAK_BF16_TFLOPS, 4),
-                         "traffic": traffic.get("sparse"), "kernel": "fwd_bf16_sp_kernel<128, 2>"},
+                         "traffic": traffic.get("sparse"), "kernel": "fwd_bf16_sp_kernel<128, 2, false>"},
         }
     if do_fp8:
         f_tflops = fp8_flops / (fp8_ms.mean() * 1e-3) / 1e12
@@ -563,7 +592,17 @@ def main():
                          "peak": round(mixed_peak, 1), "unit": "TFLOP/s",
                          "frac": round(f_tflops / mixed_peak, 4),
                          "peak_note": "S on fp8 (5.0 PFLOP/s), P V on bf16 (2.5 PFLOP/s)",
-                         "traffic": traffic.get("fp8"), "kernel": "fwd_bf16_sp_kernel<128, 3>"},
+                         "traffic": traffic.get("fp8"), "kernel": "fwd_bf16_sp_kernel<128, 3, false>"},
+        }
+    if do_fp8v:
+        v_tflops = fp8v_flops / (fp8v_ms.mean() * 1e-3) / 1e12
+        result["fp8_qkv"] = {
+            "workload": f"{v8cfg.name} with e4m3 Q, K and V (weights rounded to e4m3)",
+            "algorithmic_flops": fp8v_flops, "value": round(v_tflops, 2), "unit": "TFLOP/s",
+            "avg_call_ms": round(float(fp8v_ms.mean()), 5),
+            "roofline": {"bound": "mfma", "achieved": round(v_tflops, 2), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(v_tflops / PEAK_FP8_TFLOPS, 4),
+                         "traffic": traffic.get("fp8v"), "kernel": "fwd_bf16_sp_kernel<128, 4, false>"},
         }
     if do_bwd:
         b_tflops = bwd_flops / (bwd_ms.mean() * 1e-3) / 1e12

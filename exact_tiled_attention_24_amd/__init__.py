@@ -13,7 +13,7 @@ Entry points (same names as the C ABI):
     fa_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=True, ...)
     fa_fwd_block_sparse(q, k, v, block_offsets, block_indices, scale=None, causal=False, ...)
     fa_bwd(q, k, v, o, dout, m, l, scale=None, causal=False, workspace=None)
-    fa_fwd_fp8(q_e4m3, k_e4m3, v, scale=None, causal=False, out=None, return_stats=False)
+    fa_fwd_fp8(q_e4m3, k_e4m3, v_bf16_or_e4m3, scale=None, causal=False, out=None, return_stats=False)
     fa_merge(o_parts, m_parts, l_parts, out_dtype=torch.float32, return_stats=False)
     fa_decode_workspace_bytes(...), fa_decode_plan_splits(...), fa_status_string(code)
 """
@@ -34,6 +34,7 @@ FA_ERR_WORKSPACE_TOO_SMALL = 3
 FA_ERR_HIP = 4
 FA_F32 = 0
 FA_BF16 = 1
+FA_E4M3 = 2
 
 _lib = None
 
@@ -75,7 +76,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_block_sparse.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                         i32, i32, f32, i32, vp]
     lib.fa_fwd_block_sparse.restype = i32
-    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.fa_fwd_fp8.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.fa_fwd_fp8.restype = i32
     lib.fa_bwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                            f32, i32, vp, sz, vp]
@@ -292,13 +293,20 @@ def fa_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=
 
 def fa_fwd_fp8(q, k, v, scale=None, causal=False, out=None, return_stats=False):
     """Forward with fp8 queries and keys. q: uint8 e4m3 codes [B, Hq, N, d]; k: uint8 e4m3 codes
-    [B, Hkv, N, d]; v: bf16 [B, Hkv, N, d]. Returns O bf16 [B, Hq, N, d] (or (O, m, l))."""
+    [B, Hkv, N, d]; v: [B, Hkv, N, d] bf16, or uint8 e4m3 codes (then P is rounded to e4m3 and
+    P V runs on the fp8 matrix cores too). Returns O bf16 [B, Hq, N, d] (or (O, m, l))."""
     torch = _torch()
     lib = load_library()
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("q must be [B, Hq, N, d] and k, v [B, Hkv, N, d]")
-    if q.dtype != torch.uint8 or k.dtype != torch.uint8 or v.dtype != torch.bfloat16:
-        raise TypeError("q and k must be uint8 e4m3 codes and v bfloat16")
+    if q.dtype != torch.uint8 or k.dtype != torch.uint8:
+        raise TypeError("q and k must be uint8 e4m3 codes")
+    if v.dtype == torch.bfloat16:
+        v_dt = FA_BF16
+    elif v.dtype == torch.uint8:
+        v_dt = FA_E4M3
+    else:
+        raise TypeError("v must be bfloat16 or uint8 e4m3 codes")
     B, Hq, N, d = q.shape
     if k.shape[0] != B or k.shape[2:] != q.shape[2:]:
         raise ValueError("shape mismatch")
@@ -310,7 +318,7 @@ def fa_fwd_fp8(q, k, v, scale=None, causal=False, out=None, return_stats=False):
     _require_gpu(q, k, v, o, m, l)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     with torch.cuda.device(q.device):
-        code = lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(m), _ptr(l), B, Hq,
+        code = lib.fa_fwd_fp8(v_dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(m), _ptr(l), B, Hq,
                               k.shape[1], N, d, scale, 1 if causal else 0, _stream(q.device))
     _check(code, "fa_fwd_fp8")
     return (o, m, l) if return_stats else o

@@ -104,7 +104,7 @@ const char* fa_status_string(fa_status s) {
 fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void* o,
                  float* m_out, float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
                  int causal, void* stream) {
-    if (dt != FA_F32 && dt != FA_BF16) return FA_ERR_INVALID_ARGUMENT;
+    if (dt != FA_F32 && dt != FA_BF16) return dt == FA_E4M3 ? FA_ERR_UNSUPPORTED : FA_ERR_INVALID_ARGUMENT;
     if (B < 0 || Hq < 0 || Hkv < 0 || N < 0) return FA_ERR_INVALID_ARGUMENT;
     if (!scale_ok(scale)) return FA_ERR_INVALID_ARGUMENT;
     if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0)) return FA_ERR_INVALID_ARGUMENT;
@@ -219,9 +219,10 @@ fa_status fa_decode_splitk_noalloc(fa_dtype dt, const void* q, const void* k_cac
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* m_out,
-                     float* l_out, int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                     void* stream) {
+fa_status fa_fwd_fp8(fa_dtype v_dt, const void* q, const void* k, const void* v, void* o,
+                     float* m_out, float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
+                     int causal, void* stream) {
+    if (v_dt != FA_BF16 && v_dt != FA_E4M3) return FA_ERR_INVALID_ARGUMENT;
     if (B < 0 || Hq < 0 || Hkv < 0 || N < 0) return FA_ERR_INVALID_ARGUMENT;
     if (!scale_ok(scale)) return FA_ERR_INVALID_ARGUMENT;
     if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0)) return FA_ERR_INVALID_ARGUMENT;
@@ -232,8 +233,9 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float
         return FA_ERR_INVALID_ARGUMENT;
     if (!head_fits(N, d)) return FA_ERR_UNSUPPORTED;
     if (((long long)N + 255) / 256 * B * Hq >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
-    const hipError_t e = fa::launch_fwd_fp8qk_sp(q, k, v, o, m_out, l_out, B, Hq, Hkv, N, d, scale,
-                                                 causal ? 1 : 0, static_cast<hipStream_t>(stream));
+    const hipError_t e = fa::launch_fwd_fp8qk_sp(q, k, v, v_dt == FA_E4M3 ? 1 : 0, o, m_out, l_out,
+                                                 B, Hq, Hkv, N, d, scale, causal ? 1 : 0,
+                                                 static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

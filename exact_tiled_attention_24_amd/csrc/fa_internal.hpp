@@ -45,11 +45,12 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            void* dv, int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                            float* lse2, float* dsum, hipStream_t stream);
 
-// Forward with fp8 (OCP e4m3) Q and K: S^T on the fp8 matrix cores, softmax and P V as in the
-// bf16 kernel (V, O bf16). d = 128.
-hipError_t launch_fwd_fp8qk_sp(const void* q, const void* k, const void* v, void* o, float* m_out,
-                               float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
-                               int causal, hipStream_t stream);
+// Forward with fp8 (OCP e4m3) Q and K: S^T on the fp8 matrix cores. v_fp8 == 0: V bf16, P
+// rounded to bf16, P V as in the bf16 kernel; v_fp8 != 0: V e4m3, P rounded to e4m3, P V on the
+// fp8 matrix cores too. O bf16; d = 128.
+hipError_t launch_fwd_fp8qk_sp(const void* q, const void* k, const void* v, int v_fp8, void* o,
+                               float* m_out, float* l_out, int B, int Hq, int Hkv, int N, int d,
+                               float scale, int causal, hipStream_t stream);
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* m_out,
                           float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,

@@ -79,7 +79,8 @@ constexpr int kBc = 64;           // keys per tile (two 32-key half tiles)
 constexpr unsigned kPadOffset = 0x80000000u;
 constexpr int kStages = 4;       // LDS stages of K and of V
 constexpr int kXcds = 8;
-constexpr float kLazy = 8.f;
+constexpr float kLazy = 8.f;      // the exponent reference moves once a row maximum passes it by 2^8
+constexpr float kV8Head = 4.f;    // e4m3 weights: a moved reference sits 2^4 below the maximum
 constexpr int kAhead = 4;         // LDS operand reads kept in flight
 constexpr int kBufferDword3 = 0x00020000;
 
@@ -88,6 +89,8 @@ typedef const __attribute__((address_space(3))) unsigned char* lds_cptr;
 typedef const __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
 
 __device__ __forceinline__ int kappa(int m) {
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -101,18 +104,21 @@ __device__ __forceinline__ void barrier_lds() {
 }
 
 constexpr int kPageTok = 16;      // tokens per page of the paged cache
-constexpr int kModeDense = 0, kModePaged = 1, kModeSparse = 2, kModeFp8 = 3;
+constexpr int kModeDense = 0, kModePaged = 1, kModeSparse = 2, kModeFp8 = 3, kModeFp8V = 4;
 typedef int v8i32 __attribute__((ext_vector_type(8)));
 
-template <int D, bool kPaged, bool kFp8 = false>
+template <int D, bool kPaged, bool kFp8 = false, bool kV8 = false>
 struct Tile {
     // K element bytes (fp8 e4m3 K: 1); the 16 B pad keeps a 16 B read of 16 rows in 16
     // distinct bank groups for both row lengths
     static constexpr int kKElem = kFp8 ? 1 : 2;
     static constexpr int kKRow = D * kKElem + 16;                     // padded K row, bytes
-    // padded V row, bytes: the 64 B pad puts the four rows a transposing read touches per
-    // cycle in four different 64 B bank windows
-    static constexpr int kVRow = D * 2 + 64;
+    // V element bytes (fp8 e4m3 V: 1) and padded V row: bf16, the 64 B pad puts the four
+    // rows a transposing read touches per cycle in four different 64 B bank windows; e4m3,
+    // 144 B rows put the eight consecutive rows of an 8-bit transposing read's 16-lane group
+    // in eight distinct 16 B bank groups
+    static constexpr int kVElem = kV8 ? 1 : 2;
+    static constexpr int kVRow = kV8 ? D + 16 : D * 2 + 64;
     // paged: a K page (16 padded rows) occupies whole KiB, so no 1 KiB load spans two pages
     static constexpr int kKPage = kPaged ? (kPageTok * kKRow + 1023) / 1024 * 1024 : kPageTok * kKRow;
     static constexpr int kKStage = kPaged ? (kBc / kPageTok) * kKPage : kBc * kKRow;
@@ -159,9 +165,10 @@ struct FwdArgs {
 template <int D, int kMode, bool kStats>
 __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned char* smem) {
     constexpr bool kPaged = kMode == kModePaged, kSparse = kMode == kModeSparse;
-    constexpr bool kFp8 = kMode == kModeFp8;
-    using T = Tile<D, kPaged, kFp8>;
-    constexpr int kKTile = kBc * D * T::kKElem, kVTile = kBc * D * 2;  // HBM bytes of a tile
+    constexpr bool kV8 = kMode == kModeFp8V;              // e4m3 V, P V on the fp8 matrix cores
+    constexpr bool kFp8 = kMode == kModeFp8 || kV8;       // e4m3 Q and K
+    using T = Tile<D, kPaged, kFp8, kV8>;
+    constexpr int kKTile = kBc * D * T::kKElem, kVTile = kBc * D * T::kVElem;  // HBM bytes of a tile
     const uint16_t* __restrict__ q = a.q;
     const uint16_t* __restrict__ k = a.k;
     const uint16_t* __restrict__ v = a.v;
@@ -188,7 +195,6 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     const uint16_t* qh = q + qoff;
     // (K addressed in bytes: fp8 K has one byte per element)
     const unsigned char* kh = reinterpret_cast<const unsigned char*>(k) + koff * T::kKElem;
-    const uint16_t* vh = v + koff;
     // Keys of this item's sequence and the position offset of its queries: query row i sits
     // at position i + off (dense: the N keys, off = 0; paged: the cached length L, clamped to
     // the table, and off = L - Nq, the bottom-right alignment).
@@ -297,7 +303,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         } else {
             const int slot = 1024 * cc + 16 * lane;
             const int row = slot / row_b, col = slot - row * row_b;
-            const int rb = is_k ? D * T::kKElem : D * 2;  // HBM row bytes
+            const int rb = is_k ? D * T::kKElem : D * T::kVElem;  // HBM row bytes
             dma_src[i] = (col < rb ? unsigned(row * rb + col) : kPadOffset) +
                          unsigned(kSparse ? 0 : (is_k ? 3 * kKTile : 2 * kVTile));
             dma_pg[i] = 0;
@@ -376,17 +382,20 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         kPaged ? (a.num_pages > 0 ? (a.num_pages - 1) * (int)stride_bytes + kPageTok * D * 2 : 0)
                : row_end * D * 2);
     const int head_bytes_k = kFp8 ? __builtin_amdgcn_readfirstlane(row_end * D) : head_bytes;
+    const int head_bytes_v = kV8 ? head_bytes_k : head_bytes;
     const size_t kv_page = kPaged ? (size_t)kvh * kPageTok * D : 0;  // KV head within a page
     const __amdgpu_buffer_rsrc_t rsrc_k = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kh + kv_page * 2), (short)0, head_bytes_k, kBufferDword3);
+    // (V addressed in bytes: e4m3 V has one byte per element)
+    const unsigned char* vhb = reinterpret_cast<const unsigned char*>(v) + (koff + kv_page) * T::kVElem;
     const __amdgpu_buffer_rsrc_t rsrc_v =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vh + kv_page), (short)0, head_bytes, kBufferDword3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)vhb, (short)0, head_bytes_v, kBufferDword3);
     // DMA operation i of tile step j (stage phase P = j mod 4): K of tile j + 3 and V of
     // tile j + 2. Written as assembly: the compiler's own form makes it wait for every
     // outstanding load to LDS before each transposing read (it cannot tell the stages
     // apart); the waits here are explicit. Operations whose chunks are all K (or all V) for
     // every wave need no select.
-    auto dma_op = [&](int j, int i, int P) {  // (P is a constant at every call)
+    auto dma_op = [&](int j, int i, int P) {  // P: the stage phase (a constant, or uniform in the e4m3-V steps)
         constexpr int kK = T::kKChunks;
         const bool all_k = kWaves * i + kWaves - 1 < kK, all_v = kWaves * i >= kK;
         const bool is_k = all_k || (!all_v && wave + kWaves * i < kK);
@@ -735,6 +744,169 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     dma_tile(-1, 3);  // K2, V1
     wait_dma_all();
     barrier_lds();
+    if constexpr (kV8) {
+    // ---- e4m3 V: one step per 64-key tile. Step j computes S^T of tile j + 1 (four fp8
+    // MFMAs), the softmax of tile j (both halves against one exponent reference, so that the
+    // tile's P shares it) and O^T += V^T P^T of tile j - 1 on the fp8 matrix cores: one
+    // v_mfma_f32_32x32x64_f8f6f4 per 32 head dimensions, contracting all 64 keys, plus one
+    // against an all-ones operand that adds the tile's row sums of the e4m3 weights to every
+    // row of acc_l (so O / l is a convex combination of V rows with exactly the weights used).
+    // Over a tile, lane (query q, half hh) holds the scores of 32 keys, registers r of the two
+    // halves in order; with K read in kappa order these are keys 16 u + 8 hh + i for byte
+    // t = 8 u + i of the B operand, so P^T is the two halves' weights rounded to e4m3 in
+    // register order, and V^T takes the same keys: four 8-bit transposing reads per lane, each
+    // 8 consecutive V rows (source lane q' + 2 i of a 16-lane group reads row 16 u + 8 hh + i at
+    // byte 8 q' of its 16 head dimensions; lane j of the group receives column j of the 8 rows).
+    // The exponent reference moves only when a tile's row maximum passes it by more than 2^8,
+    // and then to 2^4 below that maximum: every weight stays at most 256, inside e4m3's range
+    // (448), and the reference stays at least 2^4 below the row's largest weight, so the
+    // weights that fall below e4m3's normal range (2^-6 of the reference) are under 2^-10 of
+    // the largest one. ----
+    const v8i32 ones8 = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                         0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+    lds_cptr base_v8 = lds + T::kVBase + (8 * hh + ((lane & 15) >> 1)) * T::kVRow +
+                       16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+    asm volatile("" : "+v"(base_v8));
+    static_assert(!kV8 || 3 * T::kVStage + 48 * T::kVRow + 96 < 65536, "V offsets fit the immediate");
+    auto vfrag8 = [&](lds_cptr vst, int db) -> v8i32 {
+        v2i32 r[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            r[u] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(vst + 16 * u * T::kVRow + 32 * db));
+        return v8i32{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+    };
+    f32x16 acc_l8 = f32x16{};
+    // O^T and the row sums += V^T P^T of the V stage at vst with the tile's P in pt
+    auto pv_tile8 = [&](lds_cptr vst, const v8i32& pt) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc_o[db] = mfma_fp8(vfrag8(vst, db), pt, acc_o[db]);
+        acc_l8 = mfma_fp8(ones8, pt, acc_l8);
+    };
+    // Step of tile jt (stage phase P = jt mod 4): its scores c0, c1 (four fp8 MFMAs), then its
+    // softmax beside the five MFMAs of P V of tile jt - 1 (weights pp). The score MFMAs have
+    // no vector work of their own to run beside; the other wave of the SIMD supplies it.
+    auto step8 = [&](int jt, f32x16& c0, f32x16& c1, const v8i32& pp, v8i32& pc, bool masked,
+                     auto with_pv) {
+        constexpr bool kPV = decltype(with_pv)::value;
+        const int P = jt & 3;  // stage phase (the stage offsets are added at run time here)
+        const lds_cptr kc = base_k + P * T::kKStage;                 // K of tile jt
+        const lds_cptr vp = base_v8 + ((P + 3) & 3) * T::kVStage;    // V of tile jt - 1
+        float t0 = 0.f, t1 = 0.f, t2 = 0.f, t3 = 0.f, t4 = 0.f, alpha = 1.f;
+        bool move = false;
+        auto val = [&](int v) -> float { return v < 16 ? c0[v] : c1[v - 16]; };
+        auto exps = [&](int k0, int k1) {  // pairs k0 .. k1 - 1: exponentials, rounded to e4m3
+#pragma unroll
+            for (int k = k0; k < k1; ++k) {
+                const int w = k >> 1;
+                const float x0 = exp2_hw(__builtin_fmaf(val(2 * k), scale_log2, -m_ref));
+                const float x1 = exp2_hw(__builtin_fmaf(val(2 * k + 1), scale_log2, -m_ref));
+                if (k & 1)
+                    pc[w] = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, pc[w], true);
+                else
+                    pc[w] = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+            }
+        };
+        auto phase8 = [&](int ph) {
+            if (ph == 0) {
+                if (__builtin_expect(masked, 0)) {
+                    mask_half(c0, 2 * jt, kvq0);
+                    mask_half(c1, 2 * jt + 1, kvq0);
+                }
+                t0 = vmax(vmax(c0[0], c0[1]), c0[2]);
+                t1 = vmax(vmax(c0[3], c0[4]), c0[5]);
+                t2 = vmax(vmax(c0[6], c0[7]), c0[8]);
+                t3 = vmax(vmax(c0[9], c0[10]), c0[11]);
+                t4 = vmax(vmax(c0[12], c0[13]), c0[14]);
+                t0 = vmax(vmax(t0, t1), t2);
+                t3 = vmax(vmax(t3, t4), c0[15]);
+            } else if (ph == 1) {
+                t1 = vmax(vmax(c1[0], c1[1]), c1[2]);
+                t2 = vmax(vmax(c1[3], c1[4]), c1[5]);
+                t4 = vmax(vmax(c1[6], c1[7]), c1[8]);
+                t1 = vmax(vmax(t1, t2), t4);
+                t2 = vmax(vmax(c1[9], c1[10]), c1[11]);
+                t4 = vmax(vmax(c1[12], c1[13]), c1[14]);
+                t2 = vmax(vmax(t2, t4), c1[15]);
+                const float mx = pair32_vmax(vmax(vmax(t0, t3), vmax(t1, t2))) * scale_log2;
+                m_run = vmax(m_run, mx);
+                move = mx > m_ref + kLazy;
+                const float r_new = move ? mx - kV8Head : m_ref;
+                alpha = move ? exp2_hw(m_ref - r_new) : 1.f;
+                m_ref = r_new;
+            } else if (ph == 2) {
+                exps(0, 5);
+            } else if (ph == 3) {
+                exps(5, 10);
+            } else {
+                exps(10, 16);
+            }
+        };
+        c0 = f32x16{};
+        c1 = f32x16{};
+        // slots 0-3: S^T of the tile (half sl / 2, 64 head dimensions sl % 2), K operands read one
+        // slot ahead; slots 4-8: P V of the previous tile (32 head dimensions each) and its row
+        // sums, V operands one slot ahead, beside the softmax phases
+        auto operand = [&](int sl) -> v8i32 {
+            if (sl < 4) return kfrag8(kc + 32 * (sl >> 1) * T::kKRow, sl & 1);
+            return vfrag8(vp, sl - 4);
+        };
+        v8i32 op[8];
+        op[0] = operand(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int sl = 0; sl < 9; ++sl) {
+            if (sl + 1 < 4 || (kPV && sl + 1 < 8)) op[sl + 1] = operand(sl + 1);
+            if (sl < 4) {
+                if (sl < 2) c0 = mfma_fp8(op[sl], qf8[sl & 1], c0);
+                else c1 = mfma_fp8(op[sl], qf8[sl & 1], c1);
+            } else if (kPV) {
+                if (sl < 8) acc_o[sl - 4] = mfma_fp8(op[sl], pp, acc_o[sl - 4]);
+                else acc_l8 = mfma_fp8(ones8, pp, acc_l8);
+            }
+            if (sl >= 4) phase8(sl - 4);
+#pragma unroll
+            for (int i = 0; i < T::kDmaPerWave; ++i)
+                if (sl == i) dma_op(jt, i, P);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        asm volatile("" : "+v"(pc));
+        if (__builtin_expect(__any(move), 0)) {
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) acc_o[i] *= alpha;
+            acc_l8 *= alpha;
+        }
+    };
+
+    advance(3);
+    v8i32 pa8 = {}, pb8 = {};
+    step8(0, sa, sb, pb8, pa8, n_plain == 0, No{});
+    wait_dma_tile();
+    barrier_lds();
+    // tiles 1 .. n_tiles - 1, two per iteration (odd tiles write pb8, even ones pa8); the
+    // accumulators leave the loop by one exit only
+    auto tile8 = [&](int jt, auto odd_c) {
+        advance(jt + 3);
+        const bool masked = jt >= n_plain;
+        if constexpr (decltype(odd_c)::value)
+            step8(jt, sa, sb, pa8, pb8, masked, Yes{});
+        else
+            step8(jt, sa, sb, pb8, pa8, masked, Yes{});
+        wait_dma_tile();
+        barrier_lds();
+    };
+    int jt = 1;
+    for (; jt + 1 < n_tiles; jt += 2) {
+        tile8(jt, Yes{});
+        tile8(jt + 1, No{});
+    }
+    if (jt < n_tiles) {
+        tile8(jt, Yes{});
+        ++jt;
+    }
+    // the last tile's O update (tile n_tiles - 1: odd ones wrote pb8)
+    pv_tile8(base_v8 + ((n_tiles - 1) & 3) * T::kVStage, ((n_tiles - 1) & 1) ? pb8 : pa8);
+    l_part = acc_l8[0];  // every row of acc_l holds the query's row sum (both lane halves)
+    } else {
     compute_s(sa, 0, 0);
 
     // ---- tile 0: half 0 has no O update yet; its first step issues K3 / V2 ----
@@ -752,7 +924,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         }
     }
     advance(3);
-    if constexpr (!kStats) {
+    if constexpr (!kStats && !kV8) {
         // Without statistics the exponent reference is fixed for the whole item at the row
         // maximum of the first half tile's admissible scores (a row with none there starts at
         // -1e30). It is a maximum of real scores, so the row's largest weight stays at least 1
@@ -808,11 +980,12 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         case 2: compute_pv(pb, 2, 1); break;
         default: compute_pv(pb, 3, 1); break;
     }
+    }
     wait_dma_all();  // no load may still be writing LDS when the item ends
     barrier_lds();   // and no wave still reads it when the next item's loads start
     }
     // ---- epilogue: O / l, bf16, optional row statistics ----
-    float l_tot = pair32_sum(l_part);
+    float l_tot = kV8 ? l_part : pair32_sum(l_part);
     if constexpr (kPaged) {
         // a query before the sequence's first key (causal, L < Nq) or an empty sequence:
         // O = 0, m = -inf, l = 0 (its lanes ran on scores that were all masked)
@@ -840,7 +1013,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
             if (l_out) l_out[ridx] = (l_tot > 0.f) ? l_tot * exp2_hw(m_ref - m_run) : 0.f;
         }
     }
-    if constexpr (!kStats) {
+    if constexpr (!kStats && !kV8) {
         // Every weight stayed at most 2^100 (and finite) iff the row sums did: then no
         // product overflowed. Otherwise the whole workgroup runs the item again with
         // statistics, which rewrites every output row the garbage above went to (the decision
@@ -871,7 +1044,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
 // workgroup moves to its next item without a new launch.
 template <int D, int kMode, bool kStats>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(FwdArgs a) {
-    using T = Tile<D, kMode == kModePaged, kMode == kModeFp8>;
+    using T = Tile<D, kMode == kModePaged, kMode == kModeFp8 || kMode == kModeFp8V, kMode == kModeFp8V>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * (T::kKStage + T::kVStage)];
 
     const int per_unit = a.nqb * (a.Hq / a.Hkv);  // items of one KV group
@@ -920,7 +1093,7 @@ hipError_t launch_sp(const FwdArgs& a, int d, hipStream_t stream) {
             hipLaunchKernelGGL((fwd_bf16_sp_kernel<128, kMode, true>), g, blk, 0, stream, a);
         else
             hipLaunchKernelGGL((fwd_bf16_sp_kernel<128, kMode, false>), g, blk, 0, stream, a);
-    } else if constexpr (kMode != kModeFp8) {
+    } else if constexpr (kMode != kModeFp8 && kMode != kModeFp8V) {
         if (stats)
             hipLaunchKernelGGL((fwd_bf16_sp_kernel<64, kMode, true>), g, blk, 0, stream, a);
         else
@@ -974,9 +1147,9 @@ hipError_t launch_fwd_bf16_sp_paged(const void* q, const void* k_cache, const vo
     return launch_sp<kModePaged>(a, d, stream);
 }
 
-hipError_t launch_fwd_fp8qk_sp(const void* q, const void* k, const void* v, void* o, float* m_out,
-                               float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
-                               int causal, hipStream_t stream) {
+hipError_t launch_fwd_fp8qk_sp(const void* q, const void* k, const void* v, int v_fp8, void* o,
+                               float* m_out, float* l_out, int B, int Hq, int Hkv, int N, int d,
+                               float scale, int causal, hipStream_t stream) {
     FwdArgs a{};
     a.q = static_cast<const uint16_t*>(q);  // e4m3 bytes, addressed as such in the kernel
     a.k = static_cast<const uint16_t*>(k);
@@ -988,7 +1161,7 @@ hipError_t launch_fwd_fp8qk_sp(const void* q, const void* k, const void* v, void
     a.scale_log2 = scale * kLog2e;
     a.causal = causal;
     a.nqb = (N + kBr - 1) / kBr;
-    return launch_sp<kModeFp8>(a, d, stream);
+    return v_fp8 ? launch_sp<kModeFp8V>(a, d, stream) : launch_sp<kModeFp8>(a, d, stream);
 }
 
 hipError_t launch_fwd_bf16_sp_block_sparse(const void* q, const void* k, const void* v, void* o,

@@ -403,21 +403,21 @@ BLOCK_SPARSE = BlockSparseConfig(
 class Fp8Inputs:
     q: np.ndarray  # [B, Hq, N, d] float32, e4m3-exact
     k: np.ndarray  # [B, Hkv, N, d] float32, e4m3-exact
-    v: np.ndarray  # [B, Hkv, N, d] float32, bf16-exact
+    v: np.ndarray  # [B, Hkv, N, d] float32, bf16-exact (or e4m3-exact)
     scale: float
     causal: bool
 
 
-def fp8_fwd_inputs(B, Hq, Hkv, N, d, seed, causal=True, k_mult=1.0, scale=None):
-    """The forward inputs of `fwd_inputs` with Q and K rounded to e4m3 instead of bf16 (V stays
-    bf16): the same draws, a different rounding."""
+def fp8_fwd_inputs(B, Hq, Hkv, N, d, seed, causal=True, k_mult=1.0, scale=None, v_fp8=False):
+    """The forward inputs of `fwd_inputs` with Q and K rounded to e4m3 instead of bf16, and V to
+    e4m3 too when `v_fp8` (else bf16): the same draws, a different rounding."""
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, Hq, N, d), dtype=np.float32)
     k = rng.standard_normal((B, Hkv, N, d), dtype=np.float32)
     if k_mult != 1.0:
         k *= np.float32(k_mult)
     v = rng.standard_normal((B, Hkv, N, d), dtype=np.float32)
-    return Fp8Inputs(round_to_e4m3(q), round_to_e4m3(k), round_to_bf16(v),
+    return Fp8Inputs(round_to_e4m3(q), round_to_e4m3(k), round_to_e4m3(v) if v_fp8 else round_to_bf16(v),
                      1.0 / math.sqrt(d) if scale is None else scale, causal)
 
 

@@ -60,7 +60,8 @@ typedef enum {
 
 typedef enum {
     FA_F32 = 0,   /* IEEE binary32 */
-    FA_BF16 = 1   /* bfloat16 (round-to-nearest-even on output) */
+    FA_BF16 = 1,  /* bfloat16 (round-to-nearest-even on output) */
+    FA_E4M3 = 2   /* OCP fp8 e4m3: sign, 4 exponent bits (bias 7), 3 mantissa bits; max 448 */
 } fa_dtype;
 
 /*
@@ -154,23 +155,31 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int d, int page_size, int max_se
 int fa_decode_plan_splits(int B, int Hkv, int page_size, int max_seq_len);
 
 /*
- * fa_fwd_fp8 - tiled forward with fp8 queries and keys.
+ * fa_fwd_fp8 - tiled forward with fp8 queries and keys, and optionally fp8 values.
  *
- *   q : [B, Hq, N, d] OCP fp8 e4m3 (one byte per element: sign, 4 exponent bits with bias 7,
- *       3 mantissa bits)
- *   k : [B, Hkv, N, d] e4m3;  v : [B, Hkv, N, d] bf16;  o : [B, Hq, N, d] bf16
+ *   q : [B, Hq, N, d] OCP fp8 e4m3 (one byte per element)
+ *   k : [B, Hkv, N, d] e4m3
+ *   v : [B, Hkv, N, d] in v_dt: FA_BF16 or FA_E4M3
+ *   o : [B, Hq, N, d] bf16
  *   m_out, l_out : optional float32 [B, Hq, N] row statistics (NULL = not written)
  *
  * Computes what fa_fwd computes for the real values the codes stand for: the scores
  * scale * q.k are exact products of e4m3 values accumulated in float32, so a per-tensor
- * descale of q and k is passed by folding it into `scale` (finite, > 0). Softmax in float32,
- * P rounded to bf16 for P V, float32 accumulation, bf16 output. causal as in fa_fwd.
- * Supported: d = 128; Hq % Hkv == 0 (else FA_ERR_INVALID_ARGUMENT); N * d * 2 <= 2^30.
- * B, Hq or N equal to 0 is a valid empty call.
+ * descale of q and k is passed by folding it into `scale` (finite, > 0). Softmax in float32.
+ * v_dt = FA_BF16: P rounded to bf16 for P V on the bf16 matrix cores.
+ * v_dt = FA_E4M3: P rounded to e4m3 (round to nearest even, at most 256 against the row
+ * maximum, so never saturated) and P V on the fp8 matrix cores; l is the sum of the rounded
+ * weights, so O is a convex combination of V rows. The rounding of P is the one added error:
+ * each weight moves by at most 2^-4 of itself, or 2^-10 of the row's largest weight when
+ * smaller (e4m3 subnormals), which bounds |O - exact| elementwise by
+ * sum_j max(2^-4 w_j, 2^-10 max_i w_i) |v_j - O| / (1 - that sum over w) (w the exact softmax
+ * weights). A per-tensor descale of v multiplies O. float32 accumulation, bf16 output.
+ * causal as in fa_fwd. Supported: d = 128; Hq % Hkv == 0 (else FA_ERR_INVALID_ARGUMENT);
+ * N * d * 2 <= 2^30. B, Hq or N equal to 0 is a valid empty call.
  */
-fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* m_out,
-                     float* l_out, int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                     void* stream);
+fa_status fa_fwd_fp8(fa_dtype v_dt, const void* q, const void* k, const void* v, void* o,
+                     float* m_out, float* l_out, int B, int Hq, int Hkv, int N, int d, float scale,
+                     int causal, void* stream);
 
 /*
  * fa_bwd - gradients of fa_fwd's output with respect to q, k and v.

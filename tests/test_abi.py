@@ -64,6 +64,7 @@ def fwd(lib, dt=1, q=DEV, k=DEV, v=DEV, o=DEV, B=1, Hq=2, Hkv=1, N=8, d=64, scal
 
 @pytest.mark.parametrize("kwargs,code", [
     (dict(dt=7), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(dt=2), fa.FA_ERR_UNSUPPORTED),            # e4m3 goes through fa_fwd_fp8
     (dict(B=-1), fa.FA_ERR_INVALID_ARGUMENT),
     (dict(N=-5), fa.FA_ERR_INVALID_ARGUMENT),
     (dict(Hq=3, Hkv=2), fa.FA_ERR_INVALID_ARGUMENT),
@@ -202,11 +203,17 @@ def test_fwd_block_sparse_validation(kwargs, code):
     assert sparse(fa.load_library(), **kwargs) == code
 
 
-def fp8(lib, q=DEV, k=DEV, v=DEV, o=DEV, B=1, Hq=4, Hkv=2, N=300, d=128, scale=0.1, causal=1):
-    return lib.fa_fwd_fp8(q, k, v, o, None, None, B, Hq, Hkv, N, d, scale, causal, None)
+def fp8(lib, vdt=1, q=DEV, k=DEV, v=DEV, o=DEV, B=1, Hq=4, Hkv=2, N=300, d=128, scale=0.1, causal=1):
+    return lib.fa_fwd_fp8(vdt, q, k, v, o, None, None, B, Hq, Hkv, N, d, scale, causal, None)
 
 
 @pytest.mark.parametrize("kwargs,code", [
+    (dict(vdt=0), fa.FA_ERR_INVALID_ARGUMENT),      # float32 V: no such variant
+    (dict(vdt=9), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(vdt=2, d=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(vdt=2, N=(1 << 22) + 1), fa.FA_ERR_UNSUPPORTED),
+    (dict(vdt=2, k=NULL), fa.FA_ERR_INVALID_ARGUMENT),
+    (dict(vdt=2, N=0, q=NULL), fa.FA_OK),
     (dict(d=64), fa.FA_ERR_UNSUPPORTED),
     (dict(Hq=3, Hkv=2), fa.FA_ERR_INVALID_ARGUMENT),
     (dict(B=-1), fa.FA_ERR_INVALID_ARGUMENT),

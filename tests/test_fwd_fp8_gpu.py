@@ -4,6 +4,10 @@ Q and K are rounded to OCP e4m3 on the host (the oracle is fed those exact value
 same bf16 values); the scores are exact products of e4m3 values accumulated in float32, so
 the result carries the bf16 path's errors (P and O rounded to bf16) and is held to the bf16
 tolerance.
+
+With V in e4m3 too, the weights are rounded to e4m3 before P V: each output element is held
+to the bound that rounding admits (`e4m3_output_tolerance`), computed from the oracle's
+weights of that row.
 """
 
 import numpy as np
@@ -12,7 +16,7 @@ import pytest
 import oracle
 import exact_tiled_attention_24_amd as fa
 from exact_tiled_attention_24_amd import inputs as gen
-from helpers import assert_close, cuda_device, log_case, to_np, L_RTOL_BF16
+from helpers import assert_close, cuda_device, e4m3_output_tolerance, log_case, to_np, L_RTOL_BF16
 
 pytestmark = pytest.mark.gpu
 
@@ -22,12 +26,12 @@ def dev():
     return cuda_device()
 
 
-def run(x, dev, stats=True):
+def run(x, dev, stats=True, v_fp8=False):
     import torch
 
     q = gen.to_torch(x.q, "e4m3", dev)
     k = gen.to_torch(x.k, "e4m3", dev)
-    v = gen.to_torch(x.v, "bf16", dev)
+    v = gen.to_torch(x.v, "e4m3" if v_fp8 else "bf16", dev)
     res = fa.fa_fwd_fp8(q, k, v, scale=x.scale, causal=x.causal, return_stats=stats)
     torch.cuda.synchronize()
     return res
@@ -75,3 +79,101 @@ def test_fp8_forward_long_workload_sampled_rows(dev):
         assert_close(o2[b, h][rows], o_ref, "bf16", f"fp8 rows of (b={b}, h={h}) without statistics")
         np.testing.assert_allclose(m[b, h][rows], m_ref, atol=2e-3)
         np.testing.assert_allclose(l[b, h][rows], l_ref, rtol=L_RTOL_BF16)
+
+
+def row_weights(q, k, scale, causal, rows):
+    """The oracle's normalised weights of the given query rows of one head ([len(rows), Nk])."""
+    out = np.zeros((len(rows), k.shape[0]))
+    for r, i in enumerate(rows):
+        n = i + 1 if causal else k.shape[0]
+        out[r, :n] = oracle.attention_probs(q[i:i + 1], k[:n], scale, False)[0]
+    return out
+
+
+def e4m3_head_reference(q, k, v, scale, causal, rows):
+    """The oracle's O, m, l of the rows `rows` of one head with the e4m3-weight tolerances of O
+    (element by element) and of l (relative)."""
+    o_ref, m_ref, l_ref = oracle.attention_head(q, k, v, scale, causal, rows=rows)
+    w = row_weights(q, k, scale, causal, rows) if causal else oracle.attention_probs(q[rows], k, scale, False)
+    tol, l_tol = e4m3_output_tolerance(w, v, o_ref, k.shape[0])
+    return o_ref, m_ref, l_ref, tol, l_tol
+
+
+def assert_within(o, o_ref, tol, what):
+    err = np.abs(o - o_ref)
+    assert np.isfinite(o).all(), what
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} out of the bound; worst excess "
+                           f"{(err - tol).max():.3e}, max err {err.max():.3e}, max bound {tol.max():.3e}")
+
+
+def check_e4m3_head(outs, m, l, q, k, v, scale, causal, rows, what):
+    """Each output in `outs` (rows `rows` of one head), and m and l, against the oracle."""
+    o_ref, m_ref, l_ref, tol, l_tol = e4m3_head_reference(q, k, v, scale, causal, rows)
+    for i, o in enumerate(outs):
+        assert_within(o, o_ref, tol, f"{what} output {i}")
+    assert np.all(np.abs(l / l_ref - 1) <= l_tol), f"{what}: row sums"
+    np.testing.assert_allclose(m, m_ref, atol=2e-3, rtol=0)
+
+
+V8_CASES = [
+    # B, Hq, Hkv, N, causal, scale (None: 1/sqrt(d))
+    (1, 2, 2, 256, False, None),
+    (2, 4, 4, 300, True, None),
+    (1, 8, 2, 1000, True, None),
+    (2, 4, 1, 777, False, None),
+    (1, 4, 2, 2048, True, None),
+    (1, 4, 4, 64, True, None),
+    (1, 2, 1, 513, True, 1.0),      # sharply peaked rows: a wrong value row fails the bound
+    (2, 2, 2, 190, False, 0.5),
+]
+
+
+@pytest.mark.parametrize("case", V8_CASES,
+                         ids=lambda c: f"B{c[0]}-Hq{c[1]}-Hkv{c[2]}-N{c[3]}-{'c' if c[4] else 'n'}-s{c[5]}")
+def test_fp8_v_forward_within_e4m3_bound(case, dev):
+    B, Hq, Hkv, N, causal, scale = case
+    seed = 960 + V8_CASES.index(case)
+    log_case(f"fa_fwd_fp8 e4m3 V {case} seed={seed}")
+    x = gen.fp8_fwd_inputs(B, Hq, Hkv, N, 128, seed, causal=causal, scale=scale, v_fp8=True)
+    o, m, l = (to_np(t) for t in run(x, dev, v_fp8=True))
+    o2 = to_np(run(x, dev, stats=False, v_fp8=True))
+    G = Hq // Hkv
+    rows = np.arange(N)
+    for b in range(B):
+        for h in range(Hq):
+            q, k, v = x.q[b, h], x.k[b, h // G], x.v[b, h // G]
+            check_e4m3_head([o[b, h], o2[b, h]], m[b, h], l[b, h], q, k, v, x.scale, causal, rows,
+                            f"(b={b}, h={h})")
+
+
+def test_fp8_v_forward_moving_reference(dev):
+    """Scores that grow along the row: the first tile's keys are scaled down by 2^-6, so later
+    tiles pass the exponent reference by far more than 2^8 and it moves, several times in the
+    rows whose maxima keep rising."""
+    log_case("fa_fwd_fp8 e4m3 V, moving reference")
+    B, H, N = 1, 4, 1100
+    x = gen.fp8_fwd_inputs(B, H, H, N, 128, 975, causal=True, scale=1.0, v_fp8=True)
+    ramp = np.exp2(np.minimum(np.arange(N) // 64, 10) * 0.5 - 6.0).astype(np.float32)
+    k = gen.round_to_e4m3(x.k * ramp[None, None, :, None])
+    x = gen.Fp8Inputs(x.q, k, x.v, x.scale, x.causal)
+    o, m, l = (to_np(t) for t in run(x, dev, v_fp8=True))
+    for h in range(H):
+        check_e4m3_head([o[0, h]], m[0, h], l[0, h], x.q[0, h], x.k[0, h], x.v[0, h], x.scale, True,
+                        np.arange(N), f"h={h}")
+
+
+def test_fp8_v_long_workload_sampled_rows(dev):
+    """The long-prefill shape (B=2, H=32, N=8192, d=128, causal, K x2) with Q, K and V in
+    e4m3, in the launch the bench times and with statistics; sampled rows within the bound."""
+    log_case("fa_fwd_fp8 e4m3 V long workload")
+    x = gen.fp8_fwd_inputs(2, 32, 32, 8192, 128, 3, causal=True, k_mult=2.0, v_fp8=True)
+    o, m, l = (to_np(t) for t in run(x, dev, v_fp8=True))
+    o2 = to_np(run(x, dev, stats=False, v_fp8=True))
+    rng = np.random.default_rng(951)
+    for _ in range(6):
+        b, h = int(rng.integers(2)), int(rng.integers(32))
+        rows = np.unique(np.concatenate([[0, 63, 64, 8191], rng.integers(0, 8192, size=24)]))
+        q, k, v = x.q[b, h], x.k[b, h], x.v[b, h]
+        check_e4m3_head([o[b, h][rows], o2[b, h][rows]], m[b, h][rows], l[b, h][rows], q, k, v,
+                        x.scale, True, rows, f"(b={b}, h={h})")
