@@ -37,6 +37,7 @@ constexpr int kBlock = 128;    // keys (dK/dV) or queries (dQ) per workgroup: 32
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef const __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef const __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef const __attribute__((address_space(3))) unsigned char* lds_cptr;
 
 // Word 3 of a raw buffer descriptor (no format, no swizzle) for the loads into LDS.
@@ -88,6 +89,16 @@ struct TileDma {
             const int row = byte / kRow, p = (byte - row * kRow) / 16;
             off[j] = (unsigned)(row * kRow + 16 * (p ^ swz<D>(row)));
         }
+    }
+    // instruction j of this wave's share: rows from byte row0 of the buffer r into the tile at
+    // LDS address lds_tile
+    __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t r, unsigned row0, unsigned lds_tile,
+                                              int wave, int j) const {
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"(row0 + off[j]), "s"(r),
+                       "{m0}"(lds_tile + 1024u * (unsigned)(wave * kPerWave + j))
+                     : "memory");
     }
     // rows from byte row0 of the buffer r into the tile at LDS address lds_tile
     __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, unsigned row0, unsigned lds_tile,
@@ -148,17 +159,31 @@ __device__ __forceinline__ int xcd_position(int total) {
 }
 
 // ---- D_i = rowsum(dO * O) and L_i = (m_i + ln l_i) log2 e, 4 threads per row ----
+// Layout of L and D: per head, per 32-row chunk, the chunk's 32 L values then its 32 D values
+// (256 bytes), so that one 4-byte-per-lane load moves a chunk's L and D together. A head's
+// rows are padded to a multiple of 32; padding rows get L = +inf, D = 0 (P = 0 there).
+constexpr int kLdChunk = 32;
+__host__ __device__ constexpr long long ld_rows(int N) { return ((long long)N + kLdChunk - 1) / kLdChunk * kLdChunk; }
+__device__ __forceinline__ long long ld_index(long long head, int N, int row) {
+    return head * 2 * ld_rows(N) + (long long)(row / kLdChunk) * (2 * kLdChunk) + row % kLdChunk;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const uint16_t* __restrict__ o,
                                                             const uint16_t* __restrict__ dout,
                                                             const float* __restrict__ m,
                                                             const float* __restrict__ l,
-                                                            float* __restrict__ lse2,
-                                                            float* __restrict__ dsum, long long rows) {
-    const long long row = (long long)blockIdx.x * (kThreads / 4) + threadIdx.x / 4;
+                                                            float* __restrict__ ld, int N,
+                                                            long long heads) {
+    const long long np = ld_rows(N);
+    const long long prow = (long long)blockIdx.x * (kThreads / 4) + threadIdx.x / 4;  // padded row
+    const long long head = prow / np;
+    const int r = (int)(prow - head * np);
+    const bool real = head < heads && r < N;
+    const long long row = head * N + r;
     const int part = threadIdx.x & 3;
     float acc = 0.f;
-    if (row < rows) {
+    if (real) {
         const uint16_t* po = o + row * D + part * (D / 4);
         const uint16_t* pd = dout + row * D + part * (D / 4);
 #pragma unroll
@@ -174,10 +199,15 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const uint16_t* __re
     }
     acc += __shfl_xor(acc, 1);
     acc += __shfl_xor(acc, 2);
-    if (row < rows && part == 0) {
-        dsum[row] = acc;
-        const float lr = l[row];
-        lse2[row] = lr > 0.f ? (m[row] + logf(lr)) * kLog2e : INFINITY;
+    if (head < heads && part == 0) {
+        const long long at = ld_index(head, N, r);
+        float lv = INFINITY;
+        if (real) {
+            const float lr = l[row];
+            lv = lr > 0.f ? (m[row] + logf(lr)) * kLog2e : INFINITY;
+        }
+        ld[at] = lv;
+        ld[at + kLdChunk] = real ? acc : 0.f;
     }
 }
 
@@ -186,8 +216,7 @@ struct BwdArgs {
     const uint16_t* k;
     const uint16_t* v;
     const uint16_t* dout;
-    const float* lse2;  // [B, Hq, N]
-    const float* dsum;  // [B, Hq, N]
+    const float* ld;    // L and D of every query row, in 32-row chunks (see bwd_prep_kernel)
     uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;
@@ -196,25 +225,48 @@ struct BwdArgs {
     int causal;
 };
 
-// ---- dK, dV: workgroup = 128 keys of one KV head; wave = 32 keys ----
-// (two waves per SIMD: the register budget is 256 per lane, with a small spill)
+// ---- dK, dV: workgroup = 128 keys of one KV head; wave = 32 keys; one wave per SIMD ----
+// Each wave keeps its 32 keys' K and V rows in registers as B operands and walks 32-query
+// chunks of every query head of the KV group. The walk is software-pipelined: the step of
+// chunk c runs S = Q K^T and dP = dO V^T of chunk c + 1 (16 products, Q and dO rows read from
+// LDS), dV^T += dO^T P and dK^T += Q^T dS of chunk c - 1 (16 products, dO^T and Q^T through
+// transposing LDS reads, P and dS of that chunk as B operands), and between them the vector
+// work of chunk c (P = exp2(s scale log2e - L), dS = P (dP - D), both rounded to bf16 as the
+// B operands of the next step). With one wave per SIMD the wave has the whole register file:
+// the accumulators live in AGPRs and K, V and two chunks of scores fit beside them.
+// Chunks stream through a ring of kRing LDS stages (Q rows, dO rows, L and D), each loaded
+// straight from global memory kAhead chunks before its first use; one barrier per step. The
+// loop is unrolled over the ring, so every LDS address is a loop-invariant lane offset plus
+// an immediate; the walk is padded to a whole number of rounds with chunks whose loads lie
+// past every buffer and fill zeros (zero Q and dO rows contribute nothing), and a zero chunk
+// stands before the first one.
+// Query chunks are walked from the last one down: the workgroups of one head, started
+// together, read the same chunks at about the same time and find them in L2.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
-    constexpr int kSub = kSubKV;
-    using S = Stage<D, kSub>;
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+    using S = Stage<D, 1>;
+    using Dma = TileDma<D, 1>;
     constexpr int kChunk = S::kChunk;
-    // two buffers, each: Q chunk, dO chunk, L and D of its 32 queries
-    constexpr int kBuf = 2 * S::kTile + 2 * kChunk * 4;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kBuf];
+    constexpr int kT = S::kTile;                          // bytes of a chunk's Q (or dO) rows
+    constexpr int kRing = 6;
+    constexpr int kAhead = kRing - 2;                     // chunks c - 1 .. c + 1 are in use
+    constexpr int kOps = 2 * Dma::kPerWave + 1;           // loads per wave and chunk
+    constexpr int kA = 3;                                 // LDS operand reads kept in flight
+    constexpr int kQ0 = 0, kDo0 = kRing * kT, kLd0 = 2 * kRing * kT;  // regions of the ring
+    constexpr int kLdB = 2 * kChunk * 4;                  // L and D of a chunk's rows
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kRing * kT + kRing * kLdB];
 
     const int N = a.N, G = a.Hq / a.Hkv;
     const int pos = xcd_position(gridDim.x * gridDim.y);
     const int bk = pos / gridDim.x;  // b * Hkv + kvh
     const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
     const int kb0 = (pos - bk * gridDim.x) * kBlock;  // (causal: the first blocks see the most queries)
-    const int lane = threadIdx.x & 63, h = lane >> 5;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, h = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int key = kb0 + 32 * wave + (lane & 31);  // this lane's key (accumulator column)
+    const int kw0 = kb0 + 32 * wave;
 
     // K and V of the lane's key as B operands (K-dim = head dimension 16 kk + 8 h ..)
     const size_t kvoff = (size_t)bk * N * D;
@@ -231,118 +283,225 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) acc_dk[i] = acc_dv[i] = f32x16{};
 
-    // causal: queries before the block's first key see none of its keys. The chunks of all
-    // query heads of the KV group form one sequence it = 0 .. G * nch - 1.
+    // causal: queries before the block's first key see none of its keys. Chunk it = g nch + j
+    // of the walk is query head kvh G + g, rows qtop - 32 j ..; chunks from `total` on (and
+    // chunk -1) are zero chunks.
     const int q_first = a.causal ? (kb0 / kChunk) * kChunk : 0;
     const int nch = (N - q_first + kChunk - 1) / kChunk;
+    const int qtop = q_first + (nch - 1) * kChunk;
     const int total = G * nch;
-    float rl = INFINITY, rd = 0.f;
-    auto chunk_rows = [&](int it, size_t& qoff) {  // first query row; qoff = head's row base
-        const int g = it / nch;
-        qoff = ((size_t)b * a.Hq + kvh * G + g) * N;
-        return q_first + (it - g * nch) * kChunk;
-    };
-    // The Q and dO rows of a chunk go straight into LDS; L and D go through registers.
+    const int rounds = (total + kRing - 1) / kRing;
     constexpr int R = S::kRow;
-    TileDma<D, kSub> dma;
+    Dma dma;
     dma.init(wave, lane);
     const unsigned lds_base = (unsigned)(size_t)(lds_cptr)smem;
     const int head_bytes = N * D * 2;
-    auto load_chunk = [&](int it, int buf) {
-        size_t qoff;
-        const int qc0 = chunk_rows(it, qoff);
-        const __amdgpu_buffer_rsrc_t rsq =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + qoff * D), (short)0, head_bytes, kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t rsdo =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(a.dout + qoff * D), (short)0, head_bytes, kRsrcWord3);
-        const unsigned row0 = (unsigned)qc0 * R, tile = lds_base + (unsigned)(buf * kBuf);
-        dma.issue(rsq, row0, tile, wave);
-        dma.issue(rsdo, row0, tile + (unsigned)S::kTile, wave);
-        if (threadIdx.x < kChunk) {
-            const int qi = qc0 + threadIdx.x;
-            rl = qi < N ? a.lse2[qoff + qi] : INFINITY;
-            rd = qi < N ? a.dsum[qoff + qi] : 0.f;
+    const int ld_bytes = (int)(ld_rows(N) * 8);
+    // The loads of one chunk: this wave's share of its Q and dO rows (kPerWave instructions
+    // each) and the chunk's L and D (256 bytes, one dword per lane; every wave loads the same
+    // bytes, so each wave issues kOps loads per chunk and one vmcnt count serves all). A chunk
+    // past the walk (or before it) reads from past every range and fills zeros.
+    struct Loads {
+        __amdgpu_buffer_rsrc_t rq, rdo, rld;
+        unsigned row0, ldo, st;
+    };
+    // chunk cursors (wave-uniform): the next chunk to load and the chunk of the next step,
+    // each as (walk index, query head g, chunk j of that head)
+    int ld_it = 0, ld_g = 0, ld_j = 0, st_it = 0, st_g = 0, st_j = 0;
+    auto prepare = [&](int it, int g, int j, int st) -> Loads {
+        const bool real = it >= 0 && it < total;
+        const int gg = real ? g : 0;
+        const int qc0 = qtop - j * kChunk;
+        const size_t hq = (size_t)b * a.Hq + (size_t)kvh * G + gg;
+        Loads l;
+        l.rq = __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + hq * N * D), (short)0, head_bytes, kRsrcWord3);
+        l.rdo = __builtin_amdgcn_make_buffer_rsrc((void*)(a.dout + hq * N * D), (short)0, head_bytes, kRsrcWord3);
+        l.rld = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ld + hq * 2 * ld_rows(N)), (short)0, ld_bytes,
+                                                  kRsrcWord3);
+        l.row0 = real ? (unsigned)qc0 * R : 0x80000000u;
+        l.ldo = real ? (unsigned)qc0 * 8u : 0x80000000u;
+        l.st = (unsigned)st;
+        return l;
+    };
+    auto next_load = [&](int st) -> Loads {
+        const Loads l = prepare(ld_it, ld_g, ld_j, st);
+        ++ld_it;
+        if (++ld_j == nch) ld_j = 0, ++ld_g;
+        return l;
+    };
+    // load k (0 .. kOps - 1) of a chunk
+    auto issue_op = [&](const Loads& l, int k) {
+        constexpr int P = Dma::kPerWave;
+        if (k < P) {
+            dma.issue_one(l.rq, l.row0, lds_base + (unsigned)kQ0 + l.st * (unsigned)kT, wave, k);
+        } else if (k < 2 * P) {
+            dma.issue_one(l.rdo, l.row0, lds_base + (unsigned)kDo0 + l.st * (unsigned)kT, wave, k - P);
+        } else {
+            asm volatile("buffer_load_dword %0, %1, 0 offen lds"
+                         :
+                         : "v"(l.ldo + 4u * (unsigned)lane), "s"(l.rld),
+                           "{m0}"(lds_base + (unsigned)kLd0 + l.st * (unsigned)kLdB)
+                         : "memory");
         }
     };
-    // L and D into LDS; then this wave's loads into LDS are waited for (vmcnt counts the
-    // wave's vector loads in issue order) before the barrier that publishes the chunk
-    auto store_chunk = [&](int buf) {
-        unsigned char* base = smem + buf * kBuf;
-        if (threadIdx.x < kChunk) {
-            reinterpret_cast<float*>(base + 2 * S::kTile)[threadIdx.x] = rl;
-            reinterpret_cast<float*>(base + 2 * S::kTile)[kChunk + threadIdx.x] = rd;
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    };
-    if (total > 0) {
-        load_chunk(0, 0);
-        store_chunk(0);
-    }
-    __syncthreads();
-    for (int it = 0; it < total; ++it) {
-        // the other buffer was last read before the previous barrier
-        if (it + 1 < total) load_chunk(it + 1, (it + 1) & 1);  // in flight during this chunk's products
-        size_t qoff_chunk;  // (the head's row base; the chunk's rows are already staged)
-        const int qc0 = chunk_rows(it, qoff_chunk);
-        const unsigned char* base = smem + (it & 1) * kBuf;
-        lds_cptr const lq = (lds_cptr)base;
-        lds_cptr const ldo = (lds_cptr)(base + S::kTile);
-        const float* s_l = reinterpret_cast<const float*>(base + 2 * S::kTile);
-        const float* s_d = s_l + kChunk;
-
-        // S = Q K^T and dP = dO V^T for each 32-query sub-chunk x the wave's 32 keys; the
-        // sub-chunks are independent until the accumulations, so their matrix and vector work
-        // can interleave
-        f32x16 sc[kSub], dp[kSub];
+    auto issue_all = [&](const Loads& l) {
 #pragma unroll
-        for (int u = 0; u < kSub; ++u) {
-            sc[u] = f32x16{};
-            dp[u] = f32x16{};
-            const lds_cptr tq = lq + 32 * u * S::kRow, tdo = ldo + 32 * u * S::kRow;
+        for (int k = 0; k < kOps; ++k) issue_op(l, k);
+    };
+    const lds_cptr lds = (lds_cptr)smem;
+
+    // products of slot sl of a step: even slots S / dP of the next chunk (S when sl % 4 == 0,
+    // head dims 16 (sl / 4) ..), odd slots dV / dK of the previous chunk (query group t,
+    // head-dim block db)
+    constexpr int kSlots = 2 * (D / 8);  // 16 next-chunk products + 16 previous-chunk ones (D = 128)
+    constexpr int kPrev = D / 8;         // previous-chunk products: 2 (t) x D / 32 (db) x 2 (dV, dK)
+    static_assert(kSlots == 2 * kPrev, "one next-chunk and one previous-chunk product per slot pair");
+    constexpr int kSpread = kSlots / 16; // slots per score of the vector work
+
+    // One step: chunk it's vector work (its scores sc_c, dp_c -> operands pb_c, sb_c), the next
+    // chunk's scores into (sc_n, dp_n) and the previous chunk's gradient products with pb_p,
+    // sb_p; the loads `ld` of a later chunk go out one at a time between the products.
+    // st_c: chunk it's ring stage.
+    auto step = [&](auto st_c, f32x16& sc_c, f32x16& dp_c, f32x16& sc_n, f32x16& dp_n,
+                    const bf16x8 (&pb_p)[2], const bf16x8 (&sb_p)[2], bf16x8 (&pb_c)[2],
+                    bf16x8 (&sb_c)[2], const Loads& ld) {
+        constexpr int Pc = decltype(st_c)::value;
+        constexpr int Pn = (Pc + 1) % kRing, Pp = (Pc + kRing - 1) % kRing;
+        const lds_cptr tn = lds + kQ0 + Pn * kT, tnd = lds + kDo0 + Pn * kT;  // next chunk's rows
+        const lds_cptr tp = lds + kQ0 + Pp * kT, tpd = lds + kDo0 + Pp * kT;  // previous chunk's
+        const lds_cptr s_l = lds + kLd0 + Pc * kLdB, s_d = s_l + 4 * kChunk;   // L, D
+        // keys past the query get the score -inf where the chunk reaches above the wave's keys
+        // (causal; a wave-uniform branch, rare: zero chunks and most chunks need none)
+        const int qc0 = qtop - st_j * kChunk;
+        if (a.causal && st_it < total && qc0 < kw0 + 31) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sc_c[r] = key <= qc0 + acc_row(r, h) ? sc_c[r] : -INFINITY;
+        }
+        ++st_it;
+        if (++st_j == nch) st_j = 0, ++st_g;
+        // L and D of register r's row acc_row(r, h): element r % 4 of the 16-byte run at row
+        // 16 (r / 8) + 8 h + 4 ((r / 4) % 2)
+        auto ld4 = [&](lds_cptr base, int r) -> f32x4 {
+            const int row = 16 * (r >> 3) + 8 * h + 4 * ((r >> 2) & 1);
+            return *reinterpret_cast<const lds_f32x4*>(base + 4 * row);
+        };
+        auto operand = [&](int sl) -> bf16x8 {
+            const int i = sl >> 1;
+            if ((sl & 1) == 0) return rows_frag<D>((i & 1) ? tnd : tn, lane, i >> 1);
+            const int t = i / (kPrev / 2), db = (i >> 1) % (D / 32);
+            return trans_frag<D>((i & 1) ? tp : tpd, lane, t, db);
+        };
+        bf16x8 op[kSlots];
+        f32x4 lq = ld4(s_l, 0), dq4 = ld4(s_d, 0);  // L, D of registers 0 .. 3
+        float p0 = 0.f, d0 = 0.f;                    // the first score of a pair
+        sc_n = f32x16{};
+        dp_n = f32x16{};
+#pragma unroll
+        for (int sl = 0; sl < kA; ++sl) op[sl] = operand(sl);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int sl = 0; sl < kSlots; ++sl) {
+            if (sl + kA < kSlots) op[sl + kA] = operand(sl + kA);
+            const int i = sl >> 1;
+            if ((sl & 1) == 0) {
+                if ((i & 1) == 0) sc_n = mfma_32x32x16(op[sl], kf[i >> 1], sc_n);
+                else dp_n = mfma_32x32x16(op[sl], vf[i >> 1], dp_n);
+            } else {
+                const int t = i / (kPrev / 2), db = (i >> 1) % (D / 32);
+                if ((i & 1) == 0) acc_dv[db] = mfma_32x32x16(op[sl], pb_p[t], acc_dv[db]);
+                else acc_dk[db] = mfma_32x32x16(op[sl], sb_p[t], acc_dk[db]);
+            }
+            // load k in slot 4 k + 2
+            if ((sl & 3) == 2 && (sl >> 2) < kOps) issue_op(ld, sl >> 2);
+            // vector work: score r (its probability and dS) in the last slot of each group of
+            // kSpread, pairs packed to bf16 as soon as both are done; L and D of the next four
+            // registers are read a score ahead of their use
+            if (sl % kSpread == kSpread - 1) {
+                const int r = sl / kSpread;
+                // (the empty asm statements keep this work in its slot: without them the
+                // compiler gathers the whole chunk's vector work ahead of the products)
+                float sr = sc_c[r], dpr = dp_c[r];
+                asm volatile("" : "+v"(sr), "+v"(dpr));
+                float pr = exp2_hw(__builtin_fmaf(sr, a.scale_log2, -lq[r & 3]));
+                float dr = pr * (dpr - dq4[r & 3]);
+                asm volatile("" : "+v"(pr), "+v"(dr));
+                if (r & 1) {
+                    const int w = (r >> 1) & 3, t = r >> 3;
+                    u32x4 pw = __builtin_bit_cast(u32x4, pb_c[t]);
+                    u32x4 sw = __builtin_bit_cast(u32x4, sb_c[t]);
+                    pw[w] = pack_bf16x2(p0, pr);
+                    sw[w] = pack_bf16x2(d0, dr);
+                    pb_c[t] = __builtin_bit_cast(bf16x8, pw);
+                    sb_c[t] = __builtin_bit_cast(bf16x8, sw);
+                } else {
+                    p0 = pr;
+                    d0 = dr;
+                }
+                if ((r & 3) == 3 && r + 1 < 16) {
+                    lq = ld4(s_l, r + 1);
+                    dq4 = ld4(s_d, r + 1);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    static_assert(4 * (kOps - 1) + 2 < kSlots, "every load of a chunk has its slot");
+    // before a step: wait for the next chunk (this wave's loads; two chunks stay in flight),
+    // barrier, then the loads of the chunk kAhead ahead into the stage chunk it - 2 used
+    auto advance = [&](int st_load) -> Loads {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kOps) : "memory");
+        __syncthreads();
+        return next_load(st_load);
+    };
+
+    if (total > 0) {
+        // prologue: the zero chunk -1 into stage kRing - 1, chunks 0 .. kAhead - 1 into stages
+        // 0 .. kAhead - 1; wait for chunks -1 and 0; chunk 0's scores
+        issue_all(prepare(-1, 0, 0, kRing - 1));
+#pragma unroll
+        for (int c = 0; c < kAhead; ++c) issue_all(next_load(c));
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - 1) * kOps) : "memory");
+        __syncthreads();
+        f32x16 sa{}, da{}, sb2{}, db2{};
+        const bf16x8 zero8 = {};
+        bf16x8 pa[2] = {zero8, zero8}, qa[2] = {zero8, zero8};   // P, dS of even chunks
+        bf16x8 pb[2] = {zero8, zero8}, qb[2] = {zero8, zero8};   // of odd chunks (and chunk -1)
+        {
+            const lds_cptr tq = lds + kQ0, tdo = lds + kDo0;
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
-                sc[u] = mfma_32x32x16(rows_frag<D>(tq, lane, kk), kf[kk], sc[u]);
-                dp[u] = mfma_32x32x16(rows_frag<D>(tdo, lane, kk), vf[kk], dp[u]);
+                sa = mfma_32x32x16(rows_frag<D>(tq, lane, kk), kf[kk], sa);
+                da = mfma_32x32x16(rows_frag<D>(tdo, lane, kk), vf[kk], da);
             }
         }
-        // No score of this chunk is masked when the wave's 32 keys and the chunk's queries all
-        // lie inside the sequence and (causal) the chunk's first query follows the wave's last
-        // key; then the probabilities take no predicate (a wave-uniform branch)
-        const int kw0 = kb0 + 32 * wave;
-        const bool plain = kw0 + 32 <= N && qc0 + kChunk <= N && (!a.causal || qc0 >= kw0 + 31);
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I3 = std::integral_constant<int, 3>;
+        using I4 = std::integral_constant<int, 4>;
+        using I5 = std::integral_constant<int, 5>;
+        // rounds of kRing steps; step it's loads go to stage (it + kAhead) % kRing
+        for (int rd = 0; rd < rounds; ++rd) {
+            step(I0{}, sa, da, sb2, db2, pb, qb, pa, qa, advance(4));
+            step(I1{}, sb2, db2, sa, da, pa, qa, pb, qb, advance(5));
+            step(I2{}, sa, da, sb2, db2, pb, qb, pa, qa, advance(0));
+            step(I3{}, sb2, db2, sa, da, pa, qa, pb, qb, advance(1));
+            step(I4{}, sa, da, sb2, db2, pb, qb, pa, qa, advance(2));
+            step(I5{}, sb2, db2, sa, da, pa, qa, pb, qb, advance(3));
+        }
+        // dV, dK of the last chunk of the walk (an odd chunk, in stage kRing - 1)
+        {
+            const lds_cptr tq = lds + kQ0 + (kRing - 1) * kT, tdo = lds + kDo0 + (kRing - 1) * kT;
 #pragma unroll
-        for (int u = 0; u < kSub; ++u) {
-            float p[16], ds[16];
-            if (plain) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    p[r] = exp2_hw(__builtin_fmaf(sc[u][r], a.scale_log2, -s_l[32 * u + acc_row(r, h)]));
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int qr = 32 * u + acc_row(r, h);
-                    const int qi = qc0 + qr;
-                    const bool ok = key < N && qi < N && (!a.causal || key <= qi);
-                    const float e = exp2_hw(__builtin_fmaf(sc[u][r], a.scale_log2, -s_l[qr]));
-                    p[r] = ok ? e : 0.f;
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ds[r] = p[r] * (dp[u][r] - s_d[32 * u + acc_row(r, h)]);
-            // dV^T += dO^T P and dK^T += Q^T dS (K-dim = the sub-chunk's queries)
-            const lds_cptr tq = lq + 32 * u * S::kRow, tdo = ldo + 32 * u * S::kRow;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const bf16x8 pb = acc_operand(p, t), sb = acc_operand(ds, t);
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    acc_dv[db] = mfma_32x32x16(trans_frag<D>(tdo, lane, t, db), pb, acc_dv[db]);
-                    acc_dk[db] = mfma_32x32x16(trans_frag<D>(tq, lane, t, db), sb, acc_dk[db]);
+                    acc_dv[db] = mfma_32x32x16(trans_frag<D>(tdo, lane, t, db), pb[t], acc_dv[db]);
+                    acc_dk[db] = mfma_32x32x16(trans_frag<D>(tq, lane, t, db), qb[t], acc_dk[db]);
                 }
-            }
         }
-        if (it + 1 < total) store_chunk((it + 1) & 1);
-        __syncthreads();
+        // no load may still be writing LDS when the workgroup ends
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     // accumulator register r of block db: head dimension 32 db + 8 (r / 4) + 4 h + r % 4
     if (key < N) {
@@ -394,8 +553,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
             dof[kk] = *reinterpret_cast<const bf16x8*>(a.dout + (qoff + qr) * D + 16 * kk + 8 * h);
         }
     }
-    const float lse = query < N ? a.lse2[qoff + query] : INFINITY;
-    const float dsum = query < N ? a.dsum[qoff + query] : 0.f;
+    const long long ldi = ld_index((long long)bh, N, min_(query, N - 1));
+    const float lse = query < N ? a.ld[ldi] : INFINITY;
+    const float dsum = query < N ? a.ld[ldi + kLdChunk] : 0.f;
     f32x16 acc_dq[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) acc_dq[i] = f32x16{};
@@ -493,10 +653,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a, const uint16_t* o, const float* m, const float* l,
-                        float* lse2, float* dsum, int B, hipStream_t stream) {
-    const long long rows = (long long)B * a.Hq * a.N;
+                        float* ld, int B, hipStream_t stream) {
+    const long long heads = (long long)B * a.Hq;
+    const long long rows = heads * ld_rows(a.N);  // padded rows
     hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + 63) / 64)), dim3(kThreads), 0,
-                       stream, o, a.dout, m, l, lse2, dsum, rows);
+                       stream, o, a.dout, m, l, ld, a.N, heads);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned blocks = (unsigned)((a.N + kBlock - 1) / kBlock);
@@ -514,14 +675,13 @@ hipError_t launch_bwd_d(const BwdArgs& a, const uint16_t* o, const float* m, con
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* m, const float* l, void* dq, void* dk,
                            void* dv, int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                           float* lse2, float* dsum, hipStream_t stream) {
+                           float* ld, hipStream_t stream) {
     BwdArgs a{};
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
     a.dout = static_cast<const uint16_t*>(dout);
-    a.lse2 = lse2;
-    a.dsum = dsum;
+    a.ld = ld;
     a.dq = static_cast<uint16_t*>(dq);
     a.dk = static_cast<uint16_t*>(dk);
     a.dv = static_cast<uint16_t*>(dv);
@@ -530,8 +690,8 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
     a.scale_log2 = scale * kLog2e;
     a.causal = causal;
     const uint16_t* op = static_cast<const uint16_t*>(o);
-    return d == 128 ? launch_bwd_d<128>(a, op, m, l, lse2, dsum, B, stream)
-                    : launch_bwd_d<64>(a, op, m, l, lse2, dsum, B, stream);
+    return d == 128 ? launch_bwd_d<128>(a, op, m, l, ld, B, stream)
+                    : launch_bwd_d<64>(a, op, m, l, ld, B, stream);
 }
 
 }  // namespace fa

@@ -92,9 +92,11 @@ struct DecodeArgs {
 };
 
 // Counts one arrival on a completion word and reports whether it was the n-th of this call.
-// Vector (global) atomics at device scope, relaxed: the caller orders the partials around it
-// with explicit fences. The loop ends because every failed exchange means another
-// workgroup's arrival succeeded.
+// Vector (global) atomics at device scope, relaxed. The caller orders the partials around it
+// without fences: every wave waits for its partial stores to complete (s_waitcnt vmcnt(0))
+// before the barrier behind which one thread arrives, and the last arriver's loads of the
+// other partials are issued only after its exchange has returned. The loop ends because every
+// failed exchange means another workgroup's arrival succeeded.
 __device__ bool arrive(unsigned long long* word, unsigned long long tag, int n) {
     unsigned long long old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (;;) {

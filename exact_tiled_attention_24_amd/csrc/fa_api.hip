@@ -241,7 +241,7 @@ fa_status fa_fwd_fp8(fa_dtype v_dt, const void* q, const void* k, const void* v,
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int N) {
     if (B < 0 || Hq < 0 || N < 0) return 0;
-    return 2 * (size_t)B * (size_t)Hq * (size_t)N * sizeof(float);
+    return fa::bwd_ld_bytes(B, Hq, N);
 }
 
 fa_status fa_bwd(fa_dtype dt, const void* q, const void* k, const void* v, const void* o,
@@ -264,10 +264,8 @@ fa_status fa_bwd(fa_dtype dt, const void* q, const void* k, const void* v, const
     if ((long long)B * Hq >= 65536 || ((long long)N + 127) / 128 >= (1LL << 31))
         return FA_ERR_UNSUPPORTED;  // grid y holds (batch, head)
     if (workspace_bytes < fa_bwd_workspace_bytes(B, Hq, N)) return FA_ERR_WORKSPACE_TOO_SMALL;
-    float* lse2 = static_cast<float*>(workspace);
-    float* dsum = lse2 + (size_t)B * Hq * N;
     const hipError_t e = fa::launch_bwd_bf16(q, k, v, o, dout, m, l, dq, dk, dv, B, Hq, Hkv, N, d,
-                                             scale, causal ? 1 : 0, lse2, dsum,
+                                             scale, causal ? 1 : 0, static_cast<float*>(workspace),
                                              static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

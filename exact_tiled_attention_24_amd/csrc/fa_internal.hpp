@@ -38,12 +38,17 @@ hipError_t launch_fwd_bf16_sp_block_sparse(const void* q, const void* k, const v
                                            int Hkv, int N, int d, float scale, int causal,
                                            hipStream_t stream);
 
-// Backward by recomputation: D and the log2 normaliser into lse2 / dsum ([B, Hq, N] float32
-// each, caller workspace), then dK/dV and dQ (bf16 outputs, float32 accumulation).
+// Backward by recomputation: D and the log2 normaliser of every query row into `ld` (caller
+// workspace of bwd_ld_bytes(B, Hq, N) bytes), then dK/dV and dQ (bf16 outputs, float32
+// accumulation).
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const void* dout, const float* m, const float* l, void* dq, void* dk,
                            void* dv, int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                           float* lse2, float* dsum, hipStream_t stream);
+                           float* ld, hipStream_t stream);
+// Bytes of that workspace: two float32 values per query row, a head's rows padded to 32.
+inline size_t bwd_ld_bytes(int B, int Hq, int N) {
+    return (size_t)B * (size_t)Hq * (((size_t)N + 31) / 32 * 32) * 2 * sizeof(float);
+}
 
 // Forward with fp8 (OCP e4m3) Q and K: S^T on the fp8 matrix cores. v_fp8 == 0: V bf16, P
 // rounded to bf16, P V as in the bf16 kernel; v_fp8 != 0: V e4m3, P rounded to e4m3, P V on the

@@ -167,13 +167,16 @@ int fa_decode_plan_splits(int B, int Hkv, int page_size, int max_seq_len);
  * scale * q.k are exact products of e4m3 values accumulated in float32, so a per-tensor
  * descale of q and k is passed by folding it into `scale` (finite, > 0). Softmax in float32.
  * v_dt = FA_BF16: P rounded to bf16 for P V on the bf16 matrix cores.
- * v_dt = FA_E4M3: P rounded to e4m3 (round to nearest even, at most 256 against the row
- * maximum, so never saturated) and P V on the fp8 matrix cores; l is the sum of the rounded
- * weights, so O is a convex combination of V rows. The rounding of P is the one added error:
- * each weight moves by at most 2^-4 of itself, or 2^-10 of the row's largest weight when
- * smaller (e4m3 subnormals), which bounds |O - exact| elementwise by
- * sum_j max(2^-4 w_j, 2^-10 max_i w_i) |v_j - O| / (1 - that sum over w) (w the exact softmax
- * weights). A per-tensor descale of v multiplies O. float32 accumulation, bf16 output.
+ * v_dt = FA_E4M3: P rounded to e4m3 (round to nearest even) and P V on the fp8 matrix cores;
+ * l is the sum of the rounded weights, so O is a convex combination of V rows. The exponent
+ * reference r of a row moves when a tile's maximum passes it by more than 2^8, and then to 2^4
+ * below that maximum: a weight is at most 256 r (never saturated) and r is at most 2^-4 of
+ * the row's largest weight. The rounding of P is the one added error: each weight w_j moves by
+ * at most b_j = min(w_j, max(2^-4 w_j, 2^-14 max_i w_i)) (3 mantissa bits; e4m3 subnormals
+ * step by 2^-9 r), which bounds |O - exact| elementwise by
+ * sum_j b_j |v_j - O| / (1 - sum_j b_j) (w the exact softmax weights, normalised) and
+ * |l / exact - 1| by sum_j b_j. A per-tensor descale of v multiplies O. float32 accumulation,
+ * bf16 output.
  * causal as in fa_fwd. Supported: d = 128; Hq % Hkv == 0 (else FA_ERR_INVALID_ARGUMENT);
  * N * d * 2 <= 2^30. B, Hq or N equal to 0 is a valid empty call.
  */
@@ -202,7 +205,8 @@ fa_status fa_bwd(fa_dtype dt, const void* q, const void* k, const void* v, const
                  int B, int Hq, int Hkv, int N, int d, float scale, int causal, void* workspace,
                  size_t workspace_bytes, void* stream);
 
-/* Workspace bytes fa_bwd needs (two float32 values per query row; 0 for negative sizes). */
+/* Workspace bytes fa_bwd needs (two float32 values per query row, a head's rows padded to a
+ * multiple of 32; 0 for negative sizes). */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int N);
 
 /* Block sizes of fa_fwd_block_sparse's mask: query rows per block, keys per block. */

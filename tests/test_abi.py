@@ -256,7 +256,8 @@ def test_bwd_validation(kwargs, code):
 
 
 def test_bwd_workspace_bytes():
-    assert fa.fa_bwd_workspace_bytes(2, 8, 1000) == 2 * 2 * 8 * 1000 * 4
+    assert fa.fa_bwd_workspace_bytes(2, 8, 1000) == 2 * 2 * 8 * 1024 * 4  # rows padded to 32
+    assert fa.fa_bwd_workspace_bytes(1, 1, 32) == 2 * 32 * 4
     assert fa.fa_bwd_workspace_bytes(-1, 8, 10) == 0
 
 

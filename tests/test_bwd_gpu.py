@@ -42,6 +42,9 @@ CASES = [
     (2, 4, 4, 512, 128, False),
     (1, 4, 1, 1000, 64, True),     # one KV head for four query heads
     (1, 8, 2, 2048, 128, True),
+    (1, 2, 1, 20, 64, True),       # a single, partial query chunk
+    (1, 1, 1, 33, 128, False),     # one row past a whole chunk
+    (1, 3, 3, 700, 128, True),     # a walk that is not a whole number of ring rounds
 ]
 
 
