@@ -446,10 +446,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
     };
     static_assert(4 * (kOps - 1) + 2 < kSlots, "every load of a chunk has its slot");
-    // before a step: wait for the next chunk (this wave's loads; two chunks stay in flight),
-    // barrier, then the loads of the chunk kAhead ahead into the stage chunk it - 2 used
+    // before a step: wait for the next chunk (this wave's loads; the kAhead - 2 chunks after it
+    // stay in flight), barrier, then the loads of the chunk kAhead ahead into the stage chunk
+    // it - 2 used
     auto advance = [&](int st_load) -> Loads {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kOps) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - 2) * kOps) : "memory");
         __syncthreads();
         return next_load(st_load);
     };
@@ -523,13 +524,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---- dQ: workgroup = 128 queries of one query head; wave = 32 queries ----
+// Each wave keeps its 32 queries' Q and dO rows in registers as B operands and walks 32-key
+// chunks of K and V, software-pipelined like the dK/dV kernel: the step of chunk c runs
+// S^T = K Q^T and dP^T = V dO^T of chunk c + 1 (16 products, K and V rows from LDS), dQ^T +=
+// K^T dS^T of chunk c - 1 (8 products, K^T through transposing LDS reads) and the vector work
+// of chunk c. K and V chunks stream through a ring of kRing LDS stages (K rows, then V rows),
+// loaded kAhead chunks ahead, one load per few products; the loop is unrolled over the ring
+// and the walk padded to whole rounds with zero chunks (zero K rows add nothing to dQ).
+// Two waves per SIMD.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
-    constexpr int kSub = kSubQ;
-    using S = Stage<D, kSub>;
+    using S = Stage<D, 1>;
+    using Dma = TileDma<D, 1>;
     constexpr int kChunk = S::kChunk;
-    // two buffers, each: K chunk, V chunk
-    __shared__ __attribute__((aligned(16))) unsigned char smem[4 * S::kTile];
+    constexpr int kT = S::kTile;            // bytes of a chunk's K (or V) rows
+    constexpr int kRing = 4;
+    constexpr int kAhead = kRing - 2;       // chunks c - 1 and c + 1 are in use during step c
+    constexpr int kOps = 2 * Dma::kPerWave; // loads per wave and chunk
+    constexpr int kA = 3;                   // LDS operand reads kept in flight
+    constexpr int kStB = 2 * kT;            // a stage: K rows, V rows
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kRing * kStB];
 
     const int N = a.N, G = a.Hq / a.Hkv;
     const int pos = xcd_position(gridDim.x * gridDim.y);
@@ -538,9 +552,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     const int kvh = hq / G;
     // last query block first: under the causal mask it sees the most keys
     const int qb0 = (gridDim.x - 1 - (pos - bh * gridDim.x)) * kBlock;
-    const int lane = threadIdx.x & 63, h = lane >> 5;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, h = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int query = qb0 + 32 * wave + (lane & 31);  // this lane's query (accumulator column)
+    const int qw0 = qb0 + 32 * wave;
 
     const size_t qoff = (size_t)bh * N;
     const size_t kvoff = ((size_t)b * a.Hkv + kvh) * N * D;
@@ -562,8 +579,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
     const int k_end = a.causal ? min_(N, qb0 + kBlock) : N;  // keys past the block's last query
     const int total = (k_end + kChunk - 1) / kChunk;
-    // K and V chunks go straight into LDS (two buffers, each: K chunk, V chunk)
-    TileDma<D, kSub> dma;
+    const int rounds = (total + kRing - 1) / kRing;
+    Dma dma;
     dma.init(wave, lane);
     const unsigned lds_base = (unsigned)(size_t)(lds_cptr)smem;
     const int head_bytes = N * D * 2;
@@ -571,71 +588,141 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + kvoff), (short)0, head_bytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rsv =
         __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + kvoff), (short)0, head_bytes, kRsrcWord3);
-    auto load_chunk = [&](int it) {
-        const unsigned row0 = (unsigned)(it * kChunk * S::kRow);
-        const unsigned tile = lds_base + (unsigned)(2 * (it & 1) * S::kTile);
-        dma.issue(rsk, row0, tile, wave);
-        dma.issue(rsv, row0, tile + (unsigned)S::kTile, wave);
+    // load k (0 .. kOps - 1) of chunk it into stage st (a chunk past the walk, or before it,
+    // reads from past the range and fills zeros)
+    auto issue_op = [&](int it, int st, int k) {
+        constexpr int P = Dma::kPerWave;
+        const unsigned row0 = (it >= 0 && it < total) ? (unsigned)(it * kChunk * S::kRow) : 0x80000000u;
+        const unsigned tile = lds_base + (unsigned)(st * kStB);
+        if (k < P) dma.issue_one(rsk, row0, tile, wave, k);
+        else dma.issue_one(rsv, row0, tile + (unsigned)kT, wave, k - P);
     };
-    auto store_chunk = [&](int) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-    if (total > 0) {
-        load_chunk(0);
-        store_chunk(0);
-    }
-    __syncthreads();
-    for (int it = 0; it < total; ++it) {
-        // the other buffer was last read before the previous barrier
-        if (it + 1 < total) load_chunk(it + 1);  // in flight during this chunk's products
-        const int kc0 = it * kChunk;
-        lds_cptr const lk = (lds_cptr)(smem + 2 * (it & 1) * S::kTile);
-        lds_cptr const lv = (lds_cptr)(smem + (2 * (it & 1) + 1) * S::kTile);
+    const lds_cptr lds = (lds_cptr)smem;
 
-        // S^T = K Q^T and dP^T = V dO^T: each 32-key sub-chunk x the wave's 32 queries
-        f32x16 sc[kSub], dp[kSub];
+    // slots of a step: groups of three, (S^T, dP^T) of the next chunk for head dims 16 k ..,
+    // then dQ^T product k of the previous chunk (key group t = k / (D / 32), head-dim block db)
+    constexpr int kNext = D / 16;                // S^T / dP^T pairs
+    constexpr int kDq = 2 * (D / 32);            // dQ^T products: 2 (t) x D / 32 (db)
+    static_assert(kNext == kDq, "one dQ product per (S, dP) pair");
+    constexpr int kSlots = 3 * kNext;
+    // vector work of score r in slot slot_of(r): spread over the step
+    auto slot_of = [](int r) { return (r * kSlots) / 16; };
+    static_assert((15 * kSlots) / 16 < kSlots, "every score has its slot");
+
+    // One step: chunk it's vector work (scores sc_c, dp_c -> dS operands sb_c), the next
+    // chunk's scores into (sc_n, dp_n), the previous chunk's dQ products with sb_p; loads of
+    // chunk it + kAhead into stage st_load. st_c: chunk it's stage.
+    auto step = [&](int it, auto st_c, f32x16& sc_c, f32x16& dp_c, f32x16& sc_n, f32x16& dp_n,
+                    const bf16x8 (&sb_p)[2], bf16x8 (&sb_c)[2], int st_load) {
+        constexpr int Pc = decltype(st_c)::value;
+        constexpr int Pn = (Pc + 1) % kRing, Pp = (Pc + kRing - 1) % kRing;
+        const lds_cptr tnk = lds + Pn * kStB, tnv = tnk + kT;  // next chunk's K, V rows
+        const lds_cptr tpk = lds + Pp * kStB;                  // previous chunk's K rows
+        // keys past the query get the score -inf where the chunk reaches past the wave's first
+        // query (causal; a wave-uniform branch)
+        const int kc0 = it * kChunk;
+        if (a.causal && it < total && kc0 + kChunk - 1 > qw0) {
 #pragma unroll
-        for (int u = 0; u < kSub; ++u) {
-            sc[u] = f32x16{};
-            dp[u] = f32x16{};
-            const lds_cptr tk = lk + 32 * u * S::kRow, tv = lv + 32 * u * S::kRow;
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                sc[u] = mfma_32x32x16(rows_frag<D>(tk, lane, kk), qf[kk], sc[u]);
-                dp[u] = mfma_32x32x16(rows_frag<D>(tv, lane, kk), dof[kk], dp[u]);
-            }
+            for (int r = 0; r < 16; ++r) sc_c[r] = kc0 + acc_row(r, h) <= query ? sc_c[r] : -INFINITY;
         }
-        // No score of this chunk is masked when the wave's 32 queries and the chunk's keys all
-        // lie inside the sequence and (causal) the chunk's last key precedes the wave's first
-        // query; then the probabilities take no predicate (a wave-uniform branch)
-        const int qw0 = qb0 + 32 * wave;
-        const bool plain = qw0 + 32 <= N && kc0 + kChunk <= N && (!a.causal || kc0 + kChunk - 1 <= qw0);
+        auto operand = [&](int sl) -> bf16x8 {
+            const int k = sl / 3, m = sl % 3;
+            if (m == 0) return rows_frag<D>(tnk, lane, k);
+            if (m == 1) return rows_frag<D>(tnv, lane, k);
+            return trans_frag<D>(tpk, lane, k / (D / 32), k % (D / 32));
+        };
+        bf16x8 op[kSlots];
+        float d0 = 0.f;  // the first dS of a pair
+        sc_n = f32x16{};
+        dp_n = f32x16{};
 #pragma unroll
-        for (int u = 0; u < kSub; ++u) {
-            float ds[16];
-            if (plain) {
+        for (int sl = 0; sl < kA; ++sl) op[sl] = operand(sl);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    ds[r] = exp2_hw(__builtin_fmaf(sc[u][r], a.scale_log2, -lse)) * (dp[u][r] - dsum);
-            } else {
+        for (int sl = 0; sl < kSlots; ++sl) {
+            if (sl + kA < kSlots) op[sl + kA] = operand(sl + kA);
+            const int k = sl / 3, m = sl % 3;
+            if (m == 0) sc_n = mfma_32x32x16(op[sl], qf[k], sc_n);
+            else if (m == 1) dp_n = mfma_32x32x16(op[sl], dof[k], dp_n);
+            else acc_dq[k % (D / 32)] = mfma_32x32x16(op[sl], sb_p[k / (D / 32)], acc_dq[k % (D / 32)]);
+            // load k of the chunk kAhead ahead in slot 4 k + 1
+            if ((sl & 3) == 1 && (sl >> 2) < kOps) issue_op(it + kAhead, st_load, sl >> 2);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kj = kc0 + 32 * u + acc_row(r, h);
-                    const bool ok = kj < N && query < N && (!a.causal || kj <= query);
-                    const float e = exp2_hw(__builtin_fmaf(sc[u][r], a.scale_log2, -lse));
-                    ds[r] = (ok ? e : 0.f) * (dp[u][r] - dsum);
+            for (int r = 0; r < 16; ++r) {
+                if (slot_of(r) != sl) continue;
+                // (the empty asm statements keep this work in its slot)
+                float sr = sc_c[r], dpr = dp_c[r];
+                asm volatile("" : "+v"(sr), "+v"(dpr));
+                float dr = exp2_hw(__builtin_fmaf(sr, a.scale_log2, -lse)) * (dpr - dsum);
+                asm volatile("" : "+v"(dr));
+                if (r & 1) {
+                    const int w = (r >> 1) & 3, t = r >> 3;
+                    u32x4 sw = __builtin_bit_cast(u32x4, sb_c[t]);
+                    sw[w] = pack_bf16x2(d0, dr);
+                    sb_c[t] = __builtin_bit_cast(bf16x8, sw);
+                } else {
+                    d0 = dr;
                 }
             }
-            // dQ^T += K^T dS^T (K-dim = the sub-chunk's keys)
-            const lds_cptr tk = lk + 32 * u * S::kRow;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    static_assert(4 * (kOps - 1) + 1 < kSlots, "every load of a chunk has its slot");
+    // before the step of chunk it: wait for chunk it + 1 (this wave's loads; the chunks after
+    // it, kAhead - 2 of them, stay in flight), barrier
+    auto advance = [&]() {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - 2) * kOps) : "memory");
+        __syncthreads();
+    };
+
+    if (total > 0) {
+        // prologue: the zero chunk -1 into stage kRing - 1, chunks 0 .. kAhead - 1 into stages
+        // 0 .. kAhead - 1; wait for chunks -1 and 0; chunk 0's scores
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const bf16x8 sb = acc_operand(ds, t);
+        for (int k = 0; k < kOps; ++k) issue_op(-1, kRing - 1, k);
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db)
-                    acc_dq[db] = mfma_32x32x16(trans_frag<D>(tk, lane, t, db), sb, acc_dq[db]);
+        for (int c = 0; c < kAhead; ++c)
+#pragma unroll
+            for (int k = 0; k < kOps; ++k) issue_op(c, c, k);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - 1) * kOps) : "memory");
+        __syncthreads();
+        f32x16 sa{}, da{}, sb2{}, db2{};
+        const bf16x8 zero8 = {};
+        bf16x8 qa[2] = {zero8, zero8}, qb[2] = {zero8, zero8};  // dS of even / odd chunks
+        {
+            const lds_cptr tk = lds, tv = lds + kT;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                sa = mfma_32x32x16(rows_frag<D>(tk, lane, kk), qf[kk], sa);
+                da = mfma_32x32x16(rows_frag<D>(tv, lane, kk), dof[kk], da);
             }
         }
-        if (it + 1 < total) store_chunk((it + 1) & 1);
-        __syncthreads();
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I3 = std::integral_constant<int, 3>;
+        static_assert(kRing == 4, "the loop below is unrolled over a ring of four stages");
+        for (int rd = 0; rd < rounds; ++rd) {
+            const int it = rd * kRing;
+            advance();
+            step(it, I0{}, sa, da, sb2, db2, qb, qa, 2);
+            advance();
+            step(it + 1, I1{}, sb2, db2, sa, da, qa, qb, 3);
+            advance();
+            step(it + 2, I2{}, sa, da, sb2, db2, qb, qa, 0);
+            advance();
+            step(it + 3, I3{}, sb2, db2, sa, da, qa, qb, 1);
+        }
+        // dQ of the last chunk of the walk (an odd chunk, in stage kRing - 1)
+        {
+            const lds_cptr tk = lds + (kRing - 1) * kStB;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+                    acc_dq[db] = mfma_32x32x16(trans_frag<D>(tk, lane, t, db), qb[t], acc_dq[db]);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still be writing LDS
     }
     if (query < N) {
         uint16_t* pq = a.dq + (qoff + query) * D;
