@@ -115,10 +115,11 @@ struct Tile {
     static constexpr int kKRow = D * kKElem + 16;                     // padded K row, bytes
     // V element bytes (fp8 e4m3 V: 1) and padded V row: bf16, the 64 B pad puts the four
     // rows a transposing read touches per cycle in four different 64 B bank windows; e4m3,
-    // 144 B rows put the eight consecutive rows of an 8-bit transposing read's 16-lane group
-    // in eight distinct 16 B bank groups
+    // an 8-bit transposing read gives two 16-lane groups 32 B of the same eight consecutive
+    // rows per cycle, and 160 B rows (5 x 32) put those eight 32 B pieces on eight distinct
+    // 32 B bank groups (144 B rows left two of them on the same banks)
     static constexpr int kVElem = kV8 ? 1 : 2;
-    static constexpr int kVRow = kV8 ? D + 16 : D * 2 + 64;
+    static constexpr int kVRow = kV8 ? D + 32 : D * 2 + 64;
     // paged: a K page (16 padded rows) occupies whole KiB, so no 1 KiB load spans two pages
     static constexpr int kKPage = kPaged ? (kPageTok * kKRow + 1023) / 1024 * 1024 : kPageTok * kKRow;
     static constexpr int kKStage = kPaged ? (kBc / kPageTok) * kKPage : kBc * kKRow;

@@ -239,3 +239,32 @@ def test_fwd_without_stats_recovers_from_a_stale_reference(causal, d, dev):
     assert_close(to_np(o), o_ref, "bf16", "O without statistics")
     o2, m2, l2 = run_fwd(x, dev, stats=True)
     assert_close(to_np(o2), o_ref, "bf16", "O with statistics")
+
+
+def test_fwd_at_the_offset_bound(dev):
+    """One head at the largest size the forward accepts (N d 2 = 2^30 bytes per head: N = 2^22
+    tokens at d = 128, causal): its last tiles sit just below 2^30 bytes into the K and V rows,
+    where the 32-bit tile offsets and the pad offset must still stay apart. Sampled rows, among
+    them the last, which sees every key, against the oracle; with and without statistics."""
+    import torch
+
+    N, d = 1 << 22, 128
+    log_case(f"fa_fwd at the offset bound: N={N} d={d}")
+    x = gen.fwd_inputs(1, 1, 1, N, d, 31, causal=True)
+    q, k, v = (gen.to_torch(t, "bf16", dev) for t in (x.q, x.k, x.v))
+    o, m, l = fa.fa_fwd(q, k, v, scale=x.scale, causal=True, return_stats=True)
+    o2 = fa.fa_fwd(q, k, v, scale=x.scale, causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(32)
+    rows = np.unique(np.concatenate([[0, 255, 256, N // 2, N - 257, N - 256, N - 1],
+                                     rng.integers(N - (1 << 16), N, size=5)]))
+    rows_t = torch.from_numpy(rows).to(dev)
+    o_s, o2_s = to_np(o[0, 0][rows_t]), to_np(o2[0, 0][rows_t])
+    m_s, l_s = to_np(m[0, 0][rows_t]), to_np(l[0, 0][rows_t])
+    del o, o2, m, l, q, k, v
+    o_ref, m_ref, l_ref = oracle.attention_head(x.q[0, 0], x.k[0, 0], x.v[0, 0], x.scale, True, rows=rows,
+                                                row_block=4)
+    assert_close(o_s, o_ref, "bf16", "rows at the offset bound")
+    assert_close(o2_s, o_ref, "bf16", "rows at the offset bound, without statistics")
+    np.testing.assert_allclose(m_s, m_ref, atol=1e-3, rtol=0)
+    np.testing.assert_allclose(l_s, l_ref, rtol=L_RTOL_BF16)
