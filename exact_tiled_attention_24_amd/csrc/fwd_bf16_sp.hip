@@ -107,19 +107,28 @@ constexpr int kPageTok = 16;      // tokens per page of the paged cache
 constexpr int kModeDense = 0, kModePaged = 1, kModeSparse = 2, kModeFp8 = 3, kModeFp8V = 4;
 typedef int v8i32 __attribute__((ext_vector_type(8)));
 
+// Chunk position of a 128-byte row's 16-byte chunk c (d = 64, bf16): c ^ swz64(r). Row bits
+// 1-3 spread the rows over the banks so that every read of the kernel is conflict-free: the
+// row reads (16 lanes, 16 rows, one chunk) and the transposing reads (two 16-lane groups, 4
+// rows, 4 adjacent chunks) each find distinct bank groups.
+__device__ __forceinline__ int swz64(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
 template <int D, bool kPaged, bool kFp8 = false, bool kV8 = false>
 struct Tile {
+    // d = 64 (bf16): unpadded rows with their 16 B chunks swizzled (swz64), so that a stage
+    // takes 16 KiB and two workgroups fit the LDS of one CU
+    static constexpr bool kSwz = D == 64 && !kFp8;
     // K element bytes (fp8 e4m3 K: 1); the 16 B pad keeps a 16 B read of 16 rows in 16
     // distinct bank groups for both row lengths
     static constexpr int kKElem = kFp8 ? 1 : 2;
-    static constexpr int kKRow = D * kKElem + 16;                     // padded K row, bytes
+    static constexpr int kKRow = kSwz ? D * 2 : D * kKElem + 16;      // padded K row, bytes
     // V element bytes (fp8 e4m3 V: 1) and padded V row: bf16, the 64 B pad puts the four
     // rows a transposing read touches per cycle in four different 64 B bank windows; e4m3,
     // an 8-bit transposing read gives two 16-lane groups 32 B of the same eight consecutive
     // rows per cycle, and 160 B rows (5 x 32) put those eight 32 B pieces on eight distinct
     // 32 B bank groups (144 B rows left two of them on the same banks)
     static constexpr int kVElem = kV8 ? 1 : 2;
-    static constexpr int kVRow = kV8 ? D + 32 : D * 2 + 64;
+    static constexpr int kVRow = kV8 ? D + 32 : (kSwz ? D * 2 : D * 2 + 64);
     // paged: a K page (16 padded rows) occupies whole KiB, so no 1 KiB load spans two pages
     static constexpr int kKPage = kPaged ? (kPageTok * kKRow + 1023) / 1024 * 1024 : kPageTok * kKRow;
     static constexpr int kKStage = kPaged ? (kBc / kPageTok) * kKPage : kBc * kKRow;
@@ -169,6 +178,9 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     constexpr bool kV8 = kMode == kModeFp8V;              // e4m3 V, P V on the fp8 matrix cores
     constexpr bool kFp8 = kMode == kModeFp8 || kV8;       // e4m3 Q and K
     using T = Tile<D, kPaged, kFp8, kV8>;
+    // LDS operand reads kept in flight: fewer for the dense d = 64 instance, whose two
+    // workgroups per CU leave a wave 128 registers
+    constexpr int kAh = T::kSwz && kMode == kModeDense ? 2 : kAhead;
     constexpr int kKTile = kBc * D * T::kKElem, kVTile = kBc * D * T::kVElem;  // HBM bytes of a tile
     const uint16_t* __restrict__ q = a.q;
     const uint16_t* __restrict__ k = a.k;
@@ -299,11 +311,15 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
             const int cpp = is_k ? T::kKChunksPerPage : T::kVChunksPerPage;
             dma_pg[i] = cc / cpp;
             const int slot = 1024 * (cc - dma_pg[i] * cpp) + 16 * lane;
-            const int row = slot / row_b, col = slot - row * row_b;
+            const int row = slot / row_b;
+            int col = slot - row * row_b;
+            if constexpr (T::kSwz) col = 16 * ((col >> 4) ^ swz64(row));  // the chunk stored here
             dma_src[i] = row < kPageTok && col < D * 2 ? unsigned(row * D * 2 + col) : kPadOffset;
         } else {
             const int slot = 1024 * cc + 16 * lane;
-            const int row = slot / row_b, col = slot - row * row_b;
+            const int row = slot / row_b;
+            int col = slot - row * row_b;
+            if constexpr (T::kSwz) col = 16 * ((col >> 4) ^ swz64(row));  // the chunk stored here
             const int rb = is_k ? D * T::kKElem : D * T::kVElem;  // HBM row bytes
             dma_src[i] = (col < rb ? unsigned(row * rb + col) : kPadOffset) +
                          unsigned(kSparse ? 0 : (is_k ? 3 * kKTile : 2 * kVTile));
@@ -470,13 +486,45 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     static_assert(!kPaged || T::kKStage + 2 * T::kKPage + 2 * D < 65536, "K offsets fit the immediate");
     static_assert(T::kVStage + 32 * T::kVRow + 20 * T::kVRow + 2 * D < 65536,
                   "V offsets fit the immediate");
+    // d = 64: swizzled rows, so the lane's column offset differs per 16-byte chunk. Every
+    // read takes a per-lane base for its chunk (K: one per 16 head dimensions; V: one per
+    // head-dimension block and row half) plus the stage offset as an immediate (two stages of
+    // K and V take 64 KiB, so one base per read reaches them all). The stage addresses below
+    // are then plain offsets from kz0 / vz0.
+    const lds_cptr kz0 = lds, vz0 = lds + T::kVBase;
+    lds_cptr base_kk[T::kSwz ? D / 16 : 1];
+    lds_cptr base_vv[T::kSwz ? D / 32 : 1][2];
+    if constexpr (T::kSwz) {
+        const int rk = kappa(l32);  // the lane's K row in a stage (paged pages are 16 whole rows)
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            base_kk[kk] = lds + rk * T::kKRow + 16 * ((2 * kk + hh) ^ swz64(rk));
+            asm volatile("" : "+v"(base_kk[kk]));
+        }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int rv = 8 * (lane >> 5) + ((lane & 15) >> 2) + 4 * h2;
+                const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+                base_vv[db][h2] = lds + T::kVBase + rv * T::kVRow + 16 * (c ^ swz64(rv)) + 8 * (lane & 1);
+                asm volatile("" : "+v"(base_vv[db][h2]));
+            }
+    }
     // K rows of half kb of stage st; V rows of half kb of stage st.
     auto k_at = [&](int st, int kb) {
-        if constexpr (kPaged) return (st < 2 ? base_k : base_k2) + (st & 1) * T::kKStage + 2 * kb * T::kKPage;
+        if constexpr (T::kSwz) return kz0 + st * T::kKStage + 32 * kb * T::kKRow;
+        else if constexpr (kPaged) return (st < 2 ? base_k : base_k2) + (st & 1) * T::kKStage + 2 * kb * T::kKPage;
         else return base_k + st * T::kKStage + 32 * kb * T::kKRow;
     };
     auto v_at = [&](int st, int kb) {
-        return (st < 2 ? base_v : base_v2) + (st & 1) * T::kVStage + 32 * kb * T::kVRow;
+        if constexpr (T::kSwz) return vz0 + st * T::kVStage + 32 * kb * T::kVRow;
+        else return (st < 2 ? base_v : base_v2) + (st & 1) * T::kVStage + 32 * kb * T::kVRow;
+    };
+    // K operand of head dimensions 16 kk .. of the rows at ks (the lane's row and chunk)
+    auto kfrag = [&](lds_cptr ks, int kk) -> bf16x8 {
+        if constexpr (T::kSwz) return *reinterpret_cast<const lds_bf16x8*>(base_kk[kk] + (ks - kz0));
+        else return *reinterpret_cast<const lds_bf16x8*>(ks + 32 * kk);
     };
 
     // fp8 K operand of the 64 head dimensions c of the rows at ks (two 16 B reads)
@@ -499,18 +547,22 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
             for (int c = 0; c < D / 64; ++c) s = mfma_fp8(kfrag8(ks, c), qf8[c], s);
         } else {
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                const bf16x8 a = *reinterpret_cast<const lds_bf16x8*>(ks + 32 * kk);
-                s = mfma_32x32x16(a, qf[kk], s);
-            }
+            for (int kk = 0; kk < D / 16; ++kk) s = mfma_32x32x16(kfrag(ks, kk), qf[kk], s);
         }
     };
     // V^T operand for key group t (16 keys) and head-dimension block db, from the V rows at
     // vb (a stage half).
     auto vfrag = [&](lds_cptr vb, int t, int db) -> bf16x8 {
-        const lds_cptr p = vb + 16 * t * T::kVRow + 64 * db;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * T::kVRow));
+        v4i16 lo, hi;
+        if constexpr (T::kSwz) {
+            const int off = (int)(vb - vz0) + 16 * t * T::kVRow;
+            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base_vv[db][0] + off));
+            hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base_vv[db][1] + off));
+        } else {
+            const lds_cptr p = vb + 16 * t * T::kVRow + 64 * db;
+            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+            hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * T::kVRow));
+        }
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     // O^T += V^T P^T of half tile (V stage st, half kb) with probabilities pk.
@@ -562,16 +614,16 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     // 16 (sl/2) ..), odd slots the O MFMAs (V^T, key group t, head-dimension block db).
     auto frag = [&](const Bases& b, int sl) -> bf16x8 {
         const int i = sl >> 1;
-        if ((sl & 1) == 0) return *reinterpret_cast<const lds_bf16x8*>(b.k + 32 * i);
+        if ((sl & 1) == 0) return kfrag(b.k, i);
         return vfrag(b.v, i / (D / 32), i % (D / 32));
     };
     // One pipeline step. Its MFMAs are O^T += V^T P^T of half tile hi-1 (probabilities
     // pk_prev) and S^T of half tile hi+1 (into s_next), taken alternately so consecutive MFMAs
     // are independent; beside them runs the softmax of half tile hi (s_cur -> pk_cur). The
-    // step is written as kSlots slots, each one LDS operand read (kAhead slots ahead), one
+    // step is written as kSlots slots, each one LDS operand read (kAh slots ahead), one
     // MFMA and a slice of the softmax, with a scheduling barrier after every slot, so the
     // instruction order is the one written here. `fr` holds on entry the operands of this
-    // step's first kAhead slots and on exit those of the next step's (read in this step's
+    // step's first kAh slots and on exit those of the next step's (read in this step's
     // last slots, so the next step starts without waiting, even across a barrier: its
     // operands were staged before the previous barrier).
     // (with_pv false: half tile 0, whose step has no O update; its odd slots stay empty.)
@@ -584,7 +636,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     // the next step (half tile hi+2) replace them in slots 2 and 6. V^T operands are read two
     // slots ahead (fr[0..1] carries the next step's first two).
     auto step = [&](int hi, int kv_tile, auto h8_c, f32x16& s_cur, f32x16& s_next, const u32x4 (&pk_prev)[2],
-                    u32x4 (&pk_cur)[2], bool masked, bf16x8 (&fr)[kAhead], v8i32 (&kq)[2],
+                    u32x4 (&pk_cur)[2], bool masked, bf16x8 (&fr)[kAh], v8i32 (&kq)[2],
                     auto with_pv, auto with_dma) {
         constexpr int H8 = decltype(h8_c)::value;
         constexpr bool kPV = decltype(with_pv)::value;
@@ -592,7 +644,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         constexpr int kS = D / 16;             // S^T MFMAs (one per 16 head dimensions)
         constexpr int kSlots = kFp8 ? D / 16 : 2 * kS;  // bf16: as many O MFMAs as S^T ones
         constexpr int kPhasesPerSlot = 16 / kSlots;
-        static_assert(kAhead <= kSlots, "read-ahead deeper than a step");
+        static_assert(kAh <= kSlots, "read-ahead deeper than a step");
 
         // Softmax of this half tile, cut into 16 phases (one per slot for d = 128) and
         // software-pipelined so that the instructions of one phase do not wait on each other:
@@ -686,14 +738,14 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
             return;
         }
 #pragma unroll
-        for (int sl = 0; sl < kAhead; ++sl) cur[sl] = fr[sl];
+        for (int sl = 0; sl < kAh; ++sl) cur[sl] = fr[sl];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int sl = 0; sl < kSlots; ++sl) {
-            if (sl + kAhead < kSlots) {
-                if (kPV || ((sl + kAhead) & 1) == 0) cur[sl + kAhead] = frag(b_cur, sl + kAhead);
+            if (sl + kAh < kSlots) {
+                if (kPV || ((sl + kAh) & 1) == 0) cur[sl + kAh] = frag(b_cur, sl + kAh);
             } else {
-                fr[sl + kAhead - kSlots] = frag(b_next, sl + kAhead - kSlots);
+                fr[sl + kAh - kSlots] = frag(b_next, sl + kAh - kSlots);
             }
             if ((sl & 1) == 0) {
                 s_next = mfma_32x32x16(cur[sl], qf[kFp8 ? 0 : sl >> 1], s_next);
@@ -725,7 +777,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
 
     f32x16 sa, sb;
     u32x4 pa[2], pb[2];
-    bf16x8 fr[kAhead];
+    bf16x8 fr[kAh];
     v8i32 kq[2] = {};  // fp8: K operands of the coming S^T (unused otherwise)
 
     using Yes = std::true_type;
@@ -916,12 +968,12 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         if constexpr (kFp8) {
             // step 0 has no O update; its S^T (half tile 1) takes K from the first stage
 #pragma unroll
-            for (int sl = 0; sl < kAhead; ++sl) fr[sl] = bf16x8{};
+            for (int sl = 0; sl < kAh; ++sl) fr[sl] = bf16x8{};
 #pragma unroll
             for (int c = 0; c < D / 64; ++c) kq[c] = kfrag8(b0.k, c);
         } else {
 #pragma unroll
-            for (int sl = 0; sl < kAhead; ++sl) fr[sl] = (sl & 1) ? bf16x8{} : frag(b0, sl);
+            for (int sl = 0; sl < kAh; ++sl) fr[sl] = (sl & 1) ? bf16x8{} : frag(b0, sl);
         }
     }
     advance(3);
@@ -1036,15 +1088,22 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     return true;
 }
 
-// Persistent grid: one workgroup per CU (the LDS allows no second one), a multiple of the 8
+// Persistent grid: one workgroup per CU (two for dense d = 64), a multiple of the 8
 // XCDs. Workgroup w runs on XCD w mod 8 and walks the x-th contiguous eighth of the work
 // list (so one KV group's tiles are re-read from one XCD's L2), taking its items in snake
 // order over the XCD's workgroups: round r gives the workgroup of local index j the item
 // r * W + j (r even) or r * W + W - 1 - j (r odd). The list runs heaviest query block first,
 // so the snake pairs heavy with light items and the workgroups finish together; and a
 // workgroup moves to its next item without a new launch.
+// Workgroups per CU: two for the dense d = 64 instance (its swizzled stages take 64 KiB of
+// LDS and it fits 128 registers a wave); one otherwise (the paged and block-sparse d = 64
+// instances would spill at 128 registers).
+template <int D, int kMode>
+constexpr int kWgPerCu = Tile<D, false>::kSwz && kMode == kModeDense ? 2 : 1;
+
+// (the second bound is the waves per SIMD the register budget must allow)
 template <int D, int kMode, bool kStats>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, (kWgPerCu<D, kMode> * kWaves / 4)) void fwd_bf16_sp_kernel(FwdArgs a) {
     using T = Tile<D, kMode == kModePaged, kMode == kModeFp8 || kMode == kModeFp8V, kMode == kModeFp8V>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * (T::kKStage + T::kVStage)];
 
@@ -1064,8 +1123,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_sp_kernel(FwdArgs a) {
         seg0 = xcd * per_xcd;
         seg_n = min_(per_xcd, total - seg0);
     }
+    // Two workgroups per CU: local ids j and j + W / 2 are taken to share a CU, so the snake
+    // runs over W / 2 units whose rounds alternate between the two (a heavy item on one of
+    // them, the matching light one on the other).
+    constexpr int kPer = kWgPerCu<D, kMode>;
+    const int Wu = W / kPer, u = j % Wu, sub = j / Wu;
     for (int r = 0; r * W < seg_n; ++r) {
-        const int local = r * W + ((r & 1) ? W - 1 - j : j);
+        const int rr = kPer * r + sub;  // the unit's round
+        const int local = rr * Wu + ((rr & 1) ? Wu - 1 - u : u);
         if (local >= seg_n) continue;
         int item;
         if constexpr (kMode != kModeDense) {
@@ -1084,8 +1149,12 @@ namespace {
 template <int kMode>
 hipError_t launch_sp(const FwdArgs& a, int d, hipStream_t stream) {
     const long long items = (long long)a.nqb * a.B * a.Hq;
-    const long long slots = (long long)(device_cus() / kXcds) * kXcds;
-    long long grid = (items + kXcds - 1) / kXcds * kXcds;
+    // (dense d = 64: two workgroups per CU; the grid is a multiple of 8 x that count, so that
+    // every XCD's workgroups pair up)
+    const int per_cu = d == 64 ? kWgPerCu<64, kMode> : 1;
+    const long long unit = (long long)kXcds * per_cu;
+    const long long slots = (long long)(device_cus() / kXcds) * unit;
+    long long grid = (items + unit - 1) / unit * unit;
     if (grid > slots) grid = slots;
     const bool stats = a.m_out != nullptr || a.l_out != nullptr;
     const dim3 g((unsigned)grid), blk(kThreads);
