@@ -139,6 +139,45 @@ __device__ __forceinline__ bf16x8 trans_frag(lds_cptr tile, int lane, int t, int
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// The same reads from lane offsets computed once: the byte offsets, from the LDS base, of this
+// lane's row reads (per K-dim chunk kk) and transposing reads (two per head-dim block db) in a
+// tile at byte `base`. They are held opaque to the compiler, so each read of a tile at base +
+// an immediate is one register plus that immediate, not an address recomputed per read.
+template <int D>
+struct LaneOffsets {
+    unsigned ro[D / 16];
+    unsigned tr[D / 32][2];
+    __device__ __forceinline__ void init(int lane, unsigned base) {
+        constexpr int R = Stage<D, 1>::kRow;
+        const int rr = kappa(lane & 31);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            ro[kk] = base + (unsigned)(rr * R + 16 * ((2 * kk + (lane >> 5)) ^ swz<D>(rr)));
+            asm volatile("" : "+v"(ro[kk]));
+        }
+        const int r = 8 * (lane >> 5) + ((lane & 15) >> 2);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+            tr[db][0] = base + (unsigned)(8 * (lane & 1) + r * R + 16 * (c ^ swz<D>(r)));
+            tr[db][1] = base + (unsigned)(8 * (lane & 1) + (r + 4) * R + 16 * (c ^ swz<D>(r + 4)));
+            asm volatile("" : "+v"(tr[db][0]), "+v"(tr[db][1]));
+        }
+    }
+    // rows_frag of the tile `at` bytes past `base`
+    __device__ __forceinline__ bf16x8 rows(lds_cptr lds, int at, int kk) const {
+        return *reinterpret_cast<const lds_bf16x8*>(lds + ro[kk] + at);
+    }
+    // trans_frag of the tile `at` bytes past `base`
+    __device__ __forceinline__ bf16x8 trans(lds_cptr lds, int at, int t, int db) const {
+        constexpr int R = Stage<D, 1>::kRow;
+        const int o = at + 16 * t * R;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds + tr[db][0] + o));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds + tr[db][1] + o));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+};
+
 // Accumulator registers 8 t .. 8 t + 7, rounded to bf16: the B operand (K-dim rows 16 t ..).
 __device__ __forceinline__ bf16x8 acc_operand(const float (&x)[16], int t) {
     u32x4 w;
@@ -252,9 +291,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     constexpr int kAhead = kRing - 2;                     // chunks c - 1 .. c + 1 are in use
     constexpr int kOps = 2 * Dma::kPerWave + 1;           // loads per wave and chunk
     constexpr int kA = 3;                                 // LDS operand reads kept in flight
-    constexpr int kQ0 = 0, kDo0 = kRing * kT, kLd0 = 2 * kRing * kT;  // regions of the ring
     constexpr int kLdB = 2 * kChunk * 4;                  // L and D of a chunk's rows
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kRing * kT + kRing * kLdB];
+    // the ring: the L and D of every stage, then the Q rows of every stage, then the dO rows;
+    // each region spans less than the 64 KiB that an LDS instruction's immediate offset
+    // reaches from one lane offset
+    constexpr int kQ0 = kRing * kLdB, kDo0 = kQ0 + kRing * kT;
+    auto ld_at = [](int st) { return st * kLdB; };
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kDo0 + kRing * kT];
 
     const int N = a.N, G = a.Hq / a.Hkv;
     const int pos = xcd_position(gridDim.x * gridDim.y);
@@ -301,46 +344,65 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     // each) and the chunk's L and D (256 bytes, one dword per lane; every wave loads the same
     // bytes, so each wave issues kOps loads per chunk and one vmcnt count serves all). A chunk
     // past the walk (or before it) reads from past every range and fills zeros.
-    struct Loads {
+    struct Heads {  // the buffers of one query head: Q rows, dO rows, L and D
         __amdgpu_buffer_rsrc_t rq, rdo, rld;
+    };
+    struct Loads {
+        Heads hd;
         unsigned row0, ldo, st;
     };
-    // chunk cursors (wave-uniform): the next chunk to load and the chunk of the next step,
-    // each as (walk index, query head g, chunk j of that head)
-    int ld_it = 0, ld_g = 0, ld_j = 0, st_it = 0, st_g = 0, st_j = 0;
-    auto prepare = [&](int it, int g, int j, int st) -> Loads {
-        const bool real = it >= 0 && it < total;
-        const int gg = real ? g : 0;
-        const int qc0 = qtop - j * kChunk;
-        const size_t hq = (size_t)b * a.Hq + (size_t)kvh * G + gg;
-        Loads l;
-        l.rq = __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + hq * N * D), (short)0, head_bytes, kRsrcWord3);
-        l.rdo = __builtin_amdgcn_make_buffer_rsrc((void*)(a.dout + hq * N * D), (short)0, head_bytes, kRsrcWord3);
-        l.rld = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ld + hq * 2 * ld_rows(N)), (short)0, ld_bytes,
+    const size_t hq0 = (size_t)b * a.Hq + (size_t)kvh * G;  // the group's first query head
+    auto head_buffers = [&](int g) -> Heads {
+        const size_t hq = hq0 + (size_t)g;
+        Heads r;
+        r.rq = __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + hq * N * D), (short)0, head_bytes, kRsrcWord3);
+        r.rdo = __builtin_amdgcn_make_buffer_rsrc((void*)(a.dout + hq * N * D), (short)0, head_bytes, kRsrcWord3);
+        r.rld = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ld + hq * 2 * ld_rows(N)), (short)0, ld_bytes,
                                                   kRsrcWord3);
-        l.row0 = real ? (unsigned)qc0 * R : 0x80000000u;
-        l.ldo = real ? (unsigned)qc0 * 8u : 0x80000000u;
-        l.st = (unsigned)st;
-        return l;
+        return r;
+    };
+    // chunk cursors (wave-uniform), kept incrementally so that a step spends a few scalar
+    // instructions on them: the next chunk to load as (walk index, query head, byte offsets
+    // of its rows and of its L and D in that head, the head's buffers, rebuilt only when the
+    // walk moves on to the next head), and the walk index and first query row of the next
+    // step's chunk
+    const unsigned row_top = (unsigned)qtop * R, row_first = (unsigned)q_first * R;
+    int ld_it = 0, ld_g = 0, st_it = 0, st_q = qtop;
+    unsigned ld_row = row_top, ld_ldo = (unsigned)qtop * 8u;
+    Heads ld_h = head_buffers(0);
+    // the loads of the next chunk into stage st; advance_load() moves on after its last load
+    auto load_of = [&](int st) -> Loads {
+        const bool real = ld_it < total;
+        return Loads{ld_h, real ? ld_row : 0x80000000u, real ? ld_ldo : 0x80000000u, (unsigned)st};
+    };
+    auto advance_load = [&]() {
+        ++ld_it;
+        if (ld_row == row_first) {
+            ld_row = row_top;
+            ld_ldo = (unsigned)qtop * 8u;
+            if (++ld_g < G) ld_h = head_buffers(ld_g);
+        } else {
+            ld_row -= (unsigned)(kChunk * R);
+            ld_ldo -= (unsigned)(kChunk * 8);
+        }
     };
     auto next_load = [&](int st) -> Loads {
-        const Loads l = prepare(ld_it, ld_g, ld_j, st);
-        ++ld_it;
-        if (++ld_j == nch) ld_j = 0, ++ld_g;
+        const Loads l = load_of(st);
+        advance_load();
         return l;
     };
     // load k (0 .. kOps - 1) of a chunk
     auto issue_op = [&](const Loads& l, int k) {
         constexpr int P = Dma::kPerWave;
         if (k < P) {
-            dma.issue_one(l.rq, l.row0, lds_base + (unsigned)kQ0 + l.st * (unsigned)kT, wave, k);
+            dma.issue_one(l.hd.rq, l.row0, lds_base + (unsigned)kQ0 + l.st * (unsigned)kT, wave, k);
         } else if (k < 2 * P) {
-            dma.issue_one(l.rdo, l.row0, lds_base + (unsigned)kDo0 + l.st * (unsigned)kT, wave, k - P);
+            dma.issue_one(l.hd.rdo, l.row0, lds_base + (unsigned)kDo0 + l.st * (unsigned)kT, wave, k - P);
         } else {
             asm volatile("buffer_load_dword %0, %1, 0 offen lds"
                          :
-                         : "v"(l.ldo + 4u * (unsigned)lane), "s"(l.rld),
-                           "{m0}"(lds_base + (unsigned)kLd0 + l.st * (unsigned)kLdB)
+                         : "v"(l.ldo + 4u * (unsigned)lane), "s"(l.hd.rld),
+                           "{m0}"(lds_base + l.st * (unsigned)kLdB)
                          : "memory");
         }
     };
@@ -349,6 +411,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         for (int k = 0; k < kOps; ++k) issue_op(l, k);
     };
     const lds_cptr lds = (lds_cptr)smem;
+    LaneOffsets<D> oq, odo;  // the Q and the dO region
+    oq.init(lane, kQ0);
+    odo.init(lane, kDo0);
 
     // products of slot sl of a step: even slots S / dP of the next chunk (S when sl % 4 == 0,
     // head dims 16 (sl / 4) ..), odd slots dV / dK of the previous chunk (query group t,
@@ -364,21 +429,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     // st_c: chunk it's ring stage.
     auto step = [&](auto st_c, f32x16& sc_c, f32x16& dp_c, f32x16& sc_n, f32x16& dp_n,
                     const bf16x8 (&pb_p)[2], const bf16x8 (&sb_p)[2], bf16x8 (&pb_c)[2],
-                    bf16x8 (&sb_c)[2], const Loads& ld) {
+                    bf16x8 (&sb_c)[2], int st_load) {
         constexpr int Pc = decltype(st_c)::value;
         constexpr int Pn = (Pc + 1) % kRing, Pp = (Pc + kRing - 1) % kRing;
-        const lds_cptr tn = lds + kQ0 + Pn * kT, tnd = lds + kDo0 + Pn * kT;  // next chunk's rows
-        const lds_cptr tp = lds + kQ0 + Pp * kT, tpd = lds + kDo0 + Pp * kT;  // previous chunk's
-        const lds_cptr s_l = lds + kLd0 + Pc * kLdB, s_d = s_l + 4 * kChunk;   // L, D
+        const lds_cptr s_l = lds + ld_at(Pc), s_d = s_l + 4 * kChunk;  // L, D
         // keys past the query get the score -inf where the chunk reaches above the wave's keys
         // (causal; a wave-uniform branch, rare: zero chunks and most chunks need none)
-        const int qc0 = qtop - st_j * kChunk;
-        if (a.causal && st_it < total && qc0 < kw0 + 31) {
+        if (a.causal && st_it < total && st_q < kw0 + 31) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sc_c[r] = key <= qc0 + acc_row(r, h) ? sc_c[r] : -INFINITY;
+            for (int r = 0; r < 16; ++r) sc_c[r] = key <= st_q + acc_row(r, h) ? sc_c[r] : -INFINITY;
         }
         ++st_it;
-        if (++st_j == nch) st_j = 0, ++st_g;
+        st_q = st_q == q_first ? qtop : st_q - kChunk;
         // L and D of register r's row acc_row(r, h): element r % 4 of the 16-byte run at row
         // 16 (r / 8) + 8 h + 4 ((r / 4) % 2)
         auto ld4 = [&](lds_cptr base, int r) -> f32x4 {
@@ -387,13 +449,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         };
         auto operand = [&](int sl) -> bf16x8 {
             const int i = sl >> 1;
-            if ((sl & 1) == 0) return rows_frag<D>((i & 1) ? tnd : tn, lane, i >> 1);
+            // next chunk: Q rows (S) and dO rows (dP); previous chunk: dO^T (dV) and Q^T (dK)
+            if ((sl & 1) == 0) return ((i & 1) ? odo : oq).rows(lds, Pn * kT, i >> 1);
             const int t = i / (kPrev / 2), db = (i >> 1) % (D / 32);
-            return trans_frag<D>((i & 1) ? tp : tpd, lane, t, db);
+            return ((i & 1) ? oq : odo).trans(lds, Pp * kT, t, db);
         };
         bf16x8 op[kSlots];
         f32x4 lq = ld4(s_l, 0), dq4 = ld4(s_d, 0);  // L, D of registers 0 .. 3
         float p0 = 0.f, d0 = 0.f;                    // the first score of a pair
+        Loads ld;  // the loads of this step's chunk kAhead ahead (set up after the first products)
         sc_n = f32x16{};
         dp_n = f32x16{};
 #pragma unroll
@@ -411,8 +475,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
                 if ((i & 1) == 0) acc_dv[db] = mfma_32x32x16(op[sl], pb_p[t], acc_dv[db]);
                 else acc_dk[db] = mfma_32x32x16(op[sl], sb_p[t], acc_dk[db]);
             }
-            // load k in slot 4 k + 2
+            // the loads' descriptors in slot 1 (scalar work beside the products), load k in
+            // slot 4 k + 2
+            if (sl == 1) ld = load_of(st_load);
             if ((sl & 3) == 2 && (sl >> 2) < kOps) issue_op(ld, sl >> 2);
+            if (sl == 4 * (kOps - 1) + 3) advance_load();
             // vector work: score r (its probability and dS) in the last slot of each group of
             // kSpread, pairs packed to bf16 as soon as both are done; L and D of the next four
             // registers are read a score ahead of their use
@@ -429,8 +496,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
                     const int w = (r >> 1) & 3, t = r >> 3;
                     u32x4 pw = __builtin_bit_cast(u32x4, pb_c[t]);
                     u32x4 sw = __builtin_bit_cast(u32x4, sb_c[t]);
-                    pw[w] = pack_bf16x2(p0, pr);
-                    sw[w] = pack_bf16x2(d0, dr);
+                    uint32_t wp = pack_bf16x2(p0, pr), wd = pack_bf16x2(d0, dr);
+                    asm volatile("" : "+v"(wp), "+v"(wd));  // packed here, not at their first use
+                    pw[w] = wp;
+                    sw[w] = wd;
                     pb_c[t] = __builtin_bit_cast(bf16x8, pw);
                     sb_c[t] = __builtin_bit_cast(bf16x8, sw);
                 } else {
@@ -447,18 +516,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     };
     static_assert(4 * (kOps - 1) + 2 < kSlots, "every load of a chunk has its slot");
     // before a step: wait for the next chunk (this wave's loads; the kAhead - 2 chunks after it
-    // stay in flight), barrier, then the loads of the chunk kAhead ahead into the stage chunk
-    // it - 2 used
-    auto advance = [&](int st_load) -> Loads {
+    // stay in flight), barrier; the step then loads the chunk kAhead ahead into stage st_load,
+    // the one chunk it - 2 used
+    auto advance = [&](int st_load) -> int {
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - 2) * kOps) : "memory");
         __syncthreads();
-        return next_load(st_load);
+        return st_load;
     };
 
     if (total > 0) {
         // prologue: the zero chunk -1 into stage kRing - 1, chunks 0 .. kAhead - 1 into stages
         // 0 .. kAhead - 1; wait for chunks -1 and 0; chunk 0's scores
-        issue_all(prepare(-1, 0, 0, kRing - 1));
+        issue_all(Loads{ld_h, 0x80000000u, 0x80000000u, (unsigned)(kRing - 1)});
 #pragma unroll
         for (int c = 0; c < kAhead; ++c) issue_all(next_load(c));
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - 1) * kOps) : "memory");
@@ -468,11 +537,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         bf16x8 pa[2] = {zero8, zero8}, qa[2] = {zero8, zero8};   // P, dS of even chunks
         bf16x8 pb[2] = {zero8, zero8}, qb[2] = {zero8, zero8};   // of odd chunks (and chunk -1)
         {
-            const lds_cptr tq = lds + kQ0, tdo = lds + kDo0;
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
-                sa = mfma_32x32x16(rows_frag<D>(tq, lane, kk), kf[kk], sa);
-                da = mfma_32x32x16(rows_frag<D>(tdo, lane, kk), vf[kk], da);
+                sa = mfma_32x32x16(oq.rows(lds, 0, kk), kf[kk], sa);
+                da = mfma_32x32x16(odo.rows(lds, 0, kk), vf[kk], da);
             }
         }
         using I0 = std::integral_constant<int, 0>;
@@ -492,13 +560,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
         // dV, dK of the last chunk of the walk (an odd chunk, in stage kRing - 1)
         {
-            const lds_cptr tq = lds + kQ0 + (kRing - 1) * kT, tdo = lds + kDo0 + (kRing - 1) * kT;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    acc_dv[db] = mfma_32x32x16(trans_frag<D>(tdo, lane, t, db), pb[t], acc_dv[db]);
-                    acc_dk[db] = mfma_32x32x16(trans_frag<D>(tq, lane, t, db), qb[t], acc_dk[db]);
+                    acc_dv[db] = mfma_32x32x16(odo.trans(lds, (kRing - 1) * kT, t, db), pb[t], acc_dv[db]);
+                    acc_dk[db] = mfma_32x32x16(oq.trans(lds, (kRing - 1) * kT, t, db), qb[t], acc_dk[db]);
                 }
         }
         // no load may still be writing LDS when the workgroup ends
