@@ -178,6 +178,23 @@ struct LaneOffsets {
     }
 };
 
+// The products of the dK, dV loop, written out so that each keeps the register file it needs:
+// S and dP in VGPRs, which the vector work reads directly, the dK and dV accumulators in
+// AGPRs, which only the products touch. The compiler does not know these for matrix
+// instructions and adds no wait states around them: every read of a product's result stands
+// a product and a dozen instructions or more after it (in the loop, a step later; before the
+// epilogue's reads an explicit wait), and the A operands come from LDS reads whose counter
+// waits the compiler places as for any instruction that reads the registers.
+__device__ __forceinline__ void mma_v0(f32x16& d, bf16x8 a, bf16x8 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mma_v(f32x16& d, bf16x8 a, bf16x8 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mma_a(f32x16& d, bf16x8 a, bf16x8 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+
 // Accumulator registers 8 t .. 8 t + 7, rounded to bf16: the B operand (K-dim rows 16 t ..).
 __device__ __forceinline__ bf16x8 acc_operand(const float (&x)[16], int t) {
     u32x4 w;
@@ -455,60 +472,102 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
             return ((i & 1) ? oq : odo).trans(lds, Pp * kT, t, db);
         };
         bf16x8 op[kSlots];
-        f32x4 lq = ld4(s_l, 0), dq4 = ld4(s_d, 0);  // L, D of registers 0 .. 3
-        float p0 = 0.f, d0 = 0.f;                    // the first score of a pair
+        // The vector work of score r in three parts, pipelined over the slots so that each
+        // slot's instructions take about as long to issue as its product takes to run (one
+        // wave per SIMD issues in order: work beyond that delays the next product):
+        //   A(r): the scores out of the accumulator registers, x = s scale log2e - L, u = dP - D
+        //   B(r): p = exp2(x)
+        //   C(r): dS = p u; pairs (r - 1, r) packed to bf16 in a later slot
+        // With two slots per score (d = 128) slot 2 r holds A(r) and C(r - 1), slot 2 r + 1
+        // holds B(r) and the pack of the pair before; with one slot per score (d = 64) a slot
+        // does all of score r. The empty asm statements keep each part in its slot (without
+        // them the compiler gathers the chunk's vector work ahead of the products).
+        // L and D of registers 4 g .. 4 g + 3 are read four scores ahead of their first use.
+        f32x4 lq = ld4(s_l, 0), dq4 = ld4(s_d, 0);   // L, D of registers 0 .. 3
+        f32x4 lqn = ld4(s_l, 4), dqn = ld4(s_d, 4);  // of registers 4 .. 7
+        float xs[16], us[16], ps[16], dss[16];
+        auto part_a = [&](int r, float sr, float dpr) {
+            if (r >= 4 && (r & 3) == 0) {
+                lq = lqn;
+                dq4 = dqn;
+                if (r + 4 < 16) {
+                    lqn = ld4(s_l, r + 4);
+                    dqn = ld4(s_d, r + 4);
+                }
+            }
+            xs[r] = __builtin_fmaf(sr, a.scale_log2, -lq[r & 3]);
+            us[r] = dpr - dq4[r & 3];
+            asm volatile("" : "+v"(xs[r]), "+v"(us[r]));
+        };
+        auto part_b = [&](int r) {
+            ps[r] = exp2_hw(xs[r]);
+            asm volatile("" : "+v"(ps[r]));
+        };
+        auto part_c = [&](int r) {
+            dss[r] = ps[r] * us[r];
+            asm volatile("" : "+v"(dss[r]));
+        };
+        // the pair (r - 1, r) into the operands
+        auto pack = [&](int r) {
+            const int w = (r >> 1) & 3, t = r >> 3;
+            u32x4 pw = __builtin_bit_cast(u32x4, pb_c[t]);
+            u32x4 sw = __builtin_bit_cast(u32x4, sb_c[t]);
+            uint32_t wp = pack_bf16x2(ps[r - 1], ps[r]), wd = pack_bf16x2(dss[r - 1], dss[r]);
+            asm volatile("" : "+v"(wp), "+v"(wd));  // packed here, not at their first use
+            pw[w] = wp;
+            sw[w] = wd;
+            pb_c[t] = __builtin_bit_cast(bf16x8, pw);
+            sb_c[t] = __builtin_bit_cast(bf16x8, sw);
+        };
         Loads ld;  // the loads of this step's chunk kAhead ahead (set up after the first products)
-        sc_n = f32x16{};
-        dp_n = f32x16{};
 #pragma unroll
         for (int sl = 0; sl < kA; ++sl) op[sl] = operand(sl);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int sl = 0; sl < kSlots; ++sl) {
+            // A(r)'s scores, taken at the slot's start. Slot 0 reads what the last products of
+            // the step before wrote (dP at its slot 2 kSlots - 2): the wait states give them the
+            // time that a matrix instruction's result needs before a vector read.
+            const bool has_a = kSpread == 1 || (sl & 1) == 0;
+            const int r = sl / kSpread;
+            if (sl == 0) asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+            float sr = 0.f, dpr = 0.f;
+            if (has_a) {
+                sr = sc_c[r];
+                dpr = dp_c[r];
+                asm volatile("" : "+v"(sr), "+v"(dpr));
+            }
             if (sl + kA < kSlots) op[sl + kA] = operand(sl + kA);
             const int i = sl >> 1;
             if ((sl & 1) == 0) {
-                if ((i & 1) == 0) sc_n = mfma_32x32x16(op[sl], kf[i >> 1], sc_n);
-                else dp_n = mfma_32x32x16(op[sl], vf[i >> 1], dp_n);
+                f32x16& acc = (i & 1) ? dp_n : sc_n;
+                const bf16x8 b = (i & 1) ? vf[i >> 1] : kf[i >> 1];
+                if (i < 2) mma_v0(acc, op[sl], b);
+                else mma_v(acc, op[sl], b);
             } else {
                 const int t = i / (kPrev / 2), db = (i >> 1) % (D / 32);
-                if ((i & 1) == 0) acc_dv[db] = mfma_32x32x16(op[sl], pb_p[t], acc_dv[db]);
-                else acc_dk[db] = mfma_32x32x16(op[sl], sb_p[t], acc_dk[db]);
+                if ((i & 1) == 0) mma_a(acc_dv[db], op[sl], pb_p[t]);
+                else mma_a(acc_dk[db], op[sl], sb_p[t]);
             }
             // the loads' descriptors in slot 1 (scalar work beside the products), load k in
             // slot 4 k + 2
             if (sl == 1) ld = load_of(st_load);
             if ((sl & 3) == 2 && (sl >> 2) < kOps) issue_op(ld, sl >> 2);
             if (sl == 4 * (kOps - 1) + 3) advance_load();
-            // vector work: score r (its probability and dS) in the last slot of each group of
-            // kSpread, pairs packed to bf16 as soon as both are done; L and D of the next four
-            // registers are read a score ahead of their use
-            if (sl % kSpread == kSpread - 1) {
-                const int r = sl / kSpread;
-                // (the empty asm statements keep this work in its slot: without them the
-                // compiler gathers the whole chunk's vector work ahead of the products)
-                float sr = sc_c[r], dpr = dp_c[r];
-                asm volatile("" : "+v"(sr), "+v"(dpr));
-                float pr = exp2_hw(__builtin_fmaf(sr, a.scale_log2, -lq[r & 3]));
-                float dr = pr * (dpr - dq4[r & 3]);
-                asm volatile("" : "+v"(pr), "+v"(dr));
-                if (r & 1) {
-                    const int w = (r >> 1) & 3, t = r >> 3;
-                    u32x4 pw = __builtin_bit_cast(u32x4, pb_c[t]);
-                    u32x4 sw = __builtin_bit_cast(u32x4, sb_c[t]);
-                    uint32_t wp = pack_bf16x2(p0, pr), wd = pack_bf16x2(d0, dr);
-                    asm volatile("" : "+v"(wp), "+v"(wd));  // packed here, not at their first use
-                    pw[w] = wp;
-                    sw[w] = wd;
-                    pb_c[t] = __builtin_bit_cast(bf16x8, pw);
-                    sb_c[t] = __builtin_bit_cast(bf16x8, sw);
-                } else {
-                    p0 = pr;
-                    d0 = dr;
-                }
-                if ((r & 3) == 3 && r + 1 < 16) {
-                    lq = ld4(s_l, r + 1);
-                    dq4 = ld4(s_d, r + 1);
+            if (kSpread == 1) {
+                part_a(r, sr, dpr);
+                part_b(r);
+                part_c(r);
+                if (r & 1) pack(r);
+            } else if (has_a) {
+                part_a(r, sr, dpr);
+                if (r >= 1) part_c(r - 1);
+            } else {
+                part_b(r);
+                if (r >= 2 && (r & 1) == 0) pack(r - 1);
+                if (r == 15) {
+                    part_c(15);
+                    pack(15);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -537,10 +596,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         bf16x8 pa[2] = {zero8, zero8}, qa[2] = {zero8, zero8};   // P, dS of even chunks
         bf16x8 pb[2] = {zero8, zero8}, qb[2] = {zero8, zero8};   // of odd chunks (and chunk -1)
         {
+            mma_v0(sa, oq.rows(lds, 0, 0), kf[0]);
+            mma_v0(da, odo.rows(lds, 0, 0), vf[0]);
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                sa = mfma_32x32x16(oq.rows(lds, 0, kk), kf[kk], sa);
-                da = mfma_32x32x16(odo.rows(lds, 0, kk), vf[kk], da);
+            for (int kk = 1; kk < D / 16; ++kk) {
+                mma_v(sa, oq.rows(lds, 0, kk), kf[kk]);
+                mma_v(da, odo.rows(lds, 0, kk), vf[kk]);
             }
         }
         using I0 = std::integral_constant<int, 0>;
@@ -564,12 +625,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    acc_dv[db] = mfma_32x32x16(odo.trans(lds, (kRing - 1) * kT, t, db), pb[t], acc_dv[db]);
-                    acc_dk[db] = mfma_32x32x16(oq.trans(lds, (kRing - 1) * kT, t, db), qb[t], acc_dk[db]);
+                    mma_a(acc_dv[db], odo.trans(lds, (kRing - 1) * kT, t, db), pb[t]);
+                    mma_a(acc_dk[db], oq.trans(lds, (kRing - 1) * kT, t, db), qb[t]);
                 }
         }
         // no load may still be writing LDS when the workgroup ends
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // the wait states between the last products and the reads of their accumulators
+        // (the accumulators pass through, so that no read moves ahead of the wait)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) asm volatile("" : "+a"(acc_dv[db]), "+a"(acc_dk[db]));
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) asm volatile("" : "+a"(acc_dv[db]), "+a"(acc_dk[db]));
     }
     // accumulator register r of block db: head dimension 32 db + 8 (r / 4) + 4 h + r % 4
     if (key < N) {
