@@ -6,7 +6,9 @@ One step = one pass of the whole path over one batch of synthetic input:
   2. fa_decode_splitk (split-K paged decode, partials merged in the same launch) on B=8
      sequences, 32 query heads over 8 KV heads, d=128, lengths uniform in [16384, 32768],
      16-token pages.
-Inputs are generated once (seeded) and are resident in HBM before timing starts. After the
+Inputs are generated once (seeded) and are resident in HBM before timing starts. The
+default 30 untimed steps (about 35 ms of work) let the clock settle first: after an idle
+period it ramps over the first 20 to 30 forward calls. After the
 steps, each in a loop of its own: fa_fwd on the other two prefill workloads (causal B=4 H=16
 N=2048 d=64, and causal GQA B=1 Hq=32 Hkv=8 N=32768 d=128), chunked prefill over the paged
 cache, the block-sparse forward, the backward and the fp8 forward.
@@ -45,7 +47,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--fwd-config", type=int, default=3, choices=[2, 3, 4])
     ap.add_argument("--decode-splits", type=int, default=0, help="0 = the library's plan")
     ap.add_argument("--kv-pools", type=int, default=2,

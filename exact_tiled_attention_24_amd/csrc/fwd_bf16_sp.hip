@@ -671,11 +671,31 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
                 e1[ke] = exp2_hw(__builtin_fmaf(s_cur[2 * ke + 1], scale_log2, -m_ref));
             }
         };
+        // without statistics: one score per phase from phase 0 (exp2), pair k packed in the
+        // phase after its second score and summed one phase later (the last pair at once)
+        float es[16];
+        auto single_stages = [&](int ph) {
+            es[ph] = exp2_hw(__builtin_fmaf(s_cur[ph], scale_log2, -m_ref));
+            auto pack_pair = [&](int k) {
+                wk[k] = pack_bf16x2(es[2 * k], es[2 * k + 1]);
+                pk_cur[k >> 2][k & 3] = wk[k];
+            };
+            auto sum_pair = [&](int k) {
+                l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wk[k]),
+                                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), l_part, false);
+            };
+            if (ph >= 2 && (ph & 1) == 0) pack_pair(ph / 2 - 1);
+            if (ph >= 3 && (ph & 1) == 1) sum_pair((ph - 3) / 2);
+            if (ph == 15) {
+                pack_pair(7);
+                sum_pair(7);
+            }
+        };
         auto phase = [&](int ph) {
             if constexpr (!kStats) {
                 // no row maximum: the exponentials start at once against the current reference
                 if (ph == 0 && __builtin_expect(masked, 0)) mask_scores();
-                pair_stages(ph, 6);
+                single_stages(ph);
                 return;
             }
             if (ph == 0) {
