@@ -107,17 +107,23 @@ constexpr int kPageTok = 16;      // tokens per page of the paged cache
 constexpr int kModeDense = 0, kModePaged = 1, kModeSparse = 2, kModeFp8 = 3, kModeFp8V = 4;
 typedef int v8i32 __attribute__((ext_vector_type(8)));
 
-// Chunk position of a 128-byte row's 16-byte chunk c (d = 64, bf16): c ^ swz64(r). Row bits
-// 1-3 spread the rows over the banks so that every read of the kernel is conflict-free: the
-// row reads (16 lanes, 16 rows, one chunk) and the transposing reads (two 16-lane groups, 4
-// rows, 4 adjacent chunks) each find distinct bank groups.
-__device__ __forceinline__ int swz64(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+// Chunk position of a staged row's 16-byte chunk c (bf16): c ^ swz<D>(r). With 64 four-byte
+// banks this keeps every read of the kernel conflict-free: the row reads (16 lanes, 16 rows,
+// one chunk) and the transposing reads (two 16-lane groups, 4 rows, 4 adjacent chunks) each
+// find distinct bank groups, which a row pad gives only at the price of pad bytes in every
+// load. d = 128 (a row fills the banks once): row bits 0-1 << 2 | row bits 2-3; d = 64 (two
+// rows per bank line): row bit 1 << 2 | row bits 2-3.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
 
 template <int D, bool kPaged, bool kFp8 = false, bool kV8 = false>
 struct Tile {
-    // d = 64 (bf16): unpadded rows with their 16 B chunks swizzled (swz64), so that a stage
-    // takes 16 KiB and two workgroups fit the LDS of one CU
-    static constexpr bool kSwz = D == 64 && !kFp8;
+    // bf16: unpadded rows with their 16 B chunks swizzled (swz), so that a stage holds only
+    // the rows' bytes (d = 64: 16 KiB, two workgroups per CU; d = 128: 32 KiB, 4 loads of
+    // 1 KiB per wave and tile)
+    static constexpr bool kSwz = !kFp8;
     // K element bytes (fp8 e4m3 K: 1); the 16 B pad keeps a 16 B read of 16 rows in 16
     // distinct bank groups for both row lengths
     static constexpr int kKElem = kFp8 ? 1 : 2;
@@ -180,7 +186,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     using T = Tile<D, kPaged, kFp8, kV8>;
     // LDS operand reads kept in flight: fewer for the dense d = 64 instance, whose two
     // workgroups per CU leave a wave 128 registers
-    constexpr int kAh = T::kSwz && kMode == kModeDense ? 2 : kAhead;
+    constexpr int kAh = D == 64 && T::kSwz && kMode == kModeDense ? 2 : kAhead;
     constexpr int kKTile = kBc * D * T::kKElem, kVTile = kBc * D * T::kVElem;  // HBM bytes of a tile
     const uint16_t* __restrict__ q = a.q;
     const uint16_t* __restrict__ k = a.k;
@@ -313,13 +319,13 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
             const int slot = 1024 * (cc - dma_pg[i] * cpp) + 16 * lane;
             const int row = slot / row_b;
             int col = slot - row * row_b;
-            if constexpr (T::kSwz) col = 16 * ((col >> 4) ^ swz64(row));  // the chunk stored here
+            if constexpr (T::kSwz) col = 16 * ((col >> 4) ^ swz<D>(row));  // the chunk stored here
             dma_src[i] = row < kPageTok && col < D * 2 ? unsigned(row * D * 2 + col) : kPadOffset;
         } else {
             const int slot = 1024 * cc + 16 * lane;
             const int row = slot / row_b;
             int col = slot - row * row_b;
-            if constexpr (T::kSwz) col = 16 * ((col >> 4) ^ swz64(row));  // the chunk stored here
+            if constexpr (T::kSwz) col = 16 * ((col >> 4) ^ swz<D>(row));  // the chunk stored here
             const int rb = is_k ? D * T::kKElem : D * T::kVElem;  // HBM row bytes
             dma_src[i] = (col < rb ? unsigned(row * rb + col) : kPadOffset) +
                          unsigned(kSparse ? 0 : (is_k ? 3 * kKTile : 2 * kVTile));
@@ -486,11 +492,11 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     static_assert(!kPaged || T::kKStage + 2 * T::kKPage + 2 * D < 65536, "K offsets fit the immediate");
     static_assert(T::kVStage + 32 * T::kVRow + 20 * T::kVRow + 2 * D < 65536,
                   "V offsets fit the immediate");
-    // d = 64: swizzled rows, so the lane's column offset differs per 16-byte chunk. Every
-    // read takes a per-lane base for its chunk (K: one per 16 head dimensions; V: one per
-    // head-dimension block and row half) plus the stage offset as an immediate (two stages of
-    // K and V take 64 KiB, so one base per read reaches them all). The stage addresses below
-    // are then plain offsets from kz0 / vz0.
+    // bf16 (swizzled rows): the lane's column offset differs per 16-byte chunk. Every read
+    // takes a per-lane base for its chunk (K: one per 16 head dimensions; V: one per
+    // head-dimension block and row half) plus the stage offset as an immediate (the four K
+    // stages, and the four V stages, span at most 64 KiB, so one base per read reaches them
+    // all). The stage addresses below are then plain offsets from kz0 / vz0.
     const lds_cptr kz0 = lds, vz0 = lds + T::kVBase;
     lds_cptr base_kk[T::kSwz ? D / 16 : 1];
     lds_cptr base_vv[T::kSwz ? D / 32 : 1][2];
@@ -498,7 +504,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         const int rk = kappa(l32);  // the lane's K row in a stage (paged pages are 16 whole rows)
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            base_kk[kk] = lds + rk * T::kKRow + 16 * ((2 * kk + hh) ^ swz64(rk));
+            base_kk[kk] = lds + rk * T::kKRow + 16 * ((2 * kk + hh) ^ swz<D>(rk));
             asm volatile("" : "+v"(base_kk[kk]));
         }
 #pragma unroll
@@ -507,7 +513,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
             for (int h2 = 0; h2 < 2; ++h2) {
                 const int rv = 8 * (lane >> 5) + ((lane & 15) >> 2) + 4 * h2;
                 const int c = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-                base_vv[db][h2] = lds + T::kVBase + rv * T::kVRow + 16 * (c ^ swz64(rv)) + 8 * (lane & 1);
+                base_vv[db][h2] = lds + T::kVBase + rv * T::kVRow + 16 * (c ^ swz<D>(rv)) + 8 * (lane & 1);
                 asm volatile("" : "+v"(base_vv[db][h2]));
             }
     }
@@ -1119,7 +1125,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
 // LDS and it fits 128 registers a wave); one otherwise (the paged and block-sparse d = 64
 // instances would spill at 128 registers).
 template <int D, int kMode>
-constexpr int kWgPerCu = Tile<D, false>::kSwz && kMode == kModeDense ? 2 : 1;
+constexpr int kWgPerCu = D == 64 && Tile<D, false>::kSwz && kMode == kModeDense ? 2 : 1;
 
 // (the second bound is the waves per SIMD the register budget must allow)
 template <int D, int kMode, bool kStats>
