@@ -45,6 +45,9 @@ CASES = [
     (1, 2, 1, 20, 64, True),       # a single, partial query chunk
     (1, 1, 1, 33, 128, False),     # one row past a whole chunk
     (1, 3, 3, 700, 128, True),     # a walk that is not a whole number of ring rounds
+    (1, 16, 2, 300, 128, True),    # GQA 8:1: the dK/dV walk crosses seven query heads
+    (1, 16, 1, 200, 64, False),    # GQA 16:1
+    (1, 8, 1, 20, 128, True),      # one chunk per query head: a new head at every chunk
 ]
 
 
