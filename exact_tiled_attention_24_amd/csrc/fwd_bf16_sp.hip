@@ -616,23 +616,24 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         constexpr int hk = (H8 + 1) & 7, hv = (H8 + 7) & 7;
         return Bases{k_at(hk >> 1, hk & 1), v_at(hv >> 1, hv & 1)};
     };
-    // MFMA operand of slot `sl`: even slots are the S^T MFMAs (K, head dimensions
-    // 16 (sl/2) ..), odd slots the O MFMAs (V^T, key group t, head-dimension block db).
+    // MFMA operand of slot `sl`: the first D / 16 slots are the S^T MFMAs (K, head
+    // dimensions 16 sl ..), the others the O MFMAs (V^T, key group t, head-dimension block db).
     auto frag = [&](const Bases& b, int sl) -> bf16x8 {
-        const int i = sl >> 1;
-        if ((sl & 1) == 0) return kfrag(b.k, i);
+        if (sl < D / 16) return kfrag(b.k, sl);
+        const int i = sl - D / 16;
         return vfrag(b.v, i / (D / 32), i % (D / 32));
     };
-    // One pipeline step. Its MFMAs are O^T += V^T P^T of half tile hi-1 (probabilities
-    // pk_prev) and S^T of half tile hi+1 (into s_next), taken alternately so consecutive MFMAs
-    // are independent; beside them runs the softmax of half tile hi (s_cur -> pk_cur). The
+    // One pipeline step. Its MFMAs are S^T of half tile hi+1 (into s_next) and then O^T +=
+    // V^T P^T of half tile hi-1 (probabilities pk_prev), so that the next step's first reads
+    // of s_next come eight products after its last one (back-to-back dependent products run
+    // at full rate); beside them runs the softmax of half tile hi (s_cur -> pk_cur). The
     // step is written as kSlots slots, each one LDS operand read (kAh slots ahead), one
     // MFMA and a slice of the softmax, with a scheduling barrier after every slot, so the
     // instruction order is the one written here. `fr` holds on entry the operands of this
     // step's first kAh slots and on exit those of the next step's (read in this step's
     // last slots, so the next step starts without waiting, even across a barrier: its
     // operands were staged before the previous barrier).
-    // (with_pv false: half tile 0, whose step has no O update; its odd slots stay empty.)
+    // (with_pv false: half tile 0, whose step has no O update; its O slots stay empty.)
     // with_dma: this step (the first of tile j = hi / 2) also issues the loads of K of tile
     // j + 3 and V of tile j + 2 (one DMA per odd slot).
     //
@@ -769,14 +770,14 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
 #pragma unroll
         for (int sl = 0; sl < kSlots; ++sl) {
             if (sl + kAh < kSlots) {
-                if (kPV || ((sl + kAh) & 1) == 0) cur[sl + kAh] = frag(b_cur, sl + kAh);
+                if (kPV || (sl + kAh) < kS) cur[sl + kAh] = frag(b_cur, sl + kAh);
             } else {
                 fr[sl + kAh - kSlots] = frag(b_next, sl + kAh - kSlots);
             }
-            if ((sl & 1) == 0) {
-                s_next = mfma_32x32x16(cur[sl], qf[kFp8 ? 0 : sl >> 1], s_next);
+            if (sl < kS) {
+                s_next = mfma_32x32x16(cur[sl], qf[kFp8 ? 0 : sl], s_next);
             } else if (kPV) {
-                const int i = sl >> 1;
+                const int i = sl - kS;
                 const int t = i / (D / 32), db = i % (D / 32);
                 acc_o[db] = mfma_32x32x16(cur[sl], __builtin_bit_cast(bf16x8, pk_prev[t]), acc_o[db]);
             }
@@ -999,7 +1000,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
             for (int c = 0; c < D / 64; ++c) kq[c] = kfrag8(b0.k, c);
         } else {
 #pragma unroll
-            for (int sl = 0; sl < kAh; ++sl) fr[sl] = (sl & 1) ? bf16x8{} : frag(b0, sl);
+            for (int sl = 0; sl < kAh; ++sl) fr[sl] = sl >= D / 16 ? bf16x8{} : frag(b0, sl);
         }
     }
     advance(3);
