@@ -432,12 +432,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     oq.init(lane, kQ0);
     odo.init(lane, kDo0);
 
-    // products of slot sl of a step: even slots S / dP of the next chunk (S when sl % 4 == 0,
-    // head dims 16 (sl / 4) ..), odd slots dV / dK of the previous chunk (query group t,
-    // head-dim block db)
+    // products of slot sl of a step: the first half S / dP of the next chunk (S in even
+    // slots, head dims 16 (sl / 2) ..), the second half dV / dK of the previous chunk (query
+    // group t, head-dim block db), so that the next step's first reads of the scores come
+    // kSlots / 2 products after the last one that wrote them (products that depend on the one
+    // just before run at full rate)
     constexpr int kSlots = 2 * (D / 8);  // 16 next-chunk products + 16 previous-chunk ones (D = 128)
     constexpr int kPrev = D / 8;         // previous-chunk products: 2 (t) x D / 32 (db) x 2 (dV, dK)
-    static_assert(kSlots == 2 * kPrev, "one next-chunk and one previous-chunk product per slot pair");
+    static_assert(kSlots == 2 * kPrev, "as many previous-chunk products as next-chunk ones");
     constexpr int kSpread = kSlots / 16; // slots per score of the vector work
 
     // One step: chunk it's vector work (its scores sc_c, dp_c -> operands pb_c, sb_c), the next
@@ -465,9 +467,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
             return *reinterpret_cast<const lds_f32x4*>(base + 4 * row);
         };
         auto operand = [&](int sl) -> bf16x8 {
-            const int i = sl >> 1;
             // next chunk: Q rows (S) and dO rows (dP); previous chunk: dO^T (dV) and Q^T (dK)
-            if ((sl & 1) == 0) return ((i & 1) ? odo : oq).rows(lds, Pn * kT, i >> 1);
+            const bool nx = sl < kSlots / 2;
+            const int i = nx ? sl : sl - kSlots / 2;
+            if (nx) return ((i & 1) ? odo : oq).rows(lds, Pn * kT, i >> 1);
             const int t = i / (kPrev / 2), db = (i >> 1) % (D / 32);
             return ((i & 1) ? oq : odo).trans(lds, Pp * kT, t, db);
         };
@@ -525,9 +528,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int sl = 0; sl < kSlots; ++sl) {
-            // A(r)'s scores, taken at the slot's start. Slot 0 reads what the last products of
-            // the step before wrote (dP at its slot 2 kSlots - 2): the wait states give them the
-            // time that a matrix instruction's result needs before a vector read.
+            // A(r)'s scores, taken at the slot's start. Slot 0 reads what the step before wrote
+            // in its slots kSlots / 2 - 2 and kSlots / 2 - 1, kSlots / 2 products earlier; the
+            // wait states are a margin beyond the time a matrix instruction's result needs
+            // before a vector read.
             const bool has_a = kSpread == 1 || (sl & 1) == 0;
             const int r = sl / kSpread;
             if (sl == 0) asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
@@ -538,8 +542,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
                 asm volatile("" : "+v"(sr), "+v"(dpr));
             }
             if (sl + kA < kSlots) op[sl + kA] = operand(sl + kA);
-            const int i = sl >> 1;
-            if ((sl & 1) == 0) {
+            const int i = sl < kSlots / 2 ? sl : sl - kSlots / 2;
+            if (sl < kSlots / 2) {
                 f32x16& acc = (i & 1) ? dp_n : sc_n;
                 const bf16x8 b = (i & 1) ? vf[i >> 1] : kf[i >> 1];
                 if (i < 2) mma_v0(acc, op[sl], b);
