@@ -738,12 +738,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     };
     const lds_cptr lds = (lds_cptr)smem;
 
-    // slots of a step: groups of three, (S^T, dP^T) of the next chunk for head dims 16 k ..,
-    // then dQ^T product k of the previous chunk (key group t = k / (D / 32), head-dim block db)
+    // slots of a step: first the (S^T, dP^T) pairs of the next chunk (head dims 16 k ..),
+    // then the dQ^T products k of the previous chunk (key group t = k / (D / 32), head-dim
+    // block db), so that the next step's first reads of the scores come kDq products after
+    // the last one that wrote them (products that depend on the one just before run at full
+    // rate)
     constexpr int kNext = D / 16;                // S^T / dP^T pairs
     constexpr int kDq = 2 * (D / 32);            // dQ^T products: 2 (t) x D / 32 (db)
     static_assert(kNext == kDq, "one dQ product per (S, dP) pair");
     constexpr int kSlots = 3 * kNext;
+    // product k and kind m (0: S^T, 1: dP^T, 2: dQ^T) of slot sl
+    auto slot_k = [](int sl) { return sl < 2 * kNext ? sl >> 1 : sl - 2 * kNext; };
+    auto slot_m = [](int sl) { return sl < 2 * kNext ? (sl & 1) : 2; };
     // vector work of score r in slot slot_of(r): spread over the step
     auto slot_of = [](int r) { return (r * kSlots) / 16; };
     static_assert((15 * kSlots) / 16 < kSlots, "every score has its slot");
@@ -765,7 +771,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
             for (int r = 0; r < 16; ++r) sc_c[r] = kc0 + acc_row(r, h) <= query ? sc_c[r] : -INFINITY;
         }
         auto operand = [&](int sl) -> bf16x8 {
-            const int k = sl / 3, m = sl % 3;
+            const int k = slot_k(sl), m = slot_m(sl);
             if (m == 0) return rows_frag<D>(tnk, lane, k);
             if (m == 1) return rows_frag<D>(tnv, lane, k);
             return trans_frag<D>(tpk, lane, k / (D / 32), k % (D / 32));
@@ -780,7 +786,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int sl = 0; sl < kSlots; ++sl) {
             if (sl + kA < kSlots) op[sl + kA] = operand(sl + kA);
-            const int k = sl / 3, m = sl % 3;
+            const int k = slot_k(sl), m = slot_m(sl);
             if (m == 0) sc_n = mfma_32x32x16(op[sl], qf[k], sc_n);
             else if (m == 1) dp_n = mfma_32x32x16(op[sl], dof[k], dp_n);
             else acc_dq[k % (D / 32)] = mfma_32x32x16(op[sl], sb_p[k / (D / 32)], acc_dq[k % (D / 32)]);
