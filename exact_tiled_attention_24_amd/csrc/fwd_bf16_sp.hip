@@ -616,17 +616,23 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         constexpr int hk = (H8 + 1) & 7, hv = (H8 + 7) & 7;
         return Bases{k_at(hk >> 1, hk & 1), v_at(hv >> 1, hv & 1)};
     };
-    // MFMA operand of slot `sl`: the first D / 16 slots are the S^T MFMAs (K, head
-    // dimensions 16 sl ..), the others the O MFMAs (V^T, key group t, head-dimension block db).
+    // Slot order of a step: d = 128 takes the D / 16 S^T MFMAs first (K, head dimensions
+    // 16 i ..), then the O MFMAs (V^T, key group t, head-dimension block db); d = 64, whose
+    // 128 registers the first order overruns, alternates them (S^T in the even slots).
+    constexpr bool kSFirst = D == 128;
+    auto slot_is_s = [](int sl) { return kSFirst ? sl < D / 16 : (sl & 1) == 0; };
+    auto slot_i = [](int sl) { return kSFirst ? (sl < D / 16 ? sl : sl - D / 16) : sl >> 1; };
+    // MFMA operand of slot `sl`
     auto frag = [&](const Bases& b, int sl) -> bf16x8 {
-        if (sl < D / 16) return kfrag(b.k, sl);
-        const int i = sl - D / 16;
+        const int i = slot_i(sl);
+        if (slot_is_s(sl)) return kfrag(b.k, i);
         return vfrag(b.v, i / (D / 32), i % (D / 32));
     };
-    // One pipeline step. Its MFMAs are S^T of half tile hi+1 (into s_next) and then O^T +=
-    // V^T P^T of half tile hi-1 (probabilities pk_prev), so that the next step's first reads
-    // of s_next come eight products after its last one (back-to-back dependent products run
-    // at full rate); beside them runs the softmax of half tile hi (s_cur -> pk_cur). The
+    // One pipeline step. Its MFMAs are S^T of half tile hi+1 (into s_next) and O^T += V^T P^T
+    // of half tile hi-1 (probabilities pk_prev); at d = 128 all S^T ones first, so that the
+    // next step's first reads of s_next come eight products after its last one (back-to-back
+    // dependent products run at full rate); beside them runs the softmax of half tile hi
+    // (s_cur -> pk_cur). The
     // step is written as kSlots slots, each one LDS operand read (kAh slots ahead), one
     // MFMA and a slice of the softmax, with a scheduling barrier after every slot, so the
     // instruction order is the one written here. `fr` holds on entry the operands of this
@@ -770,14 +776,14 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
 #pragma unroll
         for (int sl = 0; sl < kSlots; ++sl) {
             if (sl + kAh < kSlots) {
-                if (kPV || (sl + kAh) < kS) cur[sl + kAh] = frag(b_cur, sl + kAh);
+                if (kPV || slot_is_s(sl + kAh)) cur[sl + kAh] = frag(b_cur, sl + kAh);
             } else {
                 fr[sl + kAh - kSlots] = frag(b_next, sl + kAh - kSlots);
             }
-            if (sl < kS) {
-                s_next = mfma_32x32x16(cur[sl], qf[kFp8 ? 0 : sl], s_next);
+            if (slot_is_s(sl)) {
+                s_next = mfma_32x32x16(cur[sl], qf[kFp8 ? 0 : slot_i(sl)], s_next);
             } else if (kPV) {
-                const int i = sl - kS;
+                const int i = slot_i(sl);
                 const int t = i / (D / 32), db = i % (D / 32);
                 acc_o[db] = mfma_32x32x16(cur[sl], __builtin_bit_cast(bf16x8, pk_prev[t]), acc_o[db]);
             }
@@ -1000,7 +1006,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
             for (int c = 0; c < D / 64; ++c) kq[c] = kfrag8(b0.k, c);
         } else {
 #pragma unroll
-            for (int sl = 0; sl < kAh; ++sl) fr[sl] = sl >= D / 16 ? bf16x8{} : frag(b0, sl);
+            for (int sl = 0; sl < kAh; ++sl) fr[sl] = slot_is_s(sl) ? frag(b0, sl) : bf16x8{};
         }
     }
     advance(3);
