@@ -266,16 +266,13 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
             const u32x4 hi = *reinterpret_cast<const u32x4*>(src + 64 * c + 16);
             qf8[c] = v8i32{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         }
-#pragma unroll
-        for (int c = 0; c < D / 64; ++c) asm volatile("" : "+v"(qf8[c]));
     } else {
         const uint16_t* src = qh + (size_t)min_(qrow, N - 1) * D + 8 * hh;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
             qf[kk] = *reinterpret_cast<const bf16x8*>(src + 16 * kk);
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(qf[kk]));
     }
+    // (the Q loads are waited for with the first tiles' below, so the two latencies overlap)
 
     f32x16 acc_o[D / 32];
 #pragma unroll
@@ -830,6 +827,13 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     dma_tile(-1, 3);  // K2, V1
     wait_dma_all();
     barrier_lds();
+    if constexpr (kFp8) {
+#pragma unroll
+        for (int c = 0; c < D / 64; ++c) asm volatile("" : "+v"(qf8[c]));
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(qf[kk]));
+    }
     if constexpr (kV8) {
     // ---- e4m3 V: one step per 64-key tile. Step j computes S^T of tile j + 1 (four fp8
     // MFMAs), the softmax of tile j (both halves against one exponent reference, so that the
@@ -1081,18 +1085,40 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
             for (int i = 0; i < D / 32; ++i) acc_o[i] = f32x16{};
         }
     }
-    if (qrow < nq) {
+    {
+        // O / l in bf16, through LDS: the wave writes its 32 rows row-major into a block of its
+        // own in the stage area (idle now: no load in flight, no wave reading it), then stores
+        // whole rows, 16 bytes a lane, so that one store instruction fills 1 KiB of O (the
+        // accumulator layout alone gives a lane 8 bytes in each of 16 places). A row's 16-byte
+        // chunk c sits at c ^ (r mod 16) (d = 128) or c ^ (r / 2 mod 8) (d = 64): conflict-free
+        // in both directions.
+        constexpr int kRowB = 2 * D, kCh = kRowB / 16, kRowsPer = 1024 / kRowB;
+        typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+        typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+        typedef __attribute__((address_space(3))) unsigned char* lds_ptr;
+        lds_ptr const ob = (lds_ptr)smem + wave * 32 * kRowB;
+        auto osw = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t* dst = o + qoff + (size_t)qrow * D;
+        const int sw_w = osw(l32);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int d = 32 * db + 8 * g + 4 * hh;
                 u32x2 w = {pack_bf16x2(acc_o[db][4 * g] * inv, acc_o[db][4 * g + 1] * inv),
                            pack_bf16x2(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv)};
-                *reinterpret_cast<u32x2*>(dst + d) = w;
+                *(lds_u32x2*)(ob + l32 * kRowB + 16 * ((4 * db + g) ^ sw_w) + 8 * hh) = w;
             }
+        // (a wave's LDS accesses complete in order: its reads below see all its lanes' writes)
+        __builtin_amdgcn_wave_barrier();
+        const int rr = lane / kCh, ch = lane % kCh;
+#pragma unroll
+        for (int i = 0; i < 32 / kRowsPer; ++i) {
+            const int r = kRowsPer * i + rr;
+            const u32x4 val = *(const lds_u32x4*)(ob + r * kRowB + 16 * (ch ^ osw(r)));
+            if (row0 + r < nq) *reinterpret_cast<u32x4*>(o + qoff + (size_t)(row0 + r) * D + 8 * ch) = val;
+        }
+    }
+    if (qrow < nq) {
         if (hh == 0) {
             const size_t ridx = (size_t)(b * Hq + h) * N + qrow;
             if (m_out) m_out[ridx] = (l_tot > 0.f) ? m_run * kLn2 : -INFINITY;
@@ -1104,10 +1130,11 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         // product overflowed. Otherwise the whole workgroup runs the item again with
         // statistics, which rewrites every output row the garbage above went to (the decision
         // must be uniform: the item's loads and barriers are shared).
-        // Each wave reports in one word of the tile area, idle at this point (no load in
-        // flight, no wave reading it); the second barrier keeps the next item's loads from
-        // overwriting the words before every wave has read them.
-        int* flags = reinterpret_cast<int*>(smem);
+        // Each wave reports in one word of the tile area past the O blocks, idle at this point
+        // (no load in flight, no wave reading it); the second barrier keeps the next item's
+        // loads from overwriting the words (and the O blocks) before every wave is done with
+        // them.
+        int* flags = reinterpret_cast<int*>(smem + kWaves * 32 * 2 * D);
         const bool bad = __any(!(l_part <= 0x1p100f));
         if ((threadIdx.x & 63) == 0) flags[wave] = bad ? 1 : 0;
         barrier_lds();
@@ -1116,6 +1143,8 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         for (int w = 0; w < kWaves; ++w) any |= flags[w];
         barrier_lds();
         if (any) return false;
+    } else {
+        barrier_lds();  // the next item's loads wait until every wave has read its O block
     }
 
     return true;
