@@ -113,6 +113,14 @@ typedef int v8i32 __attribute__((ext_vector_type(8)));
 // find distinct bank groups, which a row pad gives only at the price of pad bytes in every
 // load. d = 128 (a row fills the banks once): row bits 0-1 << 2 | row bits 2-3; d = 64 (two
 // rows per bank line): row bit 1 << 2 | row bits 2-3.
+// Chunk position of 16-byte chunk c of row r of a wave's 32-row block of Q or O: c ^ osw<D>(r).
+// Conflict-free for a 16-lane read or write of one chunk of 16 consecutive rows, and for whole
+// rows: d = 128, row bits 0-3; d = 64 (two rows per bank line), row bits 1-3.
+template <int D>
+__device__ __forceinline__ int osw(int r) {
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
 template <int D>
 __device__ __forceinline__ int swz(int r) {
     return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
@@ -145,6 +153,14 @@ struct Tile {
     static constexpr int kKChunks = kKStage / 1024;                   // 1 KiB DMA chunks
     static constexpr int kVChunks = kVStage / 1024;
     static constexpr int kDmaPerWave = (kKChunks + kVChunks + kWaves - 1) / kWaves;
+    // Dense bf16 (kLdsQ bytes of LDS): Q comes through LDS too, in whole 1 KiB loads, each
+    // wave's 32 rows in a block of kQBlock bytes: waves 0 and 1 in K stage 3, waves 2 .. 7 from
+    // V stage 3 on, past the stages' end (stage 3's K and V are first loaded after the item's
+    // first barrier)
+    static constexpr int kQBlock = 32 * D * 2;
+    static constexpr int kLdsQ = kStages * (kKStage + kVStage) + 6 * kQBlock - kVStage;
+    static_assert(kPaged || kFp8 || (2 * kQBlock == kKStage && kLdsQ <= 160 * 1024),
+                  "two Q blocks fill a K stage; the Q blocks fit");
     static_assert(kKStage % 1024 == 0 && kVStage % 1024 == 0, "stages are whole DMA chunks");
     static_assert(!kPaged || (kPageTok * kVRow) % 1024 == 0, "V pages are whole DMA chunks");
     static_assert(kStages * (kKStage + kVStage) <= 160 * 1024, "fits the LDS of one CU");
@@ -183,6 +199,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     constexpr bool kPaged = kMode == kModePaged, kSparse = kMode == kModeSparse;
     constexpr bool kV8 = kMode == kModeFp8V;              // e4m3 V, P V on the fp8 matrix cores
     constexpr bool kFp8 = kMode == kModeFp8 || kV8;       // e4m3 Q and K
+    constexpr bool kQLds = kMode == kModeDense;            // Q through LDS (see Tile)
     using T = Tile<D, kPaged, kFp8, kV8>;
     // LDS operand reads kept in flight: fewer for the dense d = 64 instance, whose two
     // workgroups per CU leave a wave 128 registers
@@ -266,7 +283,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
             const u32x4 hi = *reinterpret_cast<const u32x4*>(src + 64 * c + 16);
             qf8[c] = v8i32{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         }
-    } else {
+    } else if constexpr (!kQLds) {
         const uint16_t* src = qh + (size_t)min_(qrow, N - 1) * D + 8 * hh;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
@@ -415,10 +432,11 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     // outstanding load to LDS before each transposing read (it cannot tell the stages
     // apart); the waits here are explicit. Operations whose chunks are all K (or all V) for
     // every wave need no select.
-    auto dma_op = [&](int j, int i, int P) {  // P: the stage phase (a constant, or uniform in the e4m3-V steps)
+    auto dma_op = [&](int j, int i, int P, bool k_only = false) {  // P: the stage phase (a constant, or uniform in the e4m3-V steps)
         constexpr int kK = T::kKChunks;
         const bool all_k = kWaves * i + kWaves - 1 < kK, all_v = kWaves * i >= kK;
         const bool is_k = all_k || (!all_v && wave + kWaves * i < kK);
+        if (k_only && !is_k) return;  // (uniform per wave)
         const unsigned stage = is_k ? unsigned(((P + 3) & (kStages - 1)) * T::kKStage)
                                     : unsigned(((P + 2) & (kStages - 1)) * T::kVStage);
         if constexpr (kPaged) {
@@ -452,9 +470,9 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
                          : "memory");
         }
     };
-    auto dma_tile = [&](int j, int P) {
+    auto dma_tile = [&](int j, int P, bool k_only = false) {
 #pragma unroll
-        for (int i = 0; i < T::kDmaPerWave; ++i) dma_op(j, i, P);
+        for (int i = 0; i < T::kDmaPerWave; ++i) dma_op(j, i, P, k_only);
     };
     // LDS DMA is not tracked by the compiler's waits: wait for all but the newest tile's
     // loads (vmcnt counts this wave's vector loads in issue order), then the barrier.
@@ -818,14 +836,44 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     if constexpr (kPaged) win = page_offsets(table_entries(wb), wb);
     if constexpr (kSparse) win = tile_offsets(list_entries(wb), wb);
 
-    // ---- prologue: K0..K2 and V0, V1 staged; scores of half tile 0 ----
+    // ---- prologue: (Q,) K0..K2 and V0, V1 staged; scores of half tile 0 ----
+    lds_cptr qblk = lds;
+    if constexpr (kQLds) {
+        // the wave's 32 Q rows (8 B-operand chunks of 16 bytes a row, stored at chunk
+        // c ^ osw(r) of row r): load i fills bytes 1024 i .. 1024 i + 1023 of the block, lane l
+        // the 16 at 16 l; rows past N read zero through the descriptor's range
+        const unsigned qb_off = wave < 2 ? 3u * T::kKStage + unsigned(wave) * T::kQBlock
+                                         : unsigned(T::kVBase + 3 * T::kVStage) + unsigned(wave - 2) * T::kQBlock;
+        qblk = lds + qb_off;
+        const __amdgpu_buffer_rsrc_t rsrc_q =
+            __builtin_amdgcn_make_buffer_rsrc((void*)qh, (short)0, __builtin_amdgcn_readfirstlane(N * D * 2), kBufferDword3);
+#pragma unroll
+        for (int i = 0; i < T::kQBlock / 1024; ++i) {
+            const int slot = 1024 * i + 16 * lane;
+            const int r = slot / (2 * D), cs = (slot % (2 * D)) / 16;
+            const unsigned src = unsigned((row0 + r) * 2 * D + 16 * (cs ^ osw<D>(r)));
+            asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :
+                         : "v"(src), "s"(rsrc_q), "{m0}"(lds_addr + qb_off + 1024u * i)
+                         : "memory");
+        }
+    }
     advance(0);
-    dma_tile(-3, 1);  // K0 (and zeros for V of tile -1, in the stage V3 takes later)
+    dma_tile(-3, 1, kQLds);  // K0 (and zeros for V of tile -1, in the stage V3 takes later; not
+                             // with Q in that stage)
     advance(1);
     dma_tile(-2, 2);  // K1, V0
     advance(2);
     dma_tile(-1, 3);  // K2, V1
     wait_dma_all();
+    if constexpr (kQLds) {
+        // the wave's own loads have landed: its Q block is readable before the barrier, which
+        // also waits for these reads (K3 and V3 overwrite the blocks after it)
+        const int rq = l32;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            qf[kk] = *(const lds_bf16x8*)(qblk + rq * 2 * D + 16 * ((2 * kk + hh) ^ osw<D>(rq)));
+    }
     barrier_lds();
     if constexpr (kFp8) {
 #pragma unroll
@@ -1089,17 +1137,15 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         // O / l in bf16, through LDS: the wave writes its 32 rows row-major into a block of its
         // own in the stage area (idle now: no load in flight, no wave reading it), then stores
         // whole rows, 16 bytes a lane, so that one store instruction fills 1 KiB of O (the
-        // accumulator layout alone gives a lane 8 bytes in each of 16 places). A row's 16-byte
-        // chunk c sits at c ^ (r mod 16) (d = 128) or c ^ (r / 2 mod 8) (d = 64): conflict-free
-        // in both directions.
+        // accumulator layout alone gives a lane 8 bytes in each of 16 places). Chunk c of row r
+        // sits at c ^ osw(r).
         constexpr int kRowB = 2 * D, kCh = kRowB / 16, kRowsPer = 1024 / kRowB;
         typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
         typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
         typedef __attribute__((address_space(3))) unsigned char* lds_ptr;
         lds_ptr const ob = (lds_ptr)smem + wave * 32 * kRowB;
-        auto osw = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        const int sw_w = osw(l32);
+        const int sw_w = osw<D>(l32);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -1114,7 +1160,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
 #pragma unroll
         for (int i = 0; i < 32 / kRowsPer; ++i) {
             const int r = kRowsPer * i + rr;
-            const u32x4 val = *(const lds_u32x4*)(ob + r * kRowB + 16 * (ch ^ osw(r)));
+            const u32x4 val = *(const lds_u32x4*)(ob + r * kRowB + 16 * (ch ^ osw<D>(r)));
             if (row0 + r < nq) *reinterpret_cast<u32x4*>(o + qoff + (size_t)(row0 + r) * D + 8 * ch) = val;
         }
     }
@@ -1167,7 +1213,8 @@ constexpr int kWgPerCu = D == 64 && Tile<D, false>::kSwz && kMode == kModeDense 
 template <int D, int kMode, bool kStats>
 __global__ __launch_bounds__(kThreads, (kWgPerCu<D, kMode> * kWaves / 4)) void fwd_bf16_sp_kernel(FwdArgs a) {
     using T = Tile<D, kMode == kModePaged, kMode == kModeFp8 || kMode == kModeFp8V, kMode == kModeFp8V>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kStages * (T::kKStage + T::kVStage)];
+    __shared__ __attribute__((aligned(16)))
+    unsigned char smem[kMode == kModeDense ? T::kLdsQ : kStages * (T::kKStage + T::kVStage)];
 
     const int per_unit = a.nqb * (a.Hq / a.Hkv);  // items of one KV group
     const int n_kvg = a.B * a.Hkv;
@@ -1187,9 +1234,17 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, kMode> * kWaves / 4)) void f
     }
     // Two workgroups per CU: local ids j and j + W / 2 are taken to share a CU, so the snake
     // runs over W / 2 units whose rounds alternate between the two (a heavy item on one of
-    // them, the matching light one on the other).
+    // them, the matching light one on the other). The first of the two to start (the lower
+    // id) takes the heavy item: the waves that started first win the CU's instruction issue,
+    // so the heavy item runs at the pace of a workgroup alone and the light one in the gaps.
+    // For that the XCD's share, when it is whole KV groups, is walked by query block first
+    // (all its groups' heaviest blocks, then the next), so that the first W / 2 items are the
+    // heavy half.
     constexpr int kPer = kWgPerCu<D, kMode>;
     const int Wu = W / kPer, u = j % Wu, sub = j / Wu;
+    const int G = a.Hq / a.Hkv;
+    const bool by_block = kPer == 2 && seg0 % per_unit == 0 && seg_n % per_unit == 0;
+    const int seg_units = seg_n / per_unit;
     for (int r = 0; r * W < seg_n; ++r) {
         const int rr = kPer * r + sub;  // the unit's round
         const int local = rr * Wu + ((rr & 1) ? Wu - 1 - u : u);
@@ -1198,6 +1253,11 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, kMode> * kWaves / 4)) void f
         if constexpr (kMode != kModeDense) {
             const int g = local / per_unit;
             item = (xcd + kXcds * g) * per_unit + (local - g * per_unit);
+        } else if (by_block) {
+            // local = (t * units + k) * G + hg: block rank t of unit k, head hg of the group
+            const int t = local / (seg_units * G), rem = local - t * seg_units * G;
+            const int k = rem / G, hg = rem - k * G;
+            item = seg0 + k * per_unit + t * G + hg;
         } else {
             item = seg0 + local;
         }
