@@ -36,7 +36,9 @@
 //    writes the output. No second launch.
 //  * The completion word holds a tag of the call in its high bits and the arrivals in the low
 //    bits: an arrival that finds another tag counts as the first, so the words need no
-//    clearing between calls and the workspace contents on entry do not matter.
+//    clearing between calls and the workspace contents on entry do not matter. The last
+//    arrival leaves the word at zero, so that a call replayed with the same tag (a captured
+//    graph's launch) also starts from a clean count.
 #include <atomic>
 #include <mutex>
 #include <random>
@@ -91,7 +93,8 @@ struct DecodeArgs {
     float scale_log2;
 };
 
-// Counts one arrival on a completion word and reports whether it was the n-th of this call.
+// Counts one arrival on a completion word and reports whether it was the n-th of this call
+// (the n-th clears the word: zero counts as no arrival for any tag).
 // Vector (global) atomics at device scope, relaxed. The caller orders the partials around it
 // without fences: every wave waits for its partial stores to complete (s_waitcnt vmcnt(0))
 // before the barrier behind which one thread arrives, and the last arriver's loads of the
@@ -101,7 +104,7 @@ __device__ bool arrive(unsigned long long* word, unsigned long long tag, int n) 
     unsigned long long old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (;;) {
         const unsigned long long cnt = (old >> kCountBits) == tag ? (old & kCountMask) : 0;
-        const unsigned long long next = (tag << kCountBits) | (cnt + 1);
+        const unsigned long long next = cnt + 1 == (unsigned long long)n ? 0ull : (tag << kCountBits) | (cnt + 1);
         if (__hip_atomic_compare_exchange_strong(word, &old, next, __ATOMIC_RELAXED,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
             return cnt + 1 == (unsigned long long)n;
