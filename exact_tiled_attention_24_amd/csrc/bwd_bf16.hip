@@ -203,6 +203,41 @@ __device__ __forceinline__ bf16x8 acc_operand(const float (&x)[16], int t) {
     return __builtin_bit_cast(bf16x8, w);
 }
 
+// A wave's 32 output rows, from 32 x 32 accumulators (lane (r, h), register 4 g + i of block db:
+// row r, column 32 db + 8 g + 4 h + i) times s, rounded to bf16 and stored whole through LDS:
+// the wave writes them row-major into its own block blk (32 rows of 2 D bytes; chunk c of row r
+// at c ^ (r mod 16), d = 128, or c ^ (r / 2 mod 8), d = 64: conflict-free both ways), reads
+// back 16 contiguous bytes a lane and stores rows 0 .. n_valid - 1 at dst, so that one store
+// instruction covers 1 KiB of the output (the accumulator layout gives a lane 8 bytes in each
+// of 16 places).
+template <int D>
+__device__ __forceinline__ void store_rows(const f32x16 (&acc)[D / 32], float s,
+                                           __attribute__((address_space(3))) unsigned char* blk,
+                                           uint16_t* dst, int n_valid, int lane) {
+    typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+    typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
+    constexpr int kRowB = 2 * D, kCh = kRowB / 16, kRowsPer = 1024 / kRowB;
+    auto sw = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+    const int r0 = lane & 31, h = lane >> 5, s0 = sw(r0);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            u32x2 w = {pack_bf16x2(s * acc[db][4 * g], s * acc[db][4 * g + 1]),
+                       pack_bf16x2(s * acc[db][4 * g + 2], s * acc[db][4 * g + 3])};
+            *(lds_u32x2*)(blk + r0 * kRowB + 16 * ((4 * db + g) ^ s0) + 8 * h) = w;
+        }
+    // (a wave's LDS accesses complete in order: its reads below see all its lanes' writes)
+    __builtin_amdgcn_wave_barrier();
+    const int rr = lane / kCh, ch = lane % kCh;
+#pragma unroll
+    for (int i = 0; i < 32 / kRowsPer; ++i) {
+        const int r = kRowsPer * i + rr;
+        const u32x4 v = *(lds_u32x4*)(blk + r * kRowB + 16 * (ch ^ sw(r)));
+        if (r < n_valid) *reinterpret_cast<u32x4*>(dst + (size_t)r * D + 8 * ch) = v;
+    }
+}
+
 // Workgroups are dealt to the 8 XCDs round robin by linear id. xcd_position maps the linear
 // id to a position in (head, block) order so that each XCD receives a contiguous run of
 // positions: the ~32 workgroups one XCD runs at a time then share one or two heads, whose
@@ -643,22 +678,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) asm volatile("" : "+a"(acc_dv[db]), "+a"(acc_dk[db]));
     }
-    // accumulator register r of block db: head dimension 32 db + 8 (r / 4) + 4 h + r % 4
-    if (key < N) {
-        uint16_t* pk = a.dk + kvoff + (size_t)key * D;
-        uint16_t* pv = a.dv + kvoff + (size_t)key * D;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int d0 = 32 * db + 8 * gq + 4 * h;
-                u32x2 wk = {pack_bf16x2(a.scale * acc_dk[db][4 * gq], a.scale * acc_dk[db][4 * gq + 1]),
-                            pack_bf16x2(a.scale * acc_dk[db][4 * gq + 2], a.scale * acc_dk[db][4 * gq + 3])};
-                u32x2 wv = {pack_bf16x2(acc_dv[db][4 * gq], acc_dv[db][4 * gq + 1]),
-                            pack_bf16x2(acc_dv[db][4 * gq + 2], acc_dv[db][4 * gq + 3])};
-                *reinterpret_cast<u32x2*>(pk + d0) = wk;
-                *reinterpret_cast<u32x2*>(pv + d0) = wv;
-            }
+    // dK and dV rows through LDS (every wave is done with the ring after the barrier): the
+    // wave's dK block, then its dV block
+    __syncthreads();
+    {
+        typedef __attribute__((address_space(3))) unsigned char* lds_ptr;
+        lds_ptr const blk = (lds_ptr)smem + wave * 2 * 32 * 2 * D;
+        store_rows<D>(acc_dk, a.scale, blk, a.dk + kvoff + (size_t)kw0 * D, N - kw0, lane);
+        store_rows<D>(acc_dv, 1.f, blk + 32 * 2 * D, a.dv + kvoff + (size_t)kw0 * D, N - kw0, lane);
     }
 }
 
@@ -869,17 +896,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still be writing LDS
     }
-    if (query < N) {
-        uint16_t* pq = a.dq + (qoff + query) * D;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int d0 = 32 * db + 8 * gq + 4 * h;
-                u32x2 w = {pack_bf16x2(a.scale * acc_dq[db][4 * gq], a.scale * acc_dq[db][4 * gq + 1]),
-                           pack_bf16x2(a.scale * acc_dq[db][4 * gq + 2], a.scale * acc_dq[db][4 * gq + 3])};
-                *reinterpret_cast<u32x2*>(pq + d0) = w;
-            }
+    // dQ rows through LDS (every wave is done with the ring after the barrier)
+    __syncthreads();
+    {
+        typedef __attribute__((address_space(3))) unsigned char* lds_ptr;
+        store_rows<D>(acc_dq, a.scale, (lds_ptr)smem + wave * 32 * 2 * D, a.dq + (qoff + qw0) * D,
+                      N - qw0, lane);
     }
 }
 
