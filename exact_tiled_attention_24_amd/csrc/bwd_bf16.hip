@@ -349,7 +349,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     // reaches from one lane offset
     constexpr int kQ0 = kRing * kLdB, kDo0 = kQ0 + kRing * kT;
     auto ld_at = [](int st) { return st * kLdB; };
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kDo0 + kRing * kT];
+    // The workgroup's K and V rows come in through LDS (whole 1 KiB loads), each wave's 32 K
+    // rows and 32 V rows in blocks of kKV bytes past the ring; where the LDS runs out, the
+    // last block sits in stage 4's Q rows, first loaded after the prologue's barrier.
+    constexpr int kKV = 32 * 2 * D, kRingEnd = kDo0 + kRing * kT;
+    constexpr int kKVInRing = kRingEnd + 8 * kKV <= 160 * 1024 ? 0 : 1;
+    static_assert(kKVInRing == 0 || (kKV == kT && kRing > kAhead + 1), "a block fits stage 4's Q rows");
+    auto kv_block = [](int blk) {  // blocks 0 .. 3: K of waves 0 .. 3; 4 .. 7: V
+        return blk < 8 - kKVInRing ? kRingEnd + blk * kKV : kQ0 + kAhead * kT;
+    };
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kRingEnd + (8 - kKVInRing) * kKV];
 
     const int N = a.N, G = a.Hq / a.Hkv;
     const int pos = xcd_position(gridDim.x * gridDim.y);
@@ -363,15 +372,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int key = kb0 + 32 * wave + (lane & 31);  // this lane's key (accumulator column)
     const int kw0 = kb0 + 32 * wave;
 
-    // K and V of the lane's key as B operands (K-dim = head dimension 16 kk + 8 h ..)
+    // K and V of the lane's key as B operands (K-dim = head dimension 16 kk + 8 h ..), read
+    // from the wave's LDS blocks after the prologue's wait: chunk c of row r stored at chunk
+    // c ^ (r mod 16) (d = 128) or c ^ (r / 2 mod 8) (d = 64); rows past N read zero
     const size_t kvoff = (size_t)bk * N * D;
     bf16x8 kf[D / 16], vf[D / 16];
+    auto kv_sw = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
     {
-        const int kr = min_(key, N - 1);
+        const unsigned base = (unsigned)(size_t)(lds_cptr)smem;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + kvoff), (short)0, N * D * 2, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + kvoff), (short)0, N * D * 2, kRsrcWord3);
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            kf[kk] = *reinterpret_cast<const bf16x8*>(a.k + kvoff + (size_t)kr * D + 16 * kk + 8 * h);
-            vf[kk] = *reinterpret_cast<const bf16x8*>(a.v + kvoff + (size_t)kr * D + 16 * kk + 8 * h);
+        for (int i = 0; i < kKV / 1024; ++i) {
+            const int slot = 1024 * i + 16 * lane;
+            const int r = slot / (2 * D), cs = (slot % (2 * D)) / 16;
+            const unsigned src = unsigned((kw0 + r) * 2 * D + 16 * (cs ^ kv_sw(r)));
+            asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :
+                         : "v"(src), "s"(rk), "{m0}"(base + (unsigned)kv_block(wave) + 1024u * i)
+                         : "memory");
+            asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :
+                         : "v"(src), "s"(rv), "{m0}"(base + (unsigned)kv_block(4 + wave) + 1024u * i)
+                         : "memory");
         }
     }
     f32x16 acc_dk[D / 32], acc_dv[D / 32];
@@ -629,6 +654,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < kAhead; ++c) issue_all(next_load(c));
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kAhead - 1) * kOps) : "memory");
+        {
+            // the wave's K and V blocks have landed (issued before the chunks waited for)
+            const int r0 = lane & 31;
+            const lds_cptr bk_ = (lds_cptr)smem + kv_block(wave) + r0 * 2 * D;
+            const lds_cptr bv_ = (lds_cptr)smem + kv_block(4 + wave) + r0 * 2 * D;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                kf[kk] = *(const lds_bf16x8*)(bk_ + 16 * ((2 * kk + h) ^ kv_sw(r0)));
+                vf[kk] = *(const lds_bf16x8*)(bv_ + 16 * ((2 * kk + h) ^ kv_sw(r0)));
+            }
+        }
         __syncthreads();
         f32x16 sa{}, da{}, sb2{}, db2{};
         const bf16x8 zero8 = {};
@@ -678,8 +714,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) asm volatile("" : "+a"(acc_dv[db]), "+a"(acc_dk[db]));
     }
-    // dK and dV rows through LDS (every wave is done with the ring after the barrier): the
-    // wave's dK block, then its dV block
+    // dK and dV rows through LDS (every wave is done with the ring after the barrier, and no
+    // load is in flight, not even the K and V rows' without a walk): the wave's dK block, then
+    // its dV block
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     {
         typedef __attribute__((address_space(3))) unsigned char* lds_ptr;
