@@ -102,7 +102,8 @@ fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void*
  *                 one completion word per (sequence, KV head) and the float32 partial
  *                 (m, l, O) of every chunk; contents on entry are ignored (a completion
  *                 word carries a tag of the call that wrote it, so stale or arbitrary words
- *                 count as empty)
+ *                 count as empty, and the last arrival leaves it at zero, so a launch
+ *                 replayed from a captured graph, tag and all, starts clean as well)
  *
  * One launch: each chunk of a sequence's pages yields a partial; the last chunk of each
  * (sequence, KV head) to finish merges the partials, in chunk order, into o. Calls that
