@@ -589,12 +589,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int sl = 0; sl < kSlots; ++sl) {
             // A(r)'s scores, taken at the slot's start. Slot 0 reads what the step before wrote
-            // in its slots kSlots / 2 - 2 and kSlots / 2 - 1, kSlots / 2 products earlier; the
-            // wait states are a margin beyond the time a matrix instruction's result needs
-            // before a vector read.
+            // in its slots kSlots / 2 - 2 and kSlots / 2 - 1, with kSlots / 2 products and their
+            // vector work issued since: far more wait states than a matrix instruction's result
+            // needs before a vector read (the prologue's products are padded explicitly).
             const bool has_a = kSpread == 1 || (sl & 1) == 0;
             const int r = sl / kSpread;
-            if (sl == 0) asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
             float sr = 0.f, dpr = 0.f;
             if (has_a) {
                 sr = sc_c[r];
@@ -678,6 +677,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
                 mma_v(sa, oq.rows(lds, 0, kk), kf[kk]);
                 mma_v(da, odo.rows(lds, 0, kk), vf[kk]);
             }
+            // the wait states between these products and the first step's reads of their
+            // results (the masking at its start, or its slot 0)
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
         }
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
