@@ -150,7 +150,6 @@ TRAFFIC_KERNELS = {
     "fp8": ("fwd_bf16_sp_kernel<128, 3, false>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
     "fp8v": ("fwd_bf16_sp_kernel<128, 4, false>", "exact_tiled_attention_24_amd/csrc/fwd_bf16_sp.hip"),
     "decode": ("decode_mx_kernel", "exact_tiled_attention_24_amd/csrc/decode_mx.hip"),
-    "bwd_prep": ("bwd_prep_kernel<128>", "exact_tiled_attention_24_amd/csrc/bwd_bf16.hip"),
     "bwd_dkdv": ("bwd_dkdv_kernel<128>", "exact_tiled_attention_24_amd/csrc/bwd_bf16.hip"),
     "bwd_dq": ("bwd_dq_kernel<128>", "exact_tiled_attention_24_amd/csrc/bwd_bf16.hip"),
 }
@@ -636,12 +635,11 @@ def main():
             "avg_call_ms": round(float(bwd_ms.mean()), 5), "calls": int(bwd_ms.size),
             "roofline": {"bound": "mfma", "achieved": round(b_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(b_tflops / PEAK_BF16_TFLOPS, 4),
-                         "kernels": "bwd_prep_kernel, bwd_dkdv_kernel, bwd_dq_kernel",
-                         # HBM bytes of one call (the three kernels), when all were counted
-                         "traffic": (sum(traffic[k] for k in ("bwd_prep", "bwd_dkdv", "bwd_dq"))
-                                     if all(traffic.get(k) for k in ("bwd_prep", "bwd_dkdv", "bwd_dq"))
-                                     else None),
-                         "traffic_by_kernel": {k: traffic.get(k) for k in ("bwd_prep", "bwd_dkdv", "bwd_dq")}},
+                         "kernels": "bwd_dq_kernel, bwd_dkdv_kernel",
+                         # HBM bytes of one call (both kernels), when both were counted
+                         "traffic": (sum(traffic[k] for k in ("bwd_dq", "bwd_dkdv"))
+                                     if all(traffic.get(k) for k in ("bwd_dq", "bwd_dkdv")) else None),
+                         "traffic_by_kernel": {k: traffic.get(k) for k in ("bwd_dq", "bwd_dkdv")}},
         }
     try:  # the counter evidence behind the tile and split choices (from the sweeps)
         with open(os.path.join(ROOT, "profiles", "choices.json")) as f:

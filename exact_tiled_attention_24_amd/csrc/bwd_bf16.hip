@@ -6,14 +6,15 @@
 // so that dS = P * (dP - D) needs no second pass over the keys. With dP = dO V^T:
 //     dV = P^T dO,   dK = scale dS^T Q,   dQ = scale dS K.
 //
-// Three kernels:
-//  * bwd_prep: D_i and the log2-domain normaliser L_i = (m_i + ln l_i) log2 e of every query
-//    row, so that P = exp2(scale log2e q.k - L) (L = +inf for a row with no key: P = 0).
-//  * bwd_dkdv: one workgroup per (128-key block, KV head); each wave keeps its 32 keys' K and V
-//    in registers and walks the query chunks (32 rows of Q and dO staged in LDS) of every
-//    query head of the KV group, accumulating dV^T and dK^T.
+// Two kernels, dQ first:
 //  * bwd_dq: one workgroup per (128-query block, query head); each wave keeps its 32 queries'
-//    Q and dO in registers and walks the key chunks (32 rows of K and V in LDS).
+//    Q and dO in registers, computes their D_i and log2-domain normaliser
+//    L_i = (m_i + ln l_i) log2 e, so that P = exp2(scale log2e q.k - L) (L = +inf for a row
+//    with no key: P = 0), writes both for the next kernel and walks the key chunks (32 rows of
+//    K and V in LDS).
+//  * bwd_dkdv: one workgroup per (128-key block, KV head); each wave keeps its 32 keys' K and V
+//    in registers and walks the query chunks (32 rows of Q and dO staged in LDS, with their L
+//    and D) of every query head of the KV group, accumulating dV^T and dK^T.
 // Chunks are double-buffered: the next chunk's rows load straight into the other LDS buffer
 // while the current chunk's products run, with one barrier per chunk.
 // All products use v_mfma_f32_32x32x16_bf16. As in the forward kernel, the score tile is
@@ -249,57 +250,15 @@ __device__ __forceinline__ int xcd_position(int total) {
     return k * q + min_(k, r) + j;
 }
 
-// ---- D_i = rowsum(dO * O) and L_i = (m_i + ln l_i) log2 e, 4 threads per row ----
-// Layout of L and D: per head, per 32-row chunk, the chunk's 32 L values then its 32 D values
-// (256 bytes), so that one 4-byte-per-lane load moves a chunk's L and D together. A head's
-// rows are padded to a multiple of 32; padding rows get L = +inf, D = 0 (P = 0 there).
+// ---- D_i = rowsum(dO * O) and L_i = (m_i + ln l_i) log2 e ----
+// Layout of L and D (written by the dQ kernel, read by the dK/dV kernel): per head, per 32-row
+// chunk, the chunk's 32 L values then its 32 D values (256 bytes), so that one 4-byte-per-lane
+// load moves a chunk's L and D together. A head's rows are padded to a multiple of 32; padding
+// rows get L = +inf, D = 0 (P = 0 there).
 constexpr int kLdChunk = 32;
 __host__ __device__ constexpr long long ld_rows(int N) { return ((long long)N + kLdChunk - 1) / kLdChunk * kLdChunk; }
 __device__ __forceinline__ long long ld_index(long long head, int N, int row) {
     return head * 2 * ld_rows(N) + (long long)(row / kLdChunk) * (2 * kLdChunk) + row % kLdChunk;
-}
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const uint16_t* __restrict__ o,
-                                                            const uint16_t* __restrict__ dout,
-                                                            const float* __restrict__ m,
-                                                            const float* __restrict__ l,
-                                                            float* __restrict__ ld, int N,
-                                                            long long heads) {
-    const long long np = ld_rows(N);
-    const long long prow = (long long)blockIdx.x * (kThreads / 4) + threadIdx.x / 4;  // padded row
-    const long long head = prow / np;
-    const int r = (int)(prow - head * np);
-    const bool real = head < heads && r < N;
-    const long long row = head * N + r;
-    const int part = threadIdx.x & 3;
-    float acc = 0.f;
-    if (real) {
-        const uint16_t* po = o + row * D + part * (D / 4);
-        const uint16_t* pd = dout + row * D + part * (D / 4);
-#pragma unroll
-        for (int c = 0; c < D / 4; c += 8) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(po + c);
-            const u32x4 b = *reinterpret_cast<const u32x4*>(pd + c);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc = __builtin_fmaf(bf16_lo(a[i]), bf16_lo(b[i]), acc);
-                acc = __builtin_fmaf(bf16_hi(a[i]), bf16_hi(b[i]), acc);
-            }
-        }
-    }
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    if (head < heads && part == 0) {
-        const long long at = ld_index(head, N, r);
-        float lv = INFINITY;
-        if (real) {
-            const float lr = l[row];
-            lv = lr > 0.f ? (m[row] + logf(lr)) * kLog2e : INFINITY;
-        }
-        ld[at] = lv;
-        ld[at + kLdChunk] = real ? acc : 0.f;
-    }
 }
 
 struct BwdArgs {
@@ -307,7 +266,10 @@ struct BwdArgs {
     const uint16_t* k;
     const uint16_t* v;
     const uint16_t* dout;
-    const float* ld;    // L and D of every query row, in 32-row chunks (see bwd_prep_kernel)
+    const uint16_t* o;  // the forward's output and row statistics (natural-log units)
+    const float* m;
+    const float* l;
+    float* ld;          // L and D of every query row, in 32-row chunks (see ld_index)
     uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;
@@ -776,9 +738,32 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
             dof[kk] = *reinterpret_cast<const bf16x8*>(a.dout + (qoff + qr) * D + 16 * kk + 8 * h);
         }
     }
-    const long long ldi = ld_index((long long)bh, N, min_(query, N - 1));
-    const float lse = query < N ? a.ld[ldi] : INFINITY;
-    const float dsum = query < N ? a.ld[ldi + kLdChunk] : 0.f;
+    // L = (m + ln l) log2 e and D = dO . O of the lane's query, computed here and written to the
+    // workspace for the dK/dV kernel, which runs after this one (a padding row, past N, gets
+    // L = +inf and D = 0, so that its P is 0). The wave's 32 queries are one chunk of the
+    // layout: lane q writes the chunk's L value q, lane 32 + q its D value q.
+    float lse = INFINITY, dsum = 0.f;
+    {
+        const int qr = min_(query, N - 1);
+        float part = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const u32x4 ov = *reinterpret_cast<const u32x4*>(a.o + (qoff + qr) * D + 16 * kk + 8 * h);
+            const u32x4 dv = __builtin_bit_cast(u32x4, dof[kk]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                part = __builtin_fmaf(bf16_lo(ov[i]), bf16_lo(dv[i]), part);
+                part = __builtin_fmaf(bf16_hi(ov[i]), bf16_hi(dv[i]), part);
+            }
+        }
+        part += __shfl_xor(part, 32);  // the other half of the row's head dimensions
+        if (query < N) {
+            const float lr = a.l[qoff + query];
+            lse = lr > 0.f ? (a.m[qoff + query] + logf(lr)) * kLog2e : INFINITY;
+            dsum = part;
+        }
+        if (qw0 < N) a.ld[ld_index((long long)bh, N, qw0) + lane] = h == 0 ? lse : dsum;
+    }
     f32x16 acc_dq[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) acc_dq[i] = f32x16{};
@@ -946,20 +931,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 template <int D>
-hipError_t launch_bwd_d(const BwdArgs& a, const uint16_t* o, const float* m, const float* l,
-                        float* ld, int B, hipStream_t stream) {
-    const long long heads = (long long)B * a.Hq;
-    const long long rows = heads * ld_rows(a.N);  // padded rows
-    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + 63) / 64)), dim3(kThreads), 0,
-                       stream, o, a.dout, m, l, ld, a.N, heads);
+hipError_t launch_bwd_d(const BwdArgs& a, int B, hipStream_t stream) {
+    // dQ first: it writes the L and D rows that dK/dV reads
+    const unsigned blocks = (unsigned)((a.N + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(blocks, (unsigned)(B * a.Hq)), dim3(kThreads), 0,
+                       stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned blocks = (unsigned)((a.N + kBlock - 1) / kBlock);
     hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(blocks, (unsigned)(B * a.Hkv)), dim3(kThreads), 0,
-                       stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(blocks, (unsigned)(B * a.Hq)), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
 }
@@ -975,6 +954,9 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
     a.dout = static_cast<const uint16_t*>(dout);
+    a.o = static_cast<const uint16_t*>(o);
+    a.m = m;
+    a.l = l;
     a.ld = ld;
     a.dq = static_cast<uint16_t*>(dq);
     a.dk = static_cast<uint16_t*>(dk);
@@ -983,9 +965,7 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
     a.scale = scale;
     a.scale_log2 = scale * kLog2e;
     a.causal = causal;
-    const uint16_t* op = static_cast<const uint16_t*>(o);
-    return d == 128 ? launch_bwd_d<128>(a, op, m, l, ld, B, stream)
-                    : launch_bwd_d<64>(a, op, m, l, ld, B, stream);
+    return d == 128 ? launch_bwd_d<128>(a, B, stream) : launch_bwd_d<64>(a, B, stream);
 }
 
 }  // namespace fa
