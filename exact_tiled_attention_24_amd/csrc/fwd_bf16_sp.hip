@@ -200,6 +200,11 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     constexpr bool kV8 = kMode == kModeFp8V;              // e4m3 V, P V on the fp8 matrix cores
     constexpr bool kFp8 = kMode == kModeFp8 || kV8;       // e4m3 Q and K
     constexpr bool kQLds = kMode == kModeDense;            // Q through LDS (see Tile)
+    // bf16 without statistics (d = 128): Q is multiplied by the scale (log2 units) once, so
+    // that the products give the exponent arguments, and the products of each score block start
+    // from minus the row's exponent reference instead of zero: exp2 then takes the product's
+    // result as it is (no scale-and-subtract per score)
+    constexpr bool kPre = !kStats && !kFp8 && D == 128;
     using T = Tile<D, kPaged, kFp8, kV8>;
     // LDS operand reads kept in flight: fewer for the dense d = 64 instance, whose two
     // workgroups per CU leave a wave 128 registers
@@ -297,6 +302,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     // (the exponent reference starts finite: a row whose first tiles are all masked then gets
     // exp2(-inf) = 0 rather than exp2(-inf + inf), and moves to its first finite maximum)
     float m_run = -INFINITY, m_ref = -1e30f, l_part = 0.f;
+    f32x16 negm;  // (kPre) minus the exponent reference, the score products' initial value
 
     const int kv_end = causal ? min_(Nk, qb * kBr + kBr + off) : Nk;
     const int n_tiles = kSparse ? n_list : (kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0);
@@ -703,7 +709,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         // phase after its second score and summed one phase later (the last pair at once)
         float es[16];
         auto single_stages = [&](int ph) {
-            es[ph] = exp2_hw(__builtin_fmaf(s_cur[ph], scale_log2, -m_ref));
+            es[ph] = exp2_hw(kPre ? s_cur[ph] : __builtin_fmaf(s_cur[ph], scale_log2, -m_ref));
             auto pack_pair = [&](int k) {
                 wk[k] = pack_bf16x2(es[2 * k], es[2 * k + 1]);
                 pk_cur[k >> 2][k & 3] = wk[k];
@@ -787,6 +793,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         }
 #pragma unroll
         for (int sl = 0; sl < kAh; ++sl) cur[sl] = fr[sl];
+        if constexpr (kPre) s_next = negm;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int sl = 0; sl < kSlots; ++sl) {
@@ -875,6 +882,15 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
             qf[kk] = *(const lds_bf16x8*)(qblk + rq * 2 * D + 16 * ((2 * kk + hh) ^ osw<D>(rq)));
     }
     barrier_lds();
+    if constexpr (kPre) {
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            u32x4 w = __builtin_bit_cast(u32x4, qf[kk]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(bf16_lo(w[i]) * scale_log2, bf16_hi(w[i]) * scale_log2);
+            qf[kk] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
     if constexpr (kFp8) {
 #pragma unroll
         for (int c = 0; c < D / 64; ++c) asm volatile("" : "+v"(qf8[c]));
@@ -1074,8 +1090,15 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         float u = t[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) u = vmax(u, t[r]);
-        u = pair32_vmax(u) * scale_log2;
+        u = pair32_vmax(u) * (kPre ? 1.f : scale_log2);
         m_ref = u > -1e30f ? u : -1e30f;
+        if constexpr (kPre) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                negm[r] = -m_ref;
+                sa[r] -= m_ref;  // (the first half tile's products started from zero)
+            }
+        }
     }
     {
         const bool masked0 = kSparse ? kvq0 >= n_plain * kBc : n_plain == 0;
