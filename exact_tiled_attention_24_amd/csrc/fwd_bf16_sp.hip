@@ -23,15 +23,19 @@
 //    reads K rows in an order that swaps bits 2 and 3 of the row index, so the
 //    accumulator's register order is the key order the second MFMA needs.
 //  * K and V tiles go from global memory straight into LDS (buffer loads with the LDS
-//    bit): no staging registers. Both are stored row-major with padded rows (K: +16 bytes,
-//    V: +64 bytes), which makes every operand read conflict free on gfx950's 64 banks; the
-//    V^T operand comes out of row-major V through ds_read_b64_tr_b16.
+//    bit): no staging registers. bf16 rows are stored row-major with their 16-byte chunks
+//    XOR-swizzled by row (fp8 K rows padded instead), which makes every operand read conflict
+//    free on gfx950's 64 banks; the V^T operand comes out of row-major V through
+//    ds_read_b64_tr_b16. Q (dense) comes in and O goes out the same way, in whole 1 KiB
+//    pieces through a per-wave LDS block, rather than as 16 or 8 bytes spread over 32 rows.
 //  * Four LDS stages per operand: K of tile j+3 and V of tile j+2 are requested while tile
 //    j is computed, with one workgroup barrier per 64-key tile. The tile loop is unrolled
 //    over the four stages, so every operand address is a loop-invariant base plus an
 //    immediate offset.
 //  * Scores in the log2 domain; the exponent reference moves only when a row maximum beats
 //    it by more than 2^8, so the O rescale (a branch after the MFMAs, out of line) is rare.
+//    Without row statistics the reference is fixed per item, and at d = 128 the scale is
+//    folded into Q and the reference into the products' initial value (see kPre).
 //    The row sum adds the bf16-rounded probabilities (v_dot2 on the packed pairs), i.e.
 //    exactly the weights the O MFMA uses.
 //  * Every wave runs every half tile of its workgroup (those past its own diagonal are
