@@ -38,9 +38,11 @@
 //    folded into Q and the reference into the products' initial value (see kPre).
 //    The row sum adds the bf16-rounded probabilities (v_dot2 on the packed pairs), i.e.
 //    exactly the weights the O MFMA uses.
-//  * Every wave runs every half tile of its workgroup (those past its own diagonal are
-//    fully masked and contribute nothing), so all waves follow one schedule; masking is a
-//    uniform branch taken only on the diagonal and ragged tiles.
+//  * Every wave runs the half tiles of its workgroup in one schedule; masking is a uniform
+//    branch taken only on the diagonal and ragged tiles. In the dense d = 128 instance a wave
+//    leaves out the steps past its own diagonal (they would add zero weights) but still issues
+//    its share of the loads and meets every barrier; waves w and w + 4, which share a SIMD,
+//    take row blocks w and 7 - w so that those savings are spread over the SIMDs.
 //  * Grid: one persistent workgroup per CU; a work item is one (256-row query block, head),
 //    and each workgroup walks items of its XCD's contiguous share of the list in snake
 //    order (see the kernel).
@@ -275,7 +277,12 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
-    const int row0 = qb * kBr + 32 * wave;
+    // (dense, d = 128) a wave skips the steps past the last key its rows see (see the tile
+    // loop; the d = 64 instance has no registers left for the branches it takes); the
+    // waves sharing a SIMD (w and w + 4) take row blocks w and 7 - w, so that on the diagonal
+    // tiles every SIMD is left about the same number of steps
+    constexpr bool kSkip = kMode == kModeDense && D == 128;
+    const int row0 = qb * kBr + 32 * (kSkip && wave >= 4 ? 11 - wave : wave);
     const int qrow = row0 + l32;
 
     // Q as the B operand of S^T = K Q^T: bf16, 8 head dimensions per 16-wide chunk and lane
@@ -309,6 +316,9 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     f32x16 negm;  // (kPre) minus the exponent reference, the score products' initial value
 
     const int kv_end = causal ? min_(Nk, qb * kBr + kBr + off) : Nk;
+    // (dense) the last half tile holding a key some row of the wave sees: the steps of half
+    // tiles h_last + 2 on would only add zero weights, and the wave leaves them out
+    const int h_last = (causal ? min_(row0 + 31 + off, Nk - 1) : Nk - 1) >> 5;
     const int n_tiles = kSparse ? n_list : (kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0);
 
     // ---- staging: buffer loads straight into LDS (no registers). A tile's K stage (64
@@ -1122,8 +1132,17 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         constexpr int P = decltype(phase_c)::value;
         advance(j + 3);
         const bool masked = kSparse ? kvq0 >= n_plain * kBc : j >= n_plain;
-        step(2 * j, kvq0, std::integral_constant<int, 2 * P>{}, sa, sb, pb, pa, masked, fr, kq, Yes{}, Yes{});
-        step(2 * j + 1, kvq0, std::integral_constant<int, 2 * P + 1>{}, sb, sa, pa, pb, masked, fr, kq, Yes{}, No{});
+        if (kSkip && 2 * j >= h_last + 2) {
+            // every key of the tile is past the wave's rows, and the previous half tile's
+            // weights are zero: only the wave's share of the loads remains
+#pragma unroll
+            for (int i = 0; i < T::kDmaPerWave; ++i) dma_op(j, i, P);
+        } else {
+            step(2 * j, kvq0, std::integral_constant<int, 2 * P>{}, sa, sb, pb, pa, masked, fr, kq, Yes{}, Yes{});
+            if (!kSkip || 2 * j + 1 < h_last + 2)
+                step(2 * j + 1, kvq0, std::integral_constant<int, 2 * P + 1>{}, sb, sa, pa, pb, masked, fr, kq, Yes{},
+                     No{});
+        }
         wait_dma_tile();
         barrier_lds();
     };
@@ -1138,8 +1157,9 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         tile(j, std::integral_constant<int, 0>{});
         ++j;
     }
-    // last half tile's O update (its S^T step computed a score block past the end, unused)
-    switch ((n_tiles - 1) & 3) {
+    // last half tile's O update (its S^T step computed a score block past the end, unused;
+    // a wave that skipped its step has no weights there)
+    if (!kSkip || 2 * n_tiles - 1 < h_last + 2) switch ((n_tiles - 1) & 3) {
         case 0: compute_pv(pb, 0, 1); break;
         case 1: compute_pv(pb, 1, 1); break;
         case 2: compute_pv(pb, 2, 1); break;
