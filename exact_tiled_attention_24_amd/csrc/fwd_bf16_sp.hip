@@ -39,9 +39,9 @@
 //    The row sum adds the bf16-rounded probabilities (v_dot2 on the packed pairs), i.e.
 //    exactly the weights the O MFMA uses.
 //  * Every wave runs the half tiles of its workgroup in one schedule; masking is a uniform
-//    branch taken only on the diagonal and ragged tiles. In the dense d = 128 instance a wave
-//    leaves out the steps past its own diagonal (they would add zero weights) but still issues
-//    its share of the loads and meets every barrier; waves w and w + 4, which share a SIMD,
+//    branch taken only on the diagonal and ragged tiles. In the dense instances a wave leaves
+//    out the steps past its own diagonal (they would add zero weights) but still issues its
+//    share of the loads and meets every barrier; waves w and w + 4, which share a SIMD,
 //    take row blocks w and 7 - w so that those savings are spread over the SIMDs.
 //  * Grid: one persistent workgroup per CU; a work item is one (256-row query block, head),
 //    and each workgroup walks items of its XCD's contiguous share of the list in snake
@@ -277,11 +277,10 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
-    // (dense, d = 128) a wave skips the steps past the last key its rows see (see the tile
-    // loop; the d = 64 instance has no registers left for the branches it takes); the
+    // (dense) a wave skips the steps past the last key its rows see (see the tile loop); the
     // waves sharing a SIMD (w and w + 4) take row blocks w and 7 - w, so that on the diagonal
     // tiles every SIMD is left about the same number of steps
-    constexpr bool kSkip = kMode == kModeDense && D == 128;
+    constexpr bool kSkip = kMode == kModeDense;
     const int row0 = qb * kBr + 32 * (kSkip && wave >= 4 ? 11 - wave : wave);
     const int qrow = row0 + l32;
 
@@ -317,7 +316,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
 
     const int kv_end = causal ? min_(Nk, qb * kBr + kBr + off) : Nk;
     // (dense) the last half tile holding a key some row of the wave sees: the steps of half
-    // tiles h_last + 2 on would only add zero weights, and the wave leaves them out
+    // tiles h_last + 2 on would only add zero weights
     const int h_last = (causal ? min_(row0 + 31 + off, Nk - 1) : Nk - 1) >> 5;
     const int n_tiles = kSparse ? n_list : (kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0);
 
@@ -1132,34 +1131,47 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         constexpr int P = decltype(phase_c)::value;
         advance(j + 3);
         const bool masked = kSparse ? kvq0 >= n_plain * kBc : j >= n_plain;
-        if (kSkip && 2 * j >= h_last + 2) {
-            // every key of the tile is past the wave's rows, and the previous half tile's
-            // weights are zero: only the wave's share of the loads remains
-#pragma unroll
-            for (int i = 0; i < T::kDmaPerWave; ++i) dma_op(j, i, P);
-        } else {
-            step(2 * j, kvq0, std::integral_constant<int, 2 * P>{}, sa, sb, pb, pa, masked, fr, kq, Yes{}, Yes{});
-            if (!kSkip || 2 * j + 1 < h_last + 2)
-                step(2 * j + 1, kvq0, std::integral_constant<int, 2 * P + 1>{}, sb, sa, pa, pb, masked, fr, kq, Yes{},
-                     No{});
-        }
+        step(2 * j, kvq0, std::integral_constant<int, 2 * P>{}, sa, sb, pb, pa, masked, fr, kq, Yes{}, Yes{});
+        step(2 * j + 1, kvq0, std::integral_constant<int, 2 * P + 1>{}, sb, sa, pa, pb, masked, fr, kq, Yes{}, No{});
         wait_dma_tile();
         barrier_lds();
     };
+    // (dense) the wave's steps end with tile j_stop - 1: from there on the half tiles are past
+    // its last visible key (the last step run, half tile 2 j_stop - 1, is too, so its weights
+    // are zero and nothing is left for the O update that would follow)
+    const int j_stop = kSkip ? min_(n_tiles, max_(1, (h_last + 3) >> 1)) : n_tiles;
     int j = 1;
-    while (j < n_tiles) {
+    while (j < j_stop) {
         tile(j, std::integral_constant<int, 1>{});
-        if (++j >= n_tiles) break;
+        if (++j >= j_stop) break;
         tile(j, std::integral_constant<int, 2>{});
-        if (++j >= n_tiles) break;
+        if (++j >= j_stop) break;
         tile(j, std::integral_constant<int, 3>{});
-        if (++j >= n_tiles) break;
+        if (++j >= j_stop) break;
         tile(j, std::integral_constant<int, 0>{});
         ++j;
     }
-    // last half tile's O update (its S^T step computed a score block past the end, unused;
-    // a wave that skipped its step has no weights there)
-    if (!kSkip || 2 * n_tiles - 1 < h_last + 2) switch ((n_tiles - 1) & 3) {
+    if constexpr (kSkip) {
+        // the item's remaining tiles: the wave's share of their loads and the barriers only
+        auto idle_tile = [&](int jj, auto phase_c) {
+            constexpr int P = decltype(phase_c)::value;
+            advance(jj + 3);
+#pragma unroll
+            for (int i = 0; i < T::kDmaPerWave; ++i) dma_op(jj, i, P);
+            wait_dma_tile();
+            barrier_lds();
+        };
+        for (; j < n_tiles; ++j) {
+            switch (j & 3) {
+                case 0: idle_tile(j, std::integral_constant<int, 0>{}); break;
+                case 1: idle_tile(j, std::integral_constant<int, 1>{}); break;
+                case 2: idle_tile(j, std::integral_constant<int, 2>{}); break;
+                default: idle_tile(j, std::integral_constant<int, 3>{}); break;
+            }
+        }
+    }
+    // last half tile's O update (its S^T step computed a score block past the end, unused)
+    if (j_stop >= n_tiles) switch ((n_tiles - 1) & 3) {
         case 0: compute_pv(pb, 0, 1); break;
         case 1: compute_pv(pb, 1, 1); break;
         case 2: compute_pv(pb, 2, 1); break;
