@@ -277,10 +277,10 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
-    // (dense) a wave skips the steps past the last key its rows see (see the tile loop); the
-    // waves sharing a SIMD (w and w + 4) take row blocks w and 7 - w, so that on the diagonal
+    // (dense, bf16 or e4m3) a wave skips the steps past the last key its rows see (see the tile
+    // loop); the waves sharing a SIMD (w and w + 4) take row blocks w and 7 - w, so that on the diagonal
     // tiles every SIMD is left about the same number of steps
-    constexpr bool kSkip = kMode == kModeDense;
+    constexpr bool kSkip = kMode == kModeDense || kMode == kModeFp8 || kMode == kModeFp8V;
     const int row0 = qb * kBr + 32 * (kSkip && wave >= 4 ? 11 - wave : wave);
     const int qrow = row0 + l32;
 
