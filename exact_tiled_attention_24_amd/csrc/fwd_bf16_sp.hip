@@ -39,10 +39,11 @@
 //    The row sum adds the bf16-rounded probabilities (v_dot2 on the packed pairs), i.e.
 //    exactly the weights the O MFMA uses.
 //  * Every wave runs the half tiles of its workgroup in one schedule; masking is a uniform
-//    branch taken only on the diagonal and ragged tiles. In the dense instances a wave leaves
-//    out the steps past its own diagonal (they would add zero weights) but still issues its
-//    share of the loads and meets every barrier; waves w and w + 4, which share a SIMD,
-//    take row blocks w and 7 - w so that those savings are spread over the SIMDs.
+//    branch taken only on the diagonal and ragged tiles. Except in the block-sparse
+//    instance, a wave leaves out the steps past its own diagonal (they would add zero
+//    weights) but still issues its share of the loads and meets every barrier; waves w and
+//    w + 4, which share a SIMD, take row blocks w and 7 - w so that those savings are spread
+//    over the SIMDs.
 //  * Grid: one persistent workgroup per CU; a work item is one (256-row query block, head),
 //    and each workgroup walks items of its XCD's contiguous share of the list in snake
 //    order (see the kernel).
@@ -277,10 +278,10 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
-    // (dense, bf16 or e4m3) a wave skips the steps past the last key its rows see (see the tile
-    // loop); the waves sharing a SIMD (w and w + 4) take row blocks w and 7 - w, so that on the diagonal
+    // (all but block-sparse, whose lists need not be sorted) a wave skips the steps past the
+    // last key its rows see (see the tile loop); the waves sharing a SIMD (w and w + 4) take row blocks w and 7 - w, so that on the diagonal
     // tiles every SIMD is left about the same number of steps
-    constexpr bool kSkip = kMode == kModeDense || kMode == kModeFp8 || kMode == kModeFp8V;
+    constexpr bool kSkip = kMode != kModeSparse;
     const int row0 = qb * kBr + 32 * (kSkip && wave >= 4 ? 11 - wave : wave);
     const int qrow = row0 + l32;
 
@@ -315,7 +316,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
     f32x16 negm;  // (kPre) minus the exponent reference, the score products' initial value
 
     const int kv_end = causal ? min_(Nk, qb * kBr + kBr + off) : Nk;
-    // (dense) the last half tile holding a key some row of the wave sees: the steps of half
+    // (kSkip) the last half tile holding a key some row of the wave sees: the steps of half
     // tiles h_last + 2 on would only add zero weights
     const int h_last = (causal ? min_(row0 + 31 + off, Nk - 1) : Nk - 1) >> 5;
     const int n_tiles = kSparse ? n_list : (kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0);
@@ -1136,7 +1137,7 @@ __device__ __forceinline__ bool fwd_item(const FwdArgs& a, int item, unsigned ch
         wait_dma_tile();
         barrier_lds();
     };
-    // (dense) the wave's steps end with tile j_stop - 1: from there on the half tiles are past
+    // (kSkip) the wave's steps end with tile j_stop - 1: from there on the half tiles are past
     // its last visible key (the last step run, half tile 2 j_stop - 1, is too, so its weights
     // are zero and nothing is left for the O update that would follow)
     const int j_stop = kSkip ? min_(n_tiles, max_(1, (h_last + 3) >> 1)) : n_tiles;
